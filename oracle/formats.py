@@ -1,0 +1,144 @@
+"""Element formats of the KV cache, written out from their definitions (oracle).
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+The pages name the cache dtypes but not their encodings: FP16/BF16 at two
+bytes and FP8 at one byte per element ("vLLM 引擎解剖", section "KV 缓存需要多少
+内存？", the bytes-per-element factor), and fp8 as a --kv-cache-dtype choice
+("01. vLLM：从分页 KV 起家的通用推理引擎", section "KV 缓存管理与前缀缓存").
+The encodings below are the standard ones:
+
+* bf16: the upper 16 bits of an IEEE-754 binary32.
+* fp8 E4M3 (OCP "fn" variant): 1 sign bit, 4 exponent bits (bias 7), 3
+  mantissa bits; exponent field 0 is subnormal; S.1111.111 is NaN; there is no
+  infinity; the largest finite magnitude is 448 (code 0x7E).
+
+Storage is always handled as raw integers (uint16 for bf16, uint8 for fp8) or
+float32, exactly as the cache holds it; values are produced in float64.
+"""
+
+import numpy as np
+
+F32, BF16, FP8_E4M3 = "f32", "bf16", "fp8_e4m3"
+
+BYTES_PER_ELEM = {F32: 4, BF16: 2, FP8_E4M3: 1}
+
+E4M3_MAX = 448.0
+
+
+def bf16_bits_to_f64(bits):
+    """bf16 bit patterns (uint16) -> float64, exactly: the pattern is the top
+    half of a binary32."""
+    bits = np.asarray(bits, dtype=np.uint16)
+    as_u32 = bits.astype(np.uint32) << np.uint32(16)
+    return as_u32.view(np.float32).astype(np.float64)
+
+
+def f32_to_f64(x):
+    return np.asarray(x, dtype=np.float32).astype(np.float64)
+
+
+def e4m3_code_value(code):
+    """Real value of one E4M3 code (Python float, exact), NaN for the two NaN
+    codes.  Written from the field definition, one code at a time."""
+    code = int(code) & 0xFF
+    sign = -1.0 if (code >> 7) & 1 else 1.0
+    exp_field = (code >> 3) & 0xF
+    mant = code & 0x7
+    if exp_field == 0xF and mant == 0x7:
+        return float("nan")
+    if exp_field == 0:
+        return sign * (mant / 8.0) * 2.0 ** (1 - 7)
+    return sign * (1.0 + mant / 8.0) * 2.0 ** (exp_field - 7)
+
+
+# Table of all 256 codes -> float64 (NaN for 0x7F and 0xFF).
+E4M3_TABLE = np.array([e4m3_code_value(c) for c in range(256)], dtype=np.float64)
+
+
+def fp8_bits_to_f64(codes, scale=1.0):
+    """E4M3 codes (uint8) -> float64 value times the per-tensor scale."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    return E4M3_TABLE[codes.astype(np.int64)] * float(np.float32(scale))
+
+
+def storage_to_f64(raw, dtype, scale=1.0):
+    """Stored cache or tensor elements of ``dtype`` -> float64 values."""
+    if dtype == F32:
+        return f32_to_f64(raw)
+    if dtype == BF16:
+        return bf16_bits_to_f64(raw)
+    if dtype == FP8_E4M3:
+        return fp8_bits_to_f64(raw, scale)
+    raise ValueError(f"unknown dtype {dtype}")
+
+
+# The 127 non-negative finite magnitudes, codes 0x00 .. 0x7E, in code order
+# (which is also increasing value order).
+_POS_CODES = np.arange(0x7F, dtype=np.int64)
+_POS_VALUES = E4M3_TABLE[:0x7F]
+
+
+def e4m3_encode_scalar(y):
+    """Quantise one binary32 value to E4M3 by brute-force nearest search.
+
+    * NaN -> 0x7F with the input's sign bit.
+    * |y| > 448 (including infinity) saturates to 448 with the sign kept.
+    * Otherwise the nearest finite magnitude wins; an exact tie between two
+      neighbours goes to the code whose mantissa LSB is 0 (round half to
+      even).  Zero keeps its sign.
+    """
+    y = np.float32(y)
+    sign_bit = int(np.array([y], dtype=np.float32).view(np.uint32)[0] >> 31)
+    if np.isnan(y):
+        return 0x7F | (sign_bit << 7)
+    mag = abs(float(y))
+    if mag > E4M3_MAX:
+        return 0x7E | (sign_bit << 7)
+    dist = np.abs(_POS_VALUES - mag)
+    best = dist.min()
+    cands = _POS_CODES[dist == best]
+    if len(cands) == 1:
+        code = int(cands[0])
+    else:
+        even = [int(c) for c in cands if (int(c) & 1) == 0]
+        assert len(even) == 1, (y, cands)
+        code = even[0]
+    return code | (sign_bit << 7)
+
+
+def e4m3_encode(y):
+    """Vectorised form of ``e4m3_encode_scalar`` over a float32 array: the same
+    nearest search, done against all 127 magnitudes at once."""
+    y = np.asarray(y, dtype=np.float32)
+    flat = y.reshape(-1)
+    sign = (flat.view(np.uint32) >> np.uint32(31)).astype(np.int64)
+    mag = np.abs(flat.astype(np.float64))
+    out = np.empty(flat.shape, dtype=np.int64)
+    nan = np.isnan(flat)
+    sat = (~nan) & (mag > E4M3_MAX)
+    rest = ~(nan | sat)
+    if rest.any():
+        m = mag[rest][:, None]
+        dist = np.abs(_POS_VALUES[None, :] - m)
+        best = dist.min(axis=1, keepdims=True)
+        is_best = dist == best
+        # among the nearest codes keep the even one when there are two
+        n_best = is_best.sum(axis=1)
+        pick_even = is_best & ((_POS_CODES[None, :] & 1) == 0)
+        chosen = np.where((n_best > 1)[:, None], pick_even, is_best)
+        assert (chosen.sum(axis=1) == 1).all()
+        out[rest] = np.argmax(chosen, axis=1)
+    out[nan] = 0x7F
+    out[sat] = 0x7E
+    out |= sign << 7
+    return out.astype(np.uint8).reshape(y.shape)
+
+
+def quantise_to_e4m3(x_f32, scale):
+    """The cache-write quantiser: code = E4M3(fp32(x) / fp32(scale)), the
+    division done once in binary32 (numpy's float32 divide is correctly
+    rounded)."""
+    x = np.asarray(x_f32, dtype=np.float32)
+    y = x / np.float32(scale)
+    return e4m3_encode(y.astype(np.float32))
