@@ -1,0 +1,234 @@
+"""Benchmark of the paged-attention hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+                    [--no-mixed]
+
+A step is one pass of the hot path over one batch: the Llama-3.1-8B-shaped
+decode layer (64 sequences, context 512..4096, 32 q / 8 kv heads, head_dim
+128, bf16, 16-token blocks): slot mapping of the 64 new tokens, their cache
+writes, and paged decode attention (partitions + merge).  Inputs are resident
+in HBM before timing starts; two copies of the KV pool alternate between
+steps so that the 256 MB last-level cache cannot serve a re-read.
+
+Prints one JSON line (rank 0): whole-step throughput in algorithmic KV GB/s,
+KV tokens/s, the decode kernel's roofline fraction, the oracle's CPU rate on a
+bounded sample, and (unless --no-mixed) the mixed unified step with chunked
+prefill (MFMA utilisation of the prefill call).
+"""
+
+import argparse
+import json
+import multiprocessing as mp
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
+
+
+def decode_bytes(step):
+    """Algorithmic bytes of one decode call: every context token's K and V
+    once, the queries and outputs, and the block-table entries used."""
+    lens = step.decode_context_lens.astype(np.int64)
+    kvb = 1 if step.kv_dtype == "fp8_e4m3" else (4 if step.kv_dtype == "f32" else 2)
+    qb = 4 if step.q_dtype == "f32" else 2
+    kv = int(lens.sum()) * 2 * step.num_kv_heads * step.head_dim * kvb
+    qo = len(lens) * 2 * step.num_q_heads * step.head_dim * qb
+    bt = int(sum((L + 15) // 16 for L in lens)) * 4
+    return kv + qo + bt
+
+
+def prefill_flops(step):
+    """4 * D * Hq flops per attended (query, key) pair, causal pairs only."""
+    qsl = step.prefill_query_start_loc
+    comp = step.prefill_num_computed
+    pairs = 0
+    for r in range(len(comp)):
+        n = int(qsl[r + 1] - qsl[r])
+        c = int(comp[r])
+        pairs += n * c + n * (n + 1) // 2
+    return 4.0 * step.head_dim * step.num_q_heads * pairs, pairs
+
+
+def time_region(fn, iters, stream):
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(iters):
+        fn(i)
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / iters        # ms
+
+
+# ----------------------------------------------------------- CPU baseline
+
+_CPU = {}
+
+
+def _one_blas_thread():
+    from threadpoolctl import threadpool_limits
+    _CPU["limits"] = threadpool_limits(1)
+
+
+def _cpu_unit(seq):
+    from oracle import paged as P
+    d = _CPU
+    return P.decode_attention(d["q"][seq:seq + 1], d["q_dtype"], d["kc"], d["vc"],
+                              d["kv_dtype"], d["tables"][seq:seq + 1],
+                              d["lens"][seq:seq + 1], d["scale"])
+
+
+def cpu_baseline(step, budget_s=12.0):
+    """The fp64 oracle, as written, over a sample of the decode batch's
+    sequences, one process per core with one BLAS thread each."""
+    from synth import rng as R
+    _CPU.update(q=R.to_numpy_storage(step.q[0]), kc=R.to_numpy_storage(step.k_caches[0]),
+                vc=R.to_numpy_storage(step.v_caches[0]), tables=step.block_tables,
+                lens=step.decode_context_lens, q_dtype=step.q_dtype,
+                kv_dtype=step.kv_dtype, scale=step.softmax_scale)
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    nseq = len(step.decode_context_lens)
+    # time one sequence on one core, then size the sample (whole passes over
+    # the batch) to about `budget_s` seconds of wall time
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        _cpu_unit(0)
+        one = time.perf_counter() - t0
+    per_pass = one * nseq / workers
+    passes = int(max(1, min(50, round(budget_s / max(per_pass, 1e-3)))))
+    units = list(range(nseq)) * passes
+    ctx = mp.get_context("fork")
+    t0 = time.perf_counter()
+    with ctx.Pool(workers, initializer=_one_blas_thread) as pool:
+        pool.map(_cpu_unit, units, chunksize=1)
+    wall = time.perf_counter() - t0
+    tokens = int(step.decode_context_lens.astype(np.int64).sum()) * passes
+    kv_bytes = tokens * 2 * step.num_kv_heads * step.head_dim * 2
+    return {"value": round(kv_bytes / wall / 1e9, 4), "unit": "GB/s", "cores": workers,
+            "kind": "oracle",
+            "sample": f"{passes} pass(es) over all {nseq} sequences x 32 heads of the "
+                      f"decode batch ({tokens} KV tokens), {wall:.1f} s wall on "
+                      f"{workers} worker processes with one BLAS thread each",
+            "kv_tokens_per_s": round(tokens / wall, 1)}
+
+
+# ----------------------------------------------------------- GPU legs
+
+def bench_decode(args, pk, step):
+    # two device copies of the same batch, used in turn
+    dss = [pk.step.DeviceStep(step) for _ in range(2)]
+    stream = torch.cuda.current_stream()
+
+    def one_step(i):
+        ds = dss[i % 2]
+        ds.slot_mapping()
+        ds.write(0)
+        ds.decode(0)
+
+    for i in range(args.warmup):
+        one_step(i)
+    ms_step = time_region(one_step, args.steps, stream)
+    ms_decode = time_region(lambda i: dss[i % 2].decode(0), args.steps, stream)
+    nbytes = decode_bytes(step)
+    tokens = int(step.decode_context_lens.sum())
+    return dss, {"ms_step": ms_step, "ms_decode": ms_decode, "bytes": nbytes,
+                       "tokens": tokens}
+
+
+def bench_mixed(args, pk, C):
+    s = C.config4(device="cuda")
+    ds = pk.step.DeviceStep(s)
+    stream = torch.cuda.current_stream()
+    for _ in range(max(2, args.warmup)):
+        ds.run()
+    iters = max(5, args.steps // 2)
+    ms_step = time_region(lambda i: ds.run(), iters, stream)
+    ms_prefill = time_region(lambda i: ds.prefill(0), iters, stream)
+    ms_decode = time_region(lambda i: ds.decode(0), iters, stream)
+    flops, pairs = prefill_flops(s)
+    tflops = flops / (ms_prefill * 1e-3) / 1e12
+    return {"workload": "mixed unified step: 64 x 100-token chunks on a 125-block "
+                        "shared prefix + 1,022-token first chunk + 192 decodes "
+                        "(1024..8192) + 64 copy-on-write copies, 32q/8kv, d128, bf16",
+            "ms_per_step": round(ms_step, 4),
+            "prefill_ms": round(ms_prefill, 4),
+            "prefill_tflops": round(tflops, 2),
+            "prefill_mfma_frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+            "prefill_pairs": pairs,
+            "decode_ms": round(ms_decode, 4),
+            "decode_gbs": round(decode_bytes(s) / (ms_decode * 1e-3) / 1e9, 1)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-mixed", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the paged-attention path here is "
+              "built and measured on a single MI355X (no collectives); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+    import paged_kv_cache_84_amd as pk
+    from synth import configs as C
+    # The workload is built on the host; the CPU baseline runs before the GPU
+    # is touched (its worker processes are forked from this one).
+    step = C.config2(device="cpu")
+    cpu = None if args.no_cpu_baseline else cpu_baseline(step)
+    torch.cuda.set_device(0)
+    pk.library()
+
+    dss, r = bench_decode(args, pk, step)
+    gbs_step = r["bytes"] / (r["ms_step"] * 1e-3) / 1e9
+    gbs_decode = r["bytes"] / (r["ms_decode"] * 1e-3) / 1e9
+    line = {
+        "metric": "paged decode attention HBM GB/s (% of peak) + KV tokens/s; "
+                  "prefill MFMA util",
+        "value": round(gbs_step, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "Llama-3.1-8B-shaped decode layer: 64 sequences, "
+                               "context uniform in [512, 4096], 32 q / 8 kv heads, "
+                               "head_dim 128, bf16 Q/K/V, 16-token blocks, shuffled "
+                               "block placement; step = slot mapping + cache write of "
+                               "the 64 new tokens + paged decode (partitions + merge)",
+                   "num_seqs": 64, "kv_tokens": r["tokens"],
+                   "algorithmic_bytes": r["bytes"],
+                   "partition_tokens": pk.decode_partition_tokens(64, 8, int(step.decode_context_lens.max()))},
+        "pct_of_hbm_peak": round(100 * gbs_step / HBM_PEAK_GBS, 2),
+        "kv_tokens_per_s": round(r["tokens"] / (r["ms_step"] * 1e-3), 1),
+        "roofline": {"bound": "hbm", "kernel": "paged_attention_decode (partition + merge)",
+                     "achieved": round(gbs_decode, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs_decode / HBM_PEAK_GBS, 4), "traffic": None,
+                     "launch_ms": round(r["ms_decode"], 4)},
+    }
+    if not args.no_mixed:
+        line["mixed_step"] = bench_mixed(args, pk, C)
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

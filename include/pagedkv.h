@@ -1,0 +1,249 @@
+/*
+ * pagedkv.h -- C ABI of the paged KV cache hot path for AMD Instinct MI355X
+ * (CDNA4, gfx950).
+ *
+ * The KV cache of one attention layer is split into fixed physical blocks of
+ * 16 token slots; each sequence reaches its blocks through a block table that
+ * maps logical block j (tokens 16j .. 16j+15) to a physical block id
+ * ("vLLM 引擎解剖", section "PagedAttention：为 KV 缓存分页", Fig. 2).
+ *
+ * Layouts (all row-major, contiguous):
+ *   k_cache, v_cache  [num_blocks][num_kv_heads][16][head_dim]  cache dtype
+ *   block_tables      int32 [num_seqs][max_blocks_per_seq]
+ *   query / out       [num_tokens][num_q_heads][head_dim]       q dtype
+ *   key / value       [num_tokens][num_kv_heads][head_dim]      source dtype
+ *   slot_mapping      int64 [num_tokens]; slot = block * 16 + offset
+ * Query head h reads kv head h / (num_q_heads / num_kv_heads).
+ *
+ * Ownership and threading: the caller allocates every buffer (device memory
+ * unless stated otherwise) and keeps it alive until the work it was passed
+ * to has finished on the stream.  The library allocates no memory, keeps no
+ * mutable global state and may be called from several threads.  Every call
+ * validates its host-side arguments synchronously, then enqueues its kernels
+ * on `stream` (a hipStream_t; NULL = the null stream) and returns without
+ * waiting.
+ *
+ * Errors: a non-zero pkv_status means nothing was enqueued (except
+ * PKV_ERR_LAUNCH, reported when the runtime rejects a launch).  Device-resident
+ * index data (block tables, slots, lengths, copy pairs) is not inspected on
+ * the host; it must satisfy the preconditions stated per call.  Block ids
+ * outside [0, num_blocks) are never dereferenced: such a block contributes
+ * nothing to attention and such a slot or copy is skipped, so a violated
+ * precondition gives a wrong result, never an out-of-bounds access.
+ *
+ * Device pointers must be 16-byte aligned.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t pkv_status;
+enum {
+  PKV_OK = 0,
+  PKV_ERR_NULL = 1,        /* a required pointer is NULL                    */
+  PKV_ERR_ALIGN = 2,       /* a device pointer is not 16-byte aligned       */
+  PKV_ERR_SHAPE = 3,       /* inconsistent or negative sizes                */
+  PKV_ERR_UNSUPPORTED = 4, /* head_dim / dtype / group size not built       */
+  PKV_ERR_WORKSPACE = 5,   /* decode workspace missing or too small         */
+  PKV_ERR_LAUNCH = 6       /* the HIP runtime rejected a kernel launch      */
+};
+
+typedef int32_t pkv_dtype;
+enum {
+  PKV_F32 = 0,      /* IEEE binary32                                          */
+  PKV_BF16 = 1,     /* bfloat16 (upper half of a binary32)                    */
+  PKV_FP8_E4M3 = 2  /* OCP fp8 E4M3 ("fn": no inf, max 448), cache dtype only */
+};
+
+#define PKV_BLOCK_SIZE 16
+
+/* Tokens per physical block (16: the default block size of "vLLM 引擎解剖",
+ * section "PagedAttention：为 KV 缓存分页"). */
+int32_t pkv_block_size(void);
+
+/* Static, NUL-terminated description of a status code. */
+const char* pkv_status_string(pkv_status status);
+
+/* Bytes of KV cache one token occupies over a whole model:
+ * 2 (key and value) x bytes_per_elem x num_layers x num_kv_heads x head_dim
+ * ("vLLM 引擎解剖", section "KV 缓存需要多少内存？", the formula of Table 1).
+ * Returns -1 if any argument is negative. Host-only, no GPU work. */
+int64_t kv_bytes_per_token(int32_t num_layers, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t bytes_per_elem);
+
+/*
+ * compute_slot_mapping -- the cache slot of every token scheduled this step.
+ *
+ * One step is the unified schedule {request: num_tokens} ("vLLM 引擎解剖",
+ * section "V1：统一调度预填充与解码"; "v1/v0 区别", §3.1 "Token 预算"):
+ * request r brings the tokens query_start_loc[r] .. query_start_loc[r+1]-1
+ * of the flattened batch, and its i-th token sits at sequence position
+ * p = num_computed_tokens[r] + i.  Its slot is
+ *   block_tables[r][p / 16] * 16 + p % 16            (Fig. 2 layout).
+ *
+ *   block_tables        int32 [num_reqs][max_blocks_per_seq], device
+ *   query_start_loc     int32 [num_reqs + 1], device, non-decreasing, [0] = 0,
+ *                       [num_reqs] = num_tokens
+ *   num_computed_tokens int32 [num_reqs], device, >= 0
+ *   slot_mapping        int64 [num_tokens], device, written
+ * A position whose logical block lies beyond max_blocks_per_seq, or whose
+ * block id is outside [0, num_blocks), gets slot -1.
+ */
+pkv_status compute_slot_mapping(const int32_t* block_tables,
+                                int32_t max_blocks_per_seq,
+                                const int32_t* query_start_loc,
+                                const int32_t* num_computed_tokens,
+                                int32_t num_reqs, int32_t num_blocks,
+                                int64_t* slot_mapping, int32_t num_tokens,
+                                void* stream);
+
+/*
+ * reshape_and_cache -- write each token's K and V into its cache slot.
+ *
+ * The forward pass computes every new token's key and value and stores them
+ * in the KV cache, from where later steps read them ("vLLM 引擎解剖", section
+ * "预填充、解码与三个时延指标").  For token t with slot s >= 0, for every kv head:
+ *   k_cache[s / 16][head][s % 16][:] = enc(key[t][head][:])  (same for V)
+ * Equal source and cache dtypes copy the bits.  An fp8 cache stores
+ *   E4M3(fp32(x) / k_scale)   (v_scale for V)
+ * with the division in binary32 (correctly rounded), round to nearest even,
+ * saturation to +-448, NaN -> 0x7F with the sign kept, signed zero kept.
+ * Negative slots are skipped.  Supported (src, cache): (F32, F32),
+ * (BF16, BF16), (BF16, FP8_E4M3), (F32, FP8_E4M3).
+ * Precondition: slots of one call are distinct.
+ */
+pkv_status reshape_and_cache(const void* key, const void* value,
+                             void* k_cache, void* v_cache,
+                             const int64_t* slot_mapping, int32_t num_tokens,
+                             int32_t num_kv_heads, int32_t head_dim,
+                             int32_t num_blocks, pkv_dtype src_dtype,
+                             pkv_dtype cache_dtype, float k_scale,
+                             float v_scale, void* stream);
+
+/*
+ * copy_blocks -- copy whole physical blocks, in every layer.
+ *
+ * Shared blocks are read-only; a sequence about to write into a block that
+ * other sequences still reference gets its own copy and only its own table
+ * is repointed ("vLLM 引擎解剖", section "PagedAttention：为 KV 缓存分页",
+ * copy-on-write).  Such copies travel with each step as a list of
+ * (src, dst) pairs ("v1/v0 区别", §2.1 "V0 引擎循环", blocks_to_copy).
+ *
+ *   k_caches, v_caches  HOST arrays of num_layers device pointers
+ *   block_mapping       int64 [num_pairs][2] = (src, dst), device
+ *   block_bytes         bytes of one block of one layer's K (or V) cache:
+ *                       num_kv_heads * 16 * head_dim * element size; a
+ *                       positive multiple of 16
+ * For each pair and layer: K[dst] = K[src], V[dst] = V[src].
+ * Precondition: destinations are distinct and none is also a source.
+ */
+pkv_status copy_blocks(void* const* k_caches, void* const* v_caches,
+                       int32_t num_layers, const int64_t* block_mapping,
+                       int32_t num_pairs, int32_t num_blocks,
+                       int64_t block_bytes, void* stream);
+
+/*
+ * paged_attention_decode -- one query token per sequence attends to its whole
+ * paged KV history; decode streams the entire cache once per step and is
+ * bound by memory bandwidth ("vLLM 引擎解剖", section "预填充、解码与三个时延指标").
+ *
+ * For sequence s and query head h, with L = context_lens[s] (the query's own
+ * token included, its K/V already written):
+ *   out[s][h] = softmax_j(q[s][h] . K_j * softmax_scale) . V_j,  j < L
+ * where K_j, V_j are read through block_tables[s] and an fp8 cache element
+ * c stands for value(c) * k_scale (v_scale for V).  L == 0 gives zeros.
+ *
+ * The context is cut into partitions of partition_tokens tokens (0 = let the
+ * library choose; else a positive multiple of 16 up to 1024); each partition
+ * produces a (max, sum, weighted-value) partial in `workspace` and a second
+ * kernel merges the partials with a log-sum-exp rescale.  The workspace is
+ * caller-owned device memory of at least
+ * paged_attention_decode_workspace_size(...) bytes for the same arguments.
+ *
+ *   out, query          [num_seqs][num_q_heads][head_dim], q dtype
+ *   context_lens        int32 [num_seqs], device, 0 <= L <= max_context_len
+ *   block_tables        int32 [num_seqs][max_blocks_per_seq], device; entries
+ *                       0 .. ceil(L/16)-1 are read, the rest never
+ * Supported: head_dim 64 or 128; num_q_heads a multiple of num_kv_heads with
+ * a group of at most 8; (q, kv) dtypes (F32, F32), (BF16, BF16),
+ * (BF16, FP8_E4M3).  Accumulation is fp32; the output is rounded to the q
+ * dtype (nearest even).
+ */
+size_t paged_attention_decode_workspace_size(int32_t num_seqs,
+                                             int32_t num_q_heads,
+                                             int32_t num_kv_heads,
+                                             int32_t head_dim,
+                                             int32_t max_context_len,
+                                             int32_t partition_tokens);
+
+/* The partition length paged_attention_decode uses for these arguments. */
+int32_t paged_attention_decode_partition_tokens(int32_t num_seqs,
+                                                int32_t num_kv_heads,
+                                                int32_t max_context_len,
+                                                int32_t partition_tokens);
+
+pkv_status paged_attention_decode(void* out, const void* query,
+                                  const void* k_cache, const void* v_cache,
+                                  int32_t num_blocks,
+                                  const int32_t* block_tables,
+                                  int32_t max_blocks_per_seq,
+                                  const int32_t* context_lens,
+                                  int32_t num_seqs, int32_t max_context_len,
+                                  int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, float softmax_scale,
+                                  pkv_dtype q_dtype, pkv_dtype kv_dtype,
+                                  float k_scale, float v_scale,
+                                  int32_t partition_tokens, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/*
+ * paged_attention_prefill_chunk -- attention for the query rows of prompt
+ * chunks scheduled this step.  A long prompt is split into chunks that share
+ * steps with decodes ("vLLM 引擎解剖", section "V1：统一调度预填充与解码",
+ * Fig. 3); per request the kernel needs the query length, the context
+ * length and the block table ("v1/v0 区别", §3.1 "Token 预算").
+ *
+ * Request r owns query rows query_start_loc[r] .. query_start_loc[r+1]-1;
+ * with c = num_computed_tokens[r] (tokens already in the cache before this
+ * chunk, e.g. a prefix-cache hit), row i sits at position p = c + i and
+ * attends causally to positions 0 .. p (inclusive) through block_tables[r]:
+ *   out[row][h] = softmax_{j<=p}(q[row][h] . K_j * softmax_scale) . V_j
+ * The chunk's own K/V must already be in the cache (reshape_and_cache).
+ *
+ *   out, query        [num_q_tokens][num_q_heads][head_dim], q dtype
+ *   query_start_loc   int32 [num_reqs + 1], device, [0] = 0,
+ *                     [num_reqs] = num_q_tokens, steps <= max_query_len
+ *   num_computed_tokens int32 [num_reqs], device
+ * Supported: head_dim 128 with (BF16, BF16) (the MFMA path); head_dim 64 or
+ * 128 with (F32, F32) and (BF16, FP8_E4M3) are also accepted.  Group size
+ * at most 8.  Accumulation is fp32.
+ */
+pkv_status paged_attention_prefill_chunk(void* out, const void* query,
+                                         const void* k_cache,
+                                         const void* v_cache,
+                                         int32_t num_blocks,
+                                         const int32_t* block_tables,
+                                         int32_t max_blocks_per_seq,
+                                         const int32_t* query_start_loc,
+                                         const int32_t* num_computed_tokens,
+                                         int32_t num_reqs,
+                                         int32_t num_q_tokens,
+                                         int32_t max_query_len,
+                                         int32_t num_q_heads,
+                                         int32_t num_kv_heads,
+                                         int32_t head_dim, float softmax_scale,
+                                         pkv_dtype q_dtype, pkv_dtype kv_dtype,
+                                         float k_scale, float v_scale,
+                                         void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

@@ -1,0 +1,219 @@
+"""ctypes marshalling for libpagedkv.so.  Argument checks and pointers only."""
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+BLOCK_SIZE = 16
+
+PKV_F32, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2
+_STATUS = {0: "ok", 1: "null pointer", 2: "misaligned pointer", 3: "bad shape",
+           4: "unsupported", 5: "workspace too small", 6: "launch failed"}
+
+
+class LibraryNotBuilt(RuntimeError):
+    """libpagedkv.so is missing or failed to load."""
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, fn, status, text):
+        super().__init__(f"{fn} failed: status {status} ({text})")
+        self.status = status
+
+
+def library_path():
+    return os.environ.get("PAGEDKV_LIB", os.path.join(HERE, "libpagedkv.so"))
+
+
+_lib = None
+
+_c = ctypes
+_P, _I32, _I64, _F, _SZ = _c.c_void_p, _c.c_int32, _c.c_int64, _c.c_float, _c.c_size_t
+_SIGNATURES = {
+    "pkv_block_size": (_I32, []),
+    "pkv_status_string": (_c.c_char_p, [_I32]),
+    "kv_bytes_per_token": (_I64, [_I32, _I32, _I32, _I32]),
+    "compute_slot_mapping": (_I32, [_P, _I32, _P, _P, _I32, _I32, _P, _I32, _P]),
+    "reshape_and_cache": (_I32, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
+                                 _I32, _F, _F, _P]),
+    "copy_blocks": (_I32, [_P, _P, _I32, _P, _I32, _I32, _I64, _P]),
+    "paged_attention_decode_workspace_size": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32]),
+    "paged_attention_decode_partition_tokens": (_I32, [_I32, _I32, _I32, _I32]),
+    "paged_attention_decode": (_I32, [_P, _P, _P, _P, _I32, _P, _I32, _P, _I32, _I32,
+                                      _I32, _I32, _I32, _F, _I32, _I32, _F, _F, _I32,
+                                      _P, _SZ, _P]),
+    "paged_attention_prefill_chunk": (_I32, [_P, _P, _P, _P, _I32, _P, _I32, _P, _P,
+                                             _I32, _I32, _I32, _I32, _I32, _I32, _F,
+                                             _I32, _I32, _F, _F, _P]),
+}
+EXPORTED = tuple(_SIGNATURES)
+
+
+def library():
+    """The loaded library (loaded once).  torch is imported first so that the
+    library binds to the HIP runtime torch already uses."""
+    global _lib
+    if _lib is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise LibraryNotBuilt(
+                f"{path} not found; build it with python -m paged_kv_cache_84_amd.build")
+        try:
+            lib = ctypes.CDLL(path)
+        except OSError as e:
+            raise LibraryNotBuilt(f"cannot load {path}: {e}") from e
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = lib
+    return _lib
+
+
+def _check(fn, status):
+    if status != 0:
+        text = library().pkv_status_string(status).decode()
+        raise PagedKVError(fn, status, text)
+
+
+def _dtype_code(t, what):
+    if t.dtype == torch.float32:
+        return PKV_F32
+    if t.dtype == torch.bfloat16:
+        return PKV_BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return PKV_FP8_E4M3
+    raise TypeError(f"{what}: unsupported dtype {t.dtype}")
+
+
+def _dev(t, what, dtype=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{what} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(t):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def kv_bytes_per_token(num_layers, num_kv_heads, head_dim, bytes_per_elem):
+    return int(library().kv_bytes_per_token(num_layers, num_kv_heads, head_dim,
+                                            bytes_per_elem))
+
+
+def compute_slot_mapping(block_tables, query_start_loc, num_computed_tokens,
+                         num_blocks, num_tokens, out=None):
+    """int64 [num_tokens] slots of the step's tokens (see the header)."""
+    num_reqs = num_computed_tokens.shape[0]
+    if out is None:
+        out = torch.empty(num_tokens, dtype=torch.int64, device=block_tables.device)
+    assert block_tables.dim() == 2 and block_tables.shape[0] >= num_reqs
+    assert query_start_loc.shape[0] == num_reqs + 1 and out.shape[0] >= num_tokens
+    st = library().compute_slot_mapping(
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(query_start_loc, "query_start_loc", torch.int32),
+        _dev(num_computed_tokens, "num_computed_tokens", torch.int32), num_reqs,
+        int(num_blocks), _dev(out, "slot_mapping", torch.int64), int(num_tokens),
+        _stream(out))
+    _check("compute_slot_mapping", st)
+    return out
+
+
+def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, k_scale=1.0,
+                      v_scale=1.0):
+    """Write key/value [T][Hkv][D] into the caches at the given slots."""
+    t, hkv, d = key.shape
+    assert value.shape == key.shape and key.dtype == value.dtype
+    assert k_cache.shape == v_cache.shape and k_cache.shape[1:] == (hkv, BLOCK_SIZE, d)
+    assert slot_mapping.shape[0] >= t
+    st = library().reshape_and_cache(
+        _dev(key, "key"), _dev(value, "value"), _dev(k_cache, "k_cache"),
+        _dev(v_cache, "v_cache"), _dev(slot_mapping, "slot_mapping", torch.int64),
+        t, hkv, d, k_cache.shape[0], _dtype_code(key, "key"),
+        _dtype_code(k_cache, "k_cache"), float(k_scale), float(v_scale), _stream(key))
+    _check("reshape_and_cache", st)
+
+
+def copy_blocks(k_caches, v_caches, block_mapping):
+    """Copy whole blocks (src, dst) = block_mapping[i] in every layer."""
+    n = len(k_caches)
+    assert len(v_caches) == n and n > 0
+    shape, dtype = k_caches[0].shape, k_caches[0].dtype
+    for c in list(k_caches) + list(v_caches):
+        assert c.shape == shape and c.dtype == dtype
+        _dev(c, "cache")
+    block_bytes = k_caches[0][0].numel() * k_caches[0].element_size()
+    ks = (ctypes.c_void_p * n)(*[c.data_ptr() for c in k_caches])
+    vs = (ctypes.c_void_p * n)(*[c.data_ptr() for c in v_caches])
+    pairs = block_mapping.reshape(-1, 2)
+    st = library().copy_blocks(ks, vs, n, _dev(block_mapping, "block_mapping", torch.int64),
+                               pairs.shape[0], shape[0], block_bytes,
+                               _stream(k_caches[0]))
+    _check("copy_blocks", st)
+
+
+def decode_partition_tokens(num_seqs, num_kv_heads, max_context_len, partition_tokens=0):
+    return int(library().paged_attention_decode_partition_tokens(
+        num_seqs, num_kv_heads, max_context_len, partition_tokens))
+
+
+def decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                          max_context_len, partition_tokens=0):
+    return int(library().paged_attention_decode_workspace_size(
+        num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+        partition_tokens))
+
+
+def paged_attention_decode(query, k_cache, v_cache, block_tables, context_lens,
+                           max_context_len, softmax_scale, k_scale=1.0, v_scale=1.0,
+                           partition_tokens=0, out=None, workspace=None):
+    """out [S][Hq][D] (q dtype) = paged decode attention (see the header)."""
+    s, hq, d = query.shape
+    hkv = k_cache.shape[1]
+    if out is None:
+        out = torch.empty_like(query)
+    need = decode_workspace_size(s, hq, hkv, d, max_context_len, partition_tokens)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=query.device)
+    assert block_tables.shape[0] >= s and context_lens.shape[0] >= s
+    st = library().paged_attention_decode(
+        _dev(out, "out", query.dtype), _dev(query, "query"), _dev(k_cache, "k_cache"),
+        _dev(v_cache, "v_cache"), k_cache.shape[0],
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(context_lens, "context_lens", torch.int32), s, int(max_context_len), hq,
+        hkv, d, float(softmax_scale), _dtype_code(query, "query"),
+        _dtype_code(k_cache, "k_cache"), float(k_scale), float(v_scale),
+        int(partition_tokens), _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(query))
+    _check("paged_attention_decode", st)
+    return out
+
+
+def paged_attention_prefill_chunk(query, k_cache, v_cache, block_tables,
+                                  query_start_loc, num_computed_tokens, max_query_len,
+                                  softmax_scale, k_scale=1.0, v_scale=1.0, out=None):
+    """out [Tq][Hq][D] (q dtype) = causal attention of the chunks' rows."""
+    t, hq, d = query.shape
+    hkv = k_cache.shape[1]
+    r = num_computed_tokens.shape[0]
+    if out is None:
+        out = torch.empty_like(query)
+    assert query_start_loc.shape[0] == r + 1 and block_tables.shape[0] >= r
+    st = library().paged_attention_prefill_chunk(
+        _dev(out, "out", query.dtype), _dev(query, "query"), _dev(k_cache, "k_cache"),
+        _dev(v_cache, "v_cache"), k_cache.shape[0],
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(query_start_loc, "query_start_loc", torch.int32),
+        _dev(num_computed_tokens, "num_computed_tokens", torch.int32), r, t,
+        int(max_query_len), hq, hkv, d, float(softmax_scale),
+        _dtype_code(query, "query"), _dtype_code(k_cache, "k_cache"), float(k_scale),
+        float(v_scale), _stream(query))
+    _check("paged_attention_prefill_chunk", st)
+    return out

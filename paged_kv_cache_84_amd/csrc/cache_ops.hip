@@ -1,0 +1,255 @@
+// Slot mapping, cache writes and block copies: the byte-moving calls of the
+// paged KV cache ("vLLM 引擎解剖", section "PagedAttention：为 KV 缓存分页").
+// All three are bound by HBM traffic; they use 16-byte accesses and grids of
+// one workgroup per token / per copied block.
+
+#include "abi_util.h"
+#include "common.h"
+
+namespace pkv {
+
+// ------------------------------------------------------------ slot mapping
+
+// One workgroup per request; its threads walk the request's tokens.
+__global__ __launch_bounds__(256) void slot_mapping_kernel(
+    const int32_t* __restrict__ block_tables, int32_t max_blocks,
+    const int32_t* __restrict__ query_start_loc,
+    const int32_t* __restrict__ num_computed, int32_t num_blocks,
+    int64_t* __restrict__ slots, int32_t num_tokens) {
+  const int r = blockIdx.x;
+  const int begin = query_start_loc[r];
+  const int end = query_start_loc[r + 1];
+  const int computed = num_computed[r];
+  const int32_t* row = block_tables + int64_t(r) * max_blocks;
+  for (int t = begin + threadIdx.x; t < end; t += blockDim.x) {
+    if (t < 0 || t >= num_tokens) continue;
+    const int64_t p = int64_t(computed) + (t - begin);
+    const int64_t j = p / kBlock;
+    int64_t slot = -1;
+    if (p >= 0 && j < max_blocks) {
+      const int32_t b = row[j];
+      if (b >= 0 && b < num_blocks) slot = int64_t(b) * kBlock + p % kBlock;
+    }
+    slots[t] = slot;
+  }
+}
+
+// ------------------------------------------------------------ cache write
+
+// Eight source elements -> their cache encoding, as 16 (copy of bf16),
+// 32 (copy of fp32 = two 16-byte halves) or 8 (fp8) bytes.
+template <typename Src, typename Dst>
+struct Writer;
+
+template <>
+struct Writer<BF16, BF16> {
+  static constexpr int kElems = 8;
+  PKV_DEVICE static void run(const uint16_t* src, uint16_t* dst, float) {
+    store16(dst, load16(src));
+  }
+};
+
+template <>
+struct Writer<F32, F32> {
+  static constexpr int kElems = 4;
+  PKV_DEVICE static void run(const float* src, float* dst, float) {
+    store16(dst, load16(src));
+  }
+};
+
+template <>
+struct Writer<BF16, FP8> {
+  static constexpr int kElems = 8;
+  PKV_DEVICE static void run(const uint16_t* src, uint8_t* dst, float scale) {
+    const u32x4 v = load16(src);
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      lo |= uint32_t(f32_to_e4m3(bf16_lo(v[i]) / scale)) << (16 * i);
+      lo |= uint32_t(f32_to_e4m3(bf16_hi(v[i]) / scale)) << (16 * i + 8);
+      hi |= uint32_t(f32_to_e4m3(bf16_lo(v[i + 2]) / scale)) << (16 * i);
+      hi |= uint32_t(f32_to_e4m3(bf16_hi(v[i + 2]) / scale)) << (16 * i + 8);
+    }
+    *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+  }
+};
+
+template <>
+struct Writer<F32, FP8> {
+  static constexpr int kElems = 4;
+  PKV_DEVICE static void run(const float* src, uint8_t* dst, float scale) {
+    const u32x4 v = load16(src);
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w |= uint32_t(f32_to_e4m3(__uint_as_float(v[i]) / scale)) << (8 * i);
+    *reinterpret_cast<uint32_t*>(dst) = w;
+  }
+};
+
+// One workgroup per token: all kv heads of its K and V.
+template <typename Src, typename Dst>
+__global__ __launch_bounds__(256) void reshape_and_cache_kernel(
+    const typename Src::storage* __restrict__ key,
+    const typename Src::storage* __restrict__ value,
+    typename Dst::storage* __restrict__ k_cache,
+    typename Dst::storage* __restrict__ v_cache,
+    const int64_t* __restrict__ slots, int32_t num_kv_heads, int32_t head_dim,
+    int32_t num_blocks, float k_scale, float v_scale) {
+  using W = Writer<Src, Dst>;
+  const int t = blockIdx.x;
+  const int64_t slot = slots[t];
+  if (slot < 0 || slot >= int64_t(num_blocks) * kBlock) return;
+  const int64_t block = slot / kBlock;
+  const int offset = int(slot % kBlock);
+  const int vecs_per_head = head_dim / W::kElems;
+  const int vecs = num_kv_heads * vecs_per_head;
+  const int64_t src_base = int64_t(t) * num_kv_heads * head_dim;
+  for (int i = threadIdx.x; i < 2 * vecs; i += blockDim.x) {
+    const bool is_v = i >= vecs;
+    const int iv = is_v ? i - vecs : i;
+    const int h = iv / vecs_per_head;
+    const int d = (iv % vecs_per_head) * W::kElems;
+    const int64_t dst =
+        ((block * num_kv_heads + h) * kBlock + offset) * head_dim + d;
+    const int64_t src = src_base + int64_t(h) * head_dim + d;
+    if (is_v)
+      W::run(value + src, v_cache + dst, v_scale);
+    else
+      W::run(key + src, k_cache + dst, k_scale);
+  }
+}
+
+// ------------------------------------------------------------ block copies
+
+constexpr int kMaxLayersPerLaunch = 64;
+struct LayerPtrs {
+  void* k[kMaxLayersPerLaunch];
+  void* v[kMaxLayersPerLaunch];
+};
+
+// grid: (pair, layer in this launch, K or V); 16-byte vector copy.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(
+    LayerPtrs ptrs, const int64_t* __restrict__ mapping, int32_t num_blocks,
+    int64_t block_bytes) {
+  const int pair = blockIdx.x;
+  const int layer = blockIdx.y;
+  const int64_t src = mapping[2 * pair];
+  const int64_t dst = mapping[2 * pair + 1];
+  if (src < 0 || dst < 0 || src >= num_blocks || dst >= num_blocks) return;
+  char* base = static_cast<char*>(blockIdx.z == 0 ? ptrs.k[layer] : ptrs.v[layer]);
+  const u32x4* s = reinterpret_cast<const u32x4*>(base + src * block_bytes);
+  u32x4* d = reinterpret_cast<u32x4*>(base + dst * block_bytes);
+  const int64_t n = block_bytes / 16;
+  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) d[i] = s[i];
+}
+
+}  // namespace pkv
+
+// ===================================================================== ABI
+
+using namespace pkv;
+
+extern "C" pkv_status compute_slot_mapping(const int32_t* block_tables,
+                                           int32_t max_blocks_per_seq,
+                                           const int32_t* query_start_loc,
+                                           const int32_t* num_computed_tokens,
+                                           int32_t num_reqs, int32_t num_blocks,
+                                           int64_t* slot_mapping,
+                                           int32_t num_tokens, void* stream) {
+  if (num_reqs < 0 || num_tokens < 0 || max_blocks_per_seq < 0 || num_blocks < 0)
+    return PKV_ERR_SHAPE;
+  if (num_reqs == 0 || num_tokens == 0) return PKV_OK;
+  if (!block_tables || !query_start_loc || !num_computed_tokens || !slot_mapping)
+    return PKV_ERR_NULL;
+  if (!aligned(slot_mapping, 8)) return PKV_ERR_ALIGN;
+  hipLaunchKernelGGL(slot_mapping_kernel, dim3(num_reqs), dim3(256), 0,
+                     as_stream(stream), block_tables, max_blocks_per_seq,
+                     query_start_loc, num_computed_tokens, num_blocks,
+                     slot_mapping, num_tokens);
+  return launch_status();
+}
+
+template <typename Src, typename Dst>
+static pkv_status launch_write(const void* key, const void* value, void* kc,
+                               void* vc, const int64_t* slots, int32_t t,
+                               int32_t hkv, int32_t d, int32_t nb, float ks,
+                               float vs, void* stream) {
+  hipLaunchKernelGGL((reshape_and_cache_kernel<Src, Dst>), dim3(t), dim3(256), 0,
+                     as_stream(stream),
+                     static_cast<const typename Src::storage*>(key),
+                     static_cast<const typename Src::storage*>(value),
+                     static_cast<typename Dst::storage*>(kc),
+                     static_cast<typename Dst::storage*>(vc), slots, hkv, d, nb,
+                     ks, vs);
+  return launch_status();
+}
+
+extern "C" pkv_status reshape_and_cache(const void* key, const void* value,
+                                        void* k_cache, void* v_cache,
+                                        const int64_t* slot_mapping,
+                                        int32_t num_tokens, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t num_blocks,
+                                        pkv_dtype src_dtype,
+                                        pkv_dtype cache_dtype, float k_scale,
+                                        float v_scale, void* stream) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || num_blocks < 0)
+    return PKV_ERR_SHAPE;
+  if (head_dim % 8 != 0) return PKV_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PKV_OK;
+  if (!key || !value || !k_cache || !v_cache || !slot_mapping) return PKV_ERR_NULL;
+  if (!aligned(key, 16) || !aligned(value, 16) || !aligned(k_cache, 16) ||
+      !aligned(v_cache, 16) || !aligned(slot_mapping, 8))
+    return PKV_ERR_ALIGN;
+  if (cache_dtype == PKV_FP8_E4M3 && !(k_scale > 0.f && v_scale > 0.f))
+    return PKV_ERR_SHAPE;
+  if (src_dtype == PKV_BF16 && cache_dtype == PKV_BF16)
+    return launch_write<BF16, BF16>(key, value, k_cache, v_cache, slot_mapping,
+                                    num_tokens, num_kv_heads, head_dim,
+                                    num_blocks, k_scale, v_scale, stream);
+  if (src_dtype == PKV_F32 && cache_dtype == PKV_F32)
+    return launch_write<F32, F32>(key, value, k_cache, v_cache, slot_mapping,
+                                  num_tokens, num_kv_heads, head_dim, num_blocks,
+                                  k_scale, v_scale, stream);
+  if (src_dtype == PKV_BF16 && cache_dtype == PKV_FP8_E4M3)
+    return launch_write<BF16, FP8>(key, value, k_cache, v_cache, slot_mapping,
+                                   num_tokens, num_kv_heads, head_dim,
+                                   num_blocks, k_scale, v_scale, stream);
+  if (src_dtype == PKV_F32 && cache_dtype == PKV_FP8_E4M3)
+    return launch_write<F32, FP8>(key, value, k_cache, v_cache, slot_mapping,
+                                  num_tokens, num_kv_heads, head_dim, num_blocks,
+                                  k_scale, v_scale, stream);
+  return PKV_ERR_UNSUPPORTED;
+}
+
+extern "C" pkv_status copy_blocks(void* const* k_caches, void* const* v_caches,
+                                  int32_t num_layers,
+                                  const int64_t* block_mapping,
+                                  int32_t num_pairs, int32_t num_blocks,
+                                  int64_t block_bytes, void* stream) {
+  if (num_layers < 0 || num_pairs < 0 || num_blocks < 0 || block_bytes <= 0 ||
+      block_bytes % 16 != 0)
+    return PKV_ERR_SHAPE;
+  if (num_layers == 0 || num_pairs == 0) return PKV_OK;
+  if (!k_caches || !v_caches || !block_mapping) return PKV_ERR_NULL;
+  if (!aligned(block_mapping, 8)) return PKV_ERR_ALIGN;
+  for (int l = 0; l < num_layers; ++l) {
+    if (!k_caches[l] || !v_caches[l]) return PKV_ERR_NULL;
+    if (!aligned(k_caches[l], 16) || !aligned(v_caches[l], 16)) return PKV_ERR_ALIGN;
+  }
+  for (int first = 0; first < num_layers; first += kMaxLayersPerLaunch) {
+    const int n = num_layers - first < kMaxLayersPerLaunch ? num_layers - first
+                                                           : kMaxLayersPerLaunch;
+    LayerPtrs ptrs = {};
+    for (int i = 0; i < n; ++i) {
+      ptrs.k[i] = k_caches[first + i];
+      ptrs.v[i] = v_caches[first + i];
+    }
+    hipLaunchKernelGGL(copy_blocks_kernel, dim3(num_pairs, n, 2), dim3(256), 0,
+                       as_stream(stream), ptrs, block_mapping, num_blocks,
+                       block_bytes);
+    const pkv_status st = launch_status();
+    if (st != PKV_OK) return st;
+  }
+  return PKV_OK;
+}
