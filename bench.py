@@ -169,6 +169,42 @@ def bench_mixed(args, pk, C):
             "decode_gbs": round(decode_bytes(s) / (ms_decode * 1e-3) / 1e9, 1)}
 
 
+def bench_extra_decode(args, pk, C, which):
+    """Optional legs: the fp8 long-context decode (64/8 heads, 6 x 131,072
+    tokens, 512-token partitions) or the 32-layer MHA decode step (32 x 8,192
+    tokens), each timed as decode calls on inputs resident in HBM."""
+    if which == "longctx":
+        s = C.config5(device="cuda")
+        ds = pk.step.DeviceStep(s, partition_tokens=512)
+        layers = [0]
+        name = ("Llama-3.1-70B-shaped long-context decode, one layer: 6 x 131072 "
+                "tokens, 64 q / 8 kv heads, d128, bf16 q, fp8 e4m3 K/V, 512-token "
+                "partitions")
+    else:
+        s = C.config3(device="cuda")
+        ds = pk.step.DeviceStep(s)
+        layers = list(range(s.num_layers))
+        name = ("Llama-2-7B-shaped MHA decode, 32 layers back to back: 32 x 8192 "
+                "tokens, 32/32 heads, d128, bf16")
+    stream = torch.cuda.current_stream()
+
+    def run(i):
+        for layer in layers:
+            ds.decode(layer)
+
+    for i in range(2):
+        run(i)
+    iters = max(3, min(args.steps, 10))
+    ms = time_region(run, iters, stream)
+    nbytes = decode_bytes(s) * len(layers)
+    tokens = int(s.decode_context_lens.sum()) * len(layers)
+    return {"workload": name, "ms_per_step": round(ms, 4),
+            "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "kv_tokens_per_s": round(tokens / (ms * 1e-3), 1),
+            "algorithmic_bytes": nbytes}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -176,6 +212,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mixed", action="store_true")
+    ap.add_argument("--longctx", action="store_true",
+                    help="also time the fp8 long-context decode (1.6 GB of KV)")
+    ap.add_argument("--mha", action="store_true",
+                    help="also time the 32-layer MHA decode step (128 GiB of KV)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the paged-attention path here is "
@@ -225,6 +265,10 @@ def main():
     }
     if not args.no_mixed:
         line["mixed_step"] = bench_mixed(args, pk, C)
+    if args.longctx:
+        line["longctx_decode"] = bench_extra_decode(args, pk, C, "longctx")
+    if args.mha:
+        line["mha_decode"] = bench_extra_decode(args, pk, C, "mha")
     if cpu is not None:
         line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)

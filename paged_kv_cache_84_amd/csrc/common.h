@@ -131,4 +131,20 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 PKV_DEVICE u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 PKV_DEVICE void store16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
+// Buffer resource over `bytes` bytes at `base` (raw buffer, 32-bit format
+// field as the gfx9 family expects); loads past `bytes` return zeros.
+constexpr int kRawBufferFlags = 0x00020000;
+PKV_DEVICE __amdgpu_buffer_rsrc_t tile_resource(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kRawBufferFlags);
+}
+// K/V tiles are read once per step: non-temporal loads (cache policy "nt")
+// keep them from displacing reused data and stream measurably faster.
+#ifndef PKV_TILE_LOAD_AUX
+#define PKV_TILE_LOAD_AUX 2
+#endif
+PKV_DEVICE u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t offset) {
+  return __builtin_bit_cast(
+      u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, offset, 0, PKV_TILE_LOAD_AUX));
+}
+
 }  // namespace pkv

@@ -38,8 +38,11 @@ namespace pkv {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRaiseThreshold = 8.0f;   // log2 units
 
+#ifndef PKV_DECODE_MAX_HEADS_PER_WAVE
+#define PKV_DECODE_MAX_HEADS_PER_WAVE 4
+#endif
 #ifndef PKV_DECODE_WAVES_PER_EU
-#define PKV_DECODE_WAVES_PER_EU 2
+#define PKV_DECODE_WAVES_PER_EU 3
 #endif
 
 template <typename QT, typename KVT, int D>
@@ -62,11 +65,6 @@ struct Geom {
   static_assert(kKChunks >= 1 && kKPasses >= 1 && kVLoads >= 1, "unsupported row size");
 };
 
-template <typename QT, typename KVT, int D>
-struct Tile {
-  u32x4 k[Geom<QT, KVT, D>::kKLoads];
-  u32x4 v[Geom<QT, KVT, D>::kVLoads];
-};
 
 // q . k over one 16-byte piece of a K row.
 template <typename QT, typename KVT>
@@ -140,78 +138,113 @@ template <typename QT, typename KVT, int D, int GW>
 struct DecodeWave {
   using G = Geom<QT, KVT, D>;
   using KS = typename KVT::storage;
+  static constexpr int kQPieces = G::kQWords / 4;   // 16-byte q pieces per K piece
+  // LDS of one wave: the q rows of its heads (read back as fragments every
+  // block, so they cost no registers) and the 16 x GW weights of a block.
+  static constexpr int kQBytes = GW * D * QT::bytes;
+  static constexpr int kLdsBytes = kQBytes + kBlock * GW * 4;
 
-  uint32_t q[GW][G::kKChunks][G::kQWords];
   float acc[GW][G::kElems];
   float m[GW];      // running max of scaled scores (log2 units), wave-uniform
   float l[GW];      // this lane's share of the sum of weights
   int lane, krow, kq, vrow0, vcol;
+  char* lds;        // this wave's LDS
 
-  PKV_DEVICE void init(const typename QT::storage* qrow[GW]) {
+  PKV_DEVICE const u32x4* qpiece(int h, int c, int w4) const {
+    // 16-byte piece w4 of K piece (c * kKLanes + kq) of head h
+    return reinterpret_cast<const u32x4*>(
+        lds + h * D * QT::bytes + ((c * G::kKLanes + kq) * kQPieces + w4) * 16);
+  }
+  PKV_DEVICE float* plds() const { return reinterpret_cast<float*>(lds + kQBytes); }
+
+  PKV_DEVICE void init(const typename QT::storage* qrow[GW], char* wave_lds) {
     lane = lane_id();
     krow = lane / G::kKLanes;
     kq = lane % G::kKLanes;
     vrow0 = lane / G::kVLanesPerRow;
     vcol = lane % G::kVLanesPerRow;
+    lds = wave_lds;
+    // q rows -> LDS, 16 bytes per lane per step
+    constexpr int kRowPieces = D * QT::bytes / 16;
 #pragma unroll
     for (int h = 0; h < GW; ++h) {
-#pragma unroll
-      for (int c = 0; c < G::kKChunks; ++c) {
-        const int elem0 = (c * G::kKLanes + kq) * G::kElems;
-        const uint32_t* src = reinterpret_cast<const uint32_t*>(qrow[h] + elem0);
-#pragma unroll
-        for (int w = 0; w < G::kQWords; w += 4) {
-          const u32x4 x = load16(src + w);
-          q[h][c][w] = x[0];
-          q[h][c][w + 1] = x[1];
-          q[h][c][w + 2] = x[2];
-          q[h][c][w + 3] = x[3];
-        }
-      }
+      for (int pc = lane; pc < kRowPieces; pc += kWave)
+        *reinterpret_cast<u32x4*>(lds + h * D * QT::bytes + pc * 16) =
+            load16(reinterpret_cast<const char*>(qrow[h]) + pc * 16);
       m[h] = -INFINITY;
       l[h] = 0.f;
 #pragma unroll
       for (int e = 0; e < G::kElems; ++e) acc[h][e] = 0.f;
     }
+    __builtin_amdgcn_wave_barrier();
   }
 
-  // Issue the loads of one tile: K pieces first, then V.
-  PKV_DEVICE void load(Tile<QT, KVT, D>& t, const KS* ktile, const KS* vtile) const {
-    const char* kb = reinterpret_cast<const char*>(ktile) + krow * G::kRowBytes + kq * 16;
+  // The K and V pieces of one tile, issued separately.  Each (block, kv head)
+  // tile is addressed through a buffer resource (base and size in scalar
+  // registers) plus a fixed per-lane offset, so the loads need no per-step
+  // vector address arithmetic and cannot reach outside the tile.
+  static constexpr int kTileBytes = kBlock * G::kRowBytes;
+  PKV_DEVICE void load_k(u32x4 (&k)[G::kKLoads], const KS* ktile) const {
+    const auto rk = tile_resource(ktile, kTileBytes);
+    const uint32_t koff = uint32_t(krow * G::kRowBytes + kq * 16);
 #pragma unroll
     for (int ps = 0; ps < G::kKPasses; ++ps)
 #pragma unroll
       for (int c = 0; c < G::kKChunks; ++c)
-        t.k[ps * G::kKChunks + c] =
-            load16(kb + ps * G::kKRowsPerPass * G::kRowBytes + c * 16 * G::kKLanes);
-    const char* vb = reinterpret_cast<const char*>(vtile) + lane * 16;
+        k[ps * G::kKChunks + c] = buffer_load16(
+            rk, koff + (ps * G::kKRowsPerPass * G::kRowBytes + c * 16 * G::kKLanes));
+  }
+  PKV_DEVICE void load_v(u32x4 (&v)[G::kVLoads], const KS* vtile) const {
+    const auto rv = tile_resource(vtile, kTileBytes);
+    const uint32_t voff = uint32_t(lane * 16);
 #pragma unroll
-    for (int j = 0; j < G::kVLoads; ++j) t.v[j] = load16(vb + j * 1024);
+    for (int j = 0; j < G::kVLoads; ++j) v[j] = buffer_load16(rv, voff + j * 1024);
   }
 
-  // One tile; `valid_rows` < 16 only for the last, partly filled block.
-  template <bool kMasked>
-  PKV_DEVICE void consume(const Tile<QT, KVT, D>& t, int valid_rows, float scale_log2,
-                          float* plds) {
-    float s[G::kKPasses][GW];
+  // Scores of one tile's rows (scaled, base 2), masked past valid_rows, and
+  // whether any of them exceeds the running max by more than the threshold.
+  PKV_DEVICE bool scores(const u32x4 (&k)[G::kKLoads], int valid_rows, float scale_log2,
+                         float (&s)[G::kKPasses][GW]) const {
     bool raise = false;
 #pragma unroll
-    for (int ps = 0; ps < G::kKPasses; ++ps) {
-      const int row = krow + ps * G::kKRowsPerPass;
+    for (int h = 0; h < GW; ++h) {
+      uint32_t qf[G::kKChunks][G::kQWords];
 #pragma unroll
-      for (int h = 0; h < GW; ++h) {
+      for (int c = 0; c < G::kKChunks; ++c)
+#pragma unroll
+        for (int w4 = 0; w4 < kQPieces; ++w4) {
+          const u32x4 x = *qpiece(h, c, w4);
+          qf[c][4 * w4] = x[0];
+          qf[c][4 * w4 + 1] = x[1];
+          qf[c][4 * w4 + 2] = x[2];
+          qf[c][4 * w4 + 3] = x[3];
+        }
+#pragma unroll
+      for (int ps = 0; ps < G::kKPasses; ++ps) {
         float a = 0.f;
 #pragma unroll
         for (int c = 0; c < G::kKChunks; ++c)
-          a = Dot<QT, KVT>::run(q[h][c], t.k[ps * G::kKChunks + c], a);
+          a = Dot<QT, KVT>::run(qf[c], k[ps * G::kKChunks + c], a);
         a = quad_sum(a);
         if (G::kKLanes == 8) a += half_mirror(a);
         a *= scale_log2;
-        if (kMasked) a = row < valid_rows ? a : -INFINITY;
+        a = (krow + ps * G::kKRowsPerPass < valid_rows) ? a : -INFINITY;
         s[ps][h] = a;
         raise |= a > m[h] + kRaiseThreshold;
       }
     }
+    return raise;
+  }
+
+  // Raise the running max where a score exceeds it by more than the
+  // threshold (rare: the branch only computes the new maxima; the rescale
+  // itself is a multiply by 1 in the common case, which keeps the
+  // accumulators in place instead of forking them across the branch), then
+  // the weights -> LDS.
+  PKV_DEVICE void weights(float (&s)[G::kKPasses][GW], bool raise) {
+    float alpha[GW];
+#pragma unroll
+    for (int h = 0; h < GW; ++h) alpha[h] = 1.0f;
     if (__builtin_expect(__ballot(raise) != 0, 0)) {
 #pragma unroll
       for (int h = 0; h < GW; ++h) {
@@ -219,43 +252,48 @@ struct DecodeWave {
 #pragma unroll
         for (int ps = 1; ps < G::kKPasses; ++ps) bm = fmaxf(bm, s[ps][h]);
         const float mn = fmaxf(m[h], wave_max(bm));
-        const float alpha = fast_exp2(m[h] - mn);
-        l[h] *= alpha;
-#pragma unroll
-        for (int e = 0; e < G::kElems; ++e) acc[h][e] *= alpha;
+        alpha[h] = fast_exp2(m[h] - mn);
         m[h] = mn;
       }
     }
-    float p[G::kKPasses][GW];
+#pragma unroll
+    for (int h = 0; h < GW; ++h) {
+      l[h] *= alpha[h];
+#pragma unroll
+      for (int e = 0; e < G::kElems; ++e) acc[h][e] *= alpha[h];
+    }
+    float* pl = plds();
 #pragma unroll
     for (int ps = 0; ps < G::kKPasses; ++ps)
 #pragma unroll
       for (int h = 0; h < GW; ++h) {
-        p[ps][h] = fast_exp2(s[ps][h] - m[h]);
-        l[h] += p[ps][h];
+        const float p = fast_exp2(s[ps][h] - m[h]);
+        l[h] += p;
+        if (kq == 0) pl[(krow + ps * G::kKRowsPerPass) * GW + h] = p;
       }
-    // scores: K layout (row = lane / kKLanes + pass offset) -> LDS -> V layout
-    if (kq == 0) {
-#pragma unroll
-      for (int ps = 0; ps < G::kKPasses; ++ps)
-#pragma unroll
-        for (int h = 0; h < GW; ++h) plds[(krow + ps * G::kKRowsPerPass) * GW + h] = p[ps][h];
-    }
     __builtin_amdgcn_wave_barrier();
+  }
+
+  // acc += p * V over the tile's rows; rows past valid_rows hold anything
+  // (unused slots), so their values are replaced by zeros.
+  PKV_DEVICE void accumulate(const u32x4 (&v)[G::kVLoads], int valid_rows) {
+    const float* pl = plds();
 #pragma unroll
     for (int j = 0; j < G::kVLoads; ++j) {
       const int row = vrow0 + j * G::kVRowsPerLoad;
-      float v[G::kElems];
-      Unpack<KVT>::run(t.v[j], v);
-      if (kMasked && row >= valid_rows) {
+      float x[G::kElems];
+      Unpack<KVT>::run(v[j], x);
+      if (valid_rows < kBlock) {
+        if (row >= valid_rows) {
 #pragma unroll
-        for (int e = 0; e < G::kElems; ++e) v[e] = 0.f;   // unused slots may hold anything
+          for (int e = 0; e < G::kElems; ++e) x[e] = 0.f;
+        }
       }
 #pragma unroll
       for (int h = 0; h < GW; ++h) {
-        const float ph = plds[row * GW + h];
+        const float ph = pl[row * GW + h];
 #pragma unroll
-        for (int e = 0; e < G::kElems; ++e) acc[h][e] = fmaf(ph, v[e], acc[h][e]);
+        for (int e = 0; e < G::kElems; ++e) acc[h][e] = fmaf(ph, x[e], acc[h][e]);
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -269,14 +307,6 @@ PKV_DEVICE void store_out<F32>(float* p, float v) { *p = v; }
 template <>
 PKV_DEVICE void store_out<BF16>(uint16_t* p, float v) { *p = f32_to_bf16(v); }
 
-// Block ids of logical blocks first .. first+63 of one table row, one per
-// lane; -1 where the entry lies beyond the row or names no physical block.
-PKV_DEVICE int32_t load_block_ids(const int32_t* row, int32_t max_blocks,
-                                  int32_t num_blocks, int first) {
-  const int j = first + lane_id();
-  int32_t b = j < max_blocks ? row[j] : -1;
-  return (b >= 0 && b < num_blocks) ? b : -1;
-}
 
 // Attend one wave's heads to tokens [start, end) of one sequence.
 template <typename QT, typename KVT, int D, int GW>
@@ -285,54 +315,50 @@ PKV_DEVICE void attend_range(DecodeWave<QT, KVT, D, GW>& w,
                              const typename KVT::storage* v_cache,
                              int32_t num_blocks, const int32_t* table,
                              int32_t max_blocks, int kvh, int num_kv_heads,
-                             int start, int end, float scale_log2, float* plds) {
+                             int start, int end, float scale_log2) {
+  using G = Geom<QT, KVT, D>;
   const int first_block = start / kBlock;
   const int nblocks = (end - start + kBlock - 1) / kBlock;
   const int last_rows = end - (first_block + nblocks - 1) * kBlock;
   const int64_t head_stride = int64_t(kBlock) * D;
   const int64_t block_stride = int64_t(num_kv_heads) * head_stride;
   auto tile_ptr = [&](const typename KVT::storage* base, int32_t b) {
-    // invalid ids were replaced by -1 and are never consumed; read block 0
-    return base + int64_t(b < 0 ? 0 : b) * block_stride + int64_t(kvh) * head_stride;
+    return base + int64_t(b) * block_stride + int64_t(kvh) * head_stride;
   };
-  const int full = last_rows == kBlock ? nblocks : nblocks - 1;
-  // Block ids come through the scalar cache, one block ahead of their use, so
-  // the vector-memory counter only ever waits for K/V tiles.  An id is
-  // checked against the pool only where it is used.
+  // Block ids come through the scalar cache, one block ahead of their use.
   auto id_at = [&](int blk) -> int32_t {
     const int lb = first_block + blk;
     return (blk < nblocks && lb < max_blocks) ? table[lb] : -1;
   };
   auto valid = [&](int32_t b) { return b >= 0 && b < num_blocks; };
-  // Two tile buffers used in turn: the next block's loads are in flight while
-  // the current block is consumed.  Every step issues one tile of loads and
-  // consumes one tile, also after the last block (the extra load re-reads the
-  // block just consumed, a cache hit) and for an invalid id (its tile is
-  // consumed with every row masked), so the number of loads in flight is the
-  // same on every path and the wait for the current tile never drains the
-  // prefetch.
-  Tile<QT, KVT, D> ta, tb;
+  // One K and one V buffer: a block's K pieces are replaced by the next
+  // block's as soon as its scores are computed, its V pieces as soon as they
+  // are accumulated, so the next tile is always in flight while the current
+  // one is worked on.  Past the last block (or for an invalid id) the loads
+  // re-read the current block, a cache hit, and the tile is fully masked:
+  // every step has the same loads in flight on every path.
+  u32x4 kt[G::kKLoads], vt[G::kVLoads];
   int32_t id_cur = id_at(0);
   int32_t id_nxt = id_at(1);
   {
     const int32_t b0 = valid(id_cur) ? id_cur : 0;
-    w.load(ta, tile_ptr(k_cache, b0), tile_ptr(v_cache, b0));
+    w.load_k(kt, tile_ptr(k_cache, b0));
+    // keep K ahead of V in the memory queue, as inside the loop
+    __builtin_amdgcn_sched_barrier(0);
+    w.load_v(vt, tile_ptr(v_cache, b0));
   }
-  auto step = [&](Tile<QT, KVT, D>& cur, Tile<QT, KVT, D>& nxt, int i) {
+  for (int i = 0; i < nblocks; ++i) {
     const int32_t id_after = id_at(i + 2);
+    const int rows = valid(id_cur) ? (i + 1 < nblocks ? kBlock : last_rows) : 0;
     const int32_t bn = valid(id_nxt) ? id_nxt : (valid(id_cur) ? id_cur : 0);
-    w.load(nxt, tile_ptr(k_cache, bn), tile_ptr(v_cache, bn));
-    if (i < full && valid(id_cur))
-      w.template consume<false>(cur, kBlock, scale_log2, plds);
-    else
-      w.template consume<true>(cur, valid(id_cur) ? last_rows : 0, scale_log2, plds);
+    float s[G::kKPasses][GW];
+    const bool raise = w.scores(kt, rows, scale_log2, s);
+    w.load_k(kt, tile_ptr(k_cache, bn));
+    w.weights(s, raise);
+    w.accumulate(vt, rows);
+    w.load_v(vt, tile_ptr(v_cache, bn));
     id_cur = id_nxt;
     id_nxt = id_after;
-  };
-  for (int i = 0; i < nblocks; i += 2) {
-    step(ta, tb, i);
-    if (i + 1 >= nblocks) break;
-    step(tb, ta, i + 1);
   }
   // merge the row groups that share a column slice, and the rows' sums
   using G = Geom<QT, KVT, D>;
@@ -361,10 +387,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PKV_DECODE_
     int32_t partition_tokens, int32_t max_parts, float* __restrict__ part_out,
     float* __restrict__ part_ml) {
   using G = Geom<QT, KVT, D>;
-  __shared__ float plds_all[4][kBlock * GW];
-  const int part = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int seq = blockIdx.z;
+  using W = DecodeWave<QT, KVT, D, GW>;
+  __shared__ __align__(16) char lds_all[4][W::kLdsBytes];
+  // (sequence, kv head) pairs are the fastest grid dimension: consecutive
+  // workgroups are dealt to the eight XCDs in turn, so each XCD gets an even
+  // share of every partition index (partitions past a short sequence's end
+  // exit at once and would otherwise pile the work onto a few XCDs).
+  const int kvh = blockIdx.x % num_kv_heads;
+  const int seq = blockIdx.x / num_kv_heads;
+  const int part = blockIdx.y;
   const int wave = threadIdx.x / kWave;
   const int len = min(context_lens[seq], max_parts * partition_tokens);
   const int start = part * partition_tokens;
@@ -377,10 +408,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PKV_DECODE_
 #pragma unroll
   for (int h = 0; h < GW; ++h)
     qrow[h] = query + (int64_t(seq) * num_q_heads + head0 + (h < heads_here ? h : 0)) * D;
-  DecodeWave<QT, KVT, D, GW> w;
-  w.init(qrow);
+  W w;
+  w.init(qrow, lds_all[wave]);
   attend_range(w, k_cache, v_cache, num_blocks, block_tables + int64_t(seq) * max_blocks,
-               max_blocks, kvh, num_kv_heads, start, end, scale_log2, plds_all[wave]);
+               max_blocks, kvh, num_kv_heads, start, end, scale_log2);
   if (w.lane < G::kVLanesPerRow) {
 #pragma unroll
     for (int h = 0; h < GW; ++h) {
@@ -414,9 +445,10 @@ __global__ __launch_bounds__(256) void prefill_rows_kernel(
     int32_t num_q_heads, int32_t num_kv_heads, int32_t group, float scale_log2,
     float v_scale) {
   using G = Geom<QT, KVT, D>;
-  __shared__ float plds_all[4][kBlock * GW];
-  const int kvh = blockIdx.y;
-  const int row = blockIdx.z;
+  using W = DecodeWave<QT, KVT, D, GW>;
+  __shared__ __align__(16) char lds_all[4][W::kLdsBytes];
+  const int kvh = blockIdx.x % num_kv_heads;
+  const int row = blockIdx.x / num_kv_heads;
   const int wave = threadIdx.x / kWave;
   // the request owning this row: last r with query_start_loc[r] <= row
   int lo = 0, hi = num_reqs - 1;
@@ -432,12 +464,12 @@ __global__ __launch_bounds__(256) void prefill_rows_kernel(
 #pragma unroll
   for (int h = 0; h < GW; ++h)
     qrow[h] = query + (int64_t(row) * num_q_heads + head0 + (h < heads_here ? h : 0)) * D;
-  DecodeWave<QT, KVT, D, GW> w;
-  w.init(qrow);
+  W w;
+  w.init(qrow, lds_all[wave]);
   const int cap = min(len, max_blocks * kBlock);
   if (cap > 0)
     attend_range(w, k_cache, v_cache, num_blocks, block_tables + int64_t(r) * max_blocks,
-                 max_blocks, kvh, num_kv_heads, 0, cap, scale_log2, plds_all[wave]);
+                 max_blocks, kvh, num_kv_heads, 0, cap, scale_log2);
   if (w.lane < G::kVLanesPerRow) {
 #pragma unroll
     for (int h = 0; h < GW; ++h) {
@@ -451,7 +483,11 @@ __global__ __launch_bounds__(256) void prefill_rows_kernel(
   }
 }
 
-// One workgroup (one wave) per (head, sequence): merge the partitions.
+// One workgroup (one wave) per (head, sequence): merge the partitions,
+//   out = sum_k e^{m_k - M} o_k / sum_k e^{m_k - M} l_k,   M = max_k m_k
+// (m in log2 units).  The weights of up to 64 partitions at a time are
+// computed one per lane and passed through LDS, so the partials' loads do not
+// wait on each other.
 template <typename QT, int D>
 __global__ __launch_bounds__(64) void decode_reduce_kernel(
     typename QT::storage* __restrict__ out, const float* __restrict__ part_out,
@@ -459,30 +495,55 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(
     int32_t num_q_heads, int32_t partition_tokens, int32_t max_parts,
     float v_scale) {
   constexpr int kPer = D / kWave;
+  __shared__ float wts[kWave];
   const int h = blockIdx.x;
   const int seq = blockIdx.y;
   const int lane = threadIdx.x;
-  const int len = context_lens[seq];
+  const int len = min(context_lens[seq], max_parts * partition_tokens);
   typename QT::storage* o = out + (int64_t(seq) * num_q_heads + h) * D;
   if (len <= 0) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) store_out<QT>(o + lane + i * kWave, 0.f);
     return;
   }
-  const int nparts = min((len + partition_tokens - 1) / partition_tokens, max_parts);
+  const int nparts = (len + partition_tokens - 1) / partition_tokens;
   const int64_t base = (int64_t(seq) * num_q_heads + h) * max_parts;
+  const float2* ml = reinterpret_cast<const float2*>(part_ml) + base;
   float big = -INFINITY;
-  for (int k = lane; k < nparts; k += kWave) big = fmaxf(big, part_ml[2 * (base + k)]);
+  for (int k = lane; k < nparts; k += kWave) big = fmaxf(big, ml[k].x);
   big = wave_max(big);
   float acc[kPer] = {};
   float den = 0.f;
-  for (int k = 0; k < nparts; ++k) {
-    const float w = fast_exp2(part_ml[2 * (base + k)] - big);
-    den = fmaf(w, part_ml[2 * (base + k) + 1], den);
-    const float* po = part_out + (base + k) * D;
+  for (int k0 = 0; k0 < nparts; k0 += kWave) {
+    const int k = k0 + lane;
+    float w = 0.f;
+    if (k < nparts) {
+      const float2 x = ml[k];
+      w = fast_exp2(x.x - big);
+      den = fmaf(w, x.y, den);
+    }
+    wts[lane] = w;
+    __syncthreads();
+    const int n = min(kWave, nparts - k0);
+    const float* po = part_out + (base + k0) * D + lane;
+    int j = 0;
+    for (; j + 4 <= n; j += 4) {
+      float x[4][kPer];
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) acc[i] = fmaf(w, po[lane + i * kWave], acc[i]);
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) x[u][i] = po[(j + u) * D + i * kWave];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) acc[i] = fmaf(wts[j + u], x[u][i], acc[i]);
+    }
+    for (; j < n; ++j)
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) acc[i] = fmaf(wts[j], po[j * D + i * kWave], acc[i]);
+    __syncthreads();
   }
+  den = wave_sum(den);
   const float f = v_scale / den;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) store_out<QT>(o + lane + i * kWave, acc[i] * f);
@@ -490,9 +551,12 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(
 
 // ------------------------------------------------------------------ host
 
+// 512 tokens (32 blocks) per partition: long enough to amortise a
+// workgroup's start and the merge, short enough that the longest per-wave
+// chain of dependent block loads stays well under the kernel's duration.
 int32_t choose_partition(int32_t max_context_len, int32_t requested) {
-  if (requested > 0) return requested;
-  return max_context_len <= 8192 ? 256 : 512;
+  (void)max_context_len;
+  return requested > 0 ? requested : 512;
 }
 
 static size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
@@ -524,7 +588,7 @@ static pkv_status launch_decode(void* out, const void* q, const void* kc,
   float* part_out = static_cast<float*>(ws);
   float* part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + lay.out_bytes);
   hipLaunchKernelGGL((decode_partition_kernel<QT, KVT, D, GW>),
-                     dim3(lay.max_parts, hkv, s), dim3(kWave * waves), 0, st,
+                     dim3(s * hkv, lay.max_parts), dim3(kWave * waves), 0, st,
                      static_cast<const typename QT::storage*>(q),
                      static_cast<const typename KVT::storage*>(kc),
                      static_cast<const typename KVT::storage*>(vc), nb, bt, maxb,
@@ -555,7 +619,7 @@ static pkv_status dispatch_gw(int gw, void* out, const void* q, const void* kc,
 template <typename QT, typename KVT, int D, int GW>
 static pkv_status launch_rows(const PrefillArgs& a, int waves) {
   hipLaunchKernelGGL((prefill_rows_kernel<QT, KVT, D, GW>),
-                     dim3(1, a.num_kv_heads, a.num_q_tokens), dim3(kWave * waves), 0,
+                     dim3(a.num_kv_heads * a.num_q_tokens), dim3(kWave * waves), 0,
                      as_stream(a.stream), static_cast<typename QT::storage*>(a.out),
                      static_cast<const typename QT::storage*>(a.query),
                      static_cast<const typename KVT::storage*>(a.k_cache),
@@ -659,10 +723,12 @@ extern "C" pkv_status paged_attention_decode(
       layout(num_seqs, num_q_heads, head_dim, max_context_len, partition_tokens);
   if (!workspace || workspace_bytes < lay.out_bytes + lay.ml_bytes)
     return PKV_ERR_WORKSPACE;
+  if (lay.max_parts > 65535 || int64_t(num_seqs) * num_kv_heads > 0x7fffffff)
+    return PKV_ERR_SHAPE;
   if (!aligned(workspace, 16)) return PKV_ERR_ALIGN;
 
   // fp32 q with head_dim 128 keeps at most two heads per wave (registers)
-  const int max_gw = (f32 && head_dim == 128) ? 2 : 4;
+  const int max_gw = (f32 && head_dim == 128) ? 2 : PKV_DECODE_MAX_HEADS_PER_WAVE;
   const int waves = (group + max_gw - 1) / max_gw;
   const int gw = (group + waves - 1) / waves;
   const float scale_log2 = softmax_scale * k_scale * kLog2e;

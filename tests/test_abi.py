@@ -124,7 +124,8 @@ def test_decode_errors(lib):
     assert _decode(lib, kvd=FP8, ks=0.0) == SHAPE
     assert _decode(lib, nb=0) == SHAPE
     need = lib.paged_attention_decode_workspace_size(4, 32, 8, 128, 1000, 0)
-    assert need >= 4 * 32 * 4 * (128 + 2) * 4
+    pt = lib.paged_attention_decode_partition_tokens(4, 8, 1000, 0)
+    assert need >= 4 * 32 * -(-1000 // pt) * (128 + 2) * 4
     assert _decode(lib, wsb=need - 1) == WS
     assert _decode(lib, ws=None) == WS
     assert lib.paged_attention_decode_partition_tokens(4, 8, 1000, 0) in (256, 512)
