@@ -252,13 +252,14 @@ def main():
                                "context uniform in [512, 4096], 32 q / 8 kv heads, "
                                "head_dim 128, bf16 Q/K/V, 16-token blocks, shuffled "
                                "block placement; step = slot mapping + cache write of "
-                               "the 64 new tokens + paged decode (partitions + merge)",
+                               "the 64 new tokens + paged decode (balanced chunks + merge)",
                    "num_seqs": 64, "kv_tokens": r["tokens"],
                    "algorithmic_bytes": r["bytes"],
-                   "partition_tokens": pk.decode_partition_tokens(64, 8, int(step.decode_context_lens.max()))},
+                   "decode_chunks_per_kv_head": pk.decode_num_chunks(
+                       64, 32, 8, int(step.decode_context_lens.max()))},
         "pct_of_hbm_peak": round(100 * gbs_step / HBM_PEAK_GBS, 2),
         "kv_tokens_per_s": round(r["tokens"] / (r["ms_step"] * 1e-3), 1),
-        "roofline": {"bound": "hbm", "kernel": "paged_attention_decode (partition + merge)",
+        "roofline": {"bound": "hbm", "kernel": "paged_attention_decode (chunks + merge)",
                      "achieved": round(gbs_decode, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs_decode / HBM_PEAK_GBS, 4), "traffic": None,
                      "launch_ms": round(r["ms_decode"], 4)},

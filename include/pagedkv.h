@@ -159,12 +159,17 @@ pkv_status copy_blocks(void* const* k_caches, void* const* v_caches,
  * where K_j, V_j are read through block_tables[s] and an fp8 cache element
  * c stands for value(c) * k_scale (v_scale for V).  L == 0 gives zeros.
  *
- * The context is cut into partitions of partition_tokens tokens (0 = let the
- * library choose; else a positive multiple of 16 up to 1024); each partition
- * produces a (max, sum, weighted-value) partial in `workspace` and a second
- * kernel merges the partials with a log-sum-exp rescale.  The workspace is
- * caller-owned device memory of at least
- * paged_attention_decode_workspace_size(...) bytes for the same arguments.
+ * Work split: the blocks of all sequences are laid end to end and cut into
+ * equal chunks; one workgroup per (chunk, kv head) attends to its chunk.  A
+ * sequence that lies inside one chunk is written to `out` directly; one
+ * that spans chunks leaves a (max, sum, weighted-value) partial per chunk in
+ * `workspace`, and a second kernel merges them with a log-sum-exp rescale.
+ * partition_tokens = 0 lets the library size the chunks from the actual
+ * lengths (all chunks equal, enough of them to fill the GPU); otherwise each
+ * chunk is exactly partition_tokens tokens (a positive multiple of 16) of the
+ * laid-out blocks.  The workspace is caller-owned device memory of at least
+ * paged_attention_decode_workspace_size(...) bytes for the same arguments;
+ * its contents need no initialisation and are scratch after the call.
  *
  *   out, query          [num_seqs][num_q_heads][head_dim], q dtype
  *   context_lens        int32 [num_seqs], device, 0 <= L <= max_context_len
@@ -182,11 +187,12 @@ size_t paged_attention_decode_workspace_size(int32_t num_seqs,
                                              int32_t max_context_len,
                                              int32_t partition_tokens);
 
-/* The partition length paged_attention_decode uses for these arguments. */
-int32_t paged_attention_decode_partition_tokens(int32_t num_seqs,
-                                                int32_t num_kv_heads,
-                                                int32_t max_context_len,
-                                                int32_t partition_tokens);
+/* The number of chunks (per kv head) paged_attention_decode splits the work
+ * into for these arguments, or -1 when they are invalid. */
+int32_t paged_attention_decode_num_chunks(int32_t num_seqs, int32_t num_q_heads,
+                                          int32_t num_kv_heads,
+                                          int32_t max_context_len,
+                                          int32_t partition_tokens);
 
 pkv_status paged_attention_decode(void* out, const void* query,
                                   const void* k_cache, const void* v_cache,

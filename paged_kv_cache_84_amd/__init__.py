@@ -17,7 +17,7 @@ from ._binding import (  # noqa: F401
     PagedKVError,
     compute_slot_mapping,
     copy_blocks,
-    decode_partition_tokens,
+    decode_num_chunks,
     decode_workspace_size,
     kv_bytes_per_token,
     library,

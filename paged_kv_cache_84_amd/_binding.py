@@ -40,7 +40,7 @@ _SIGNATURES = {
                                  _I32, _F, _F, _P]),
     "copy_blocks": (_I32, [_P, _P, _I32, _P, _I32, _I32, _I64, _P]),
     "paged_attention_decode_workspace_size": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32]),
-    "paged_attention_decode_partition_tokens": (_I32, [_I32, _I32, _I32, _I32]),
+    "paged_attention_decode_num_chunks": (_I32, [_I32, _I32, _I32, _I32, _I32]),
     "paged_attention_decode": (_I32, [_P, _P, _P, _P, _I32, _P, _I32, _P, _I32, _I32,
                                       _I32, _I32, _I32, _F, _I32, _I32, _F, _F, _I32,
                                       _P, _SZ, _P]),
@@ -159,9 +159,10 @@ def copy_blocks(k_caches, v_caches, block_mapping):
     _check("copy_blocks", st)
 
 
-def decode_partition_tokens(num_seqs, num_kv_heads, max_context_len, partition_tokens=0):
-    return int(library().paged_attention_decode_partition_tokens(
-        num_seqs, num_kv_heads, max_context_len, partition_tokens))
+def decode_num_chunks(num_seqs, num_q_heads, num_kv_heads, max_context_len,
+                      partition_tokens=0):
+    return int(library().paged_attention_decode_num_chunks(
+        num_seqs, num_q_heads, num_kv_heads, max_context_len, partition_tokens))
 
 
 def decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,

@@ -26,6 +26,10 @@ ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC]
+# Matrix-core decode: keep MFMA accumulators in ordinary VGPRs, which the
+# vector rescale of the running softmax also touches (otherwise every block
+# copies them between the two register files).
+PER_FILE = {"decode_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc():
@@ -37,7 +41,8 @@ def hipcc():
 
 def _compile(src, extra, build_dir=BUILD):
     obj = os.path.join(build_dir, os.path.basename(src) + ".o")
-    cmd = [hipcc()] + COMMON + DEVICE_FLAGS + list(extra) + ["-c", src, "-o", obj]
+    cmd = ([hipcc()] + COMMON + DEVICE_FLAGS + PER_FILE.get(os.path.basename(src), [])
+           + list(extra) + ["-c", src, "-o", obj])
     res = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the device feature flag: drop that warning
     err = "\n".join(line for line in res.stderr.splitlines()

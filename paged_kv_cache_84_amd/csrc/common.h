@@ -124,6 +124,18 @@ PKV_DEVICE float wave_sum(float v) {
   return v;
 }
 
+// Sum of v over the lanes below this one.
+PKV_DEVICE int wave_exclusive_sum(int v) {
+  const int lane = lane_id();
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int t = __shfl_up(x, d, kWave);
+    if (lane >= d) x += t;
+  }
+  return x - v;
+}
+
 PKV_DEVICE float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // 16-byte global accesses.
@@ -145,6 +157,16 @@ PKV_DEVICE __amdgpu_buffer_rsrc_t tile_resource(const void* base, int bytes) {
 PKV_DEVICE u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t offset) {
   return __builtin_bit_cast(
       u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, offset, 0, PKV_TILE_LOAD_AUX));
+}
+// The same with a constant part of the offset in the scalar offset field, so
+// that one per-lane offset register serves every piece of a tile.
+PKV_DEVICE u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t offset, int scalar_offset) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                       r, offset, scalar_offset, PKV_TILE_LOAD_AUX));
+}
+// The same with the default cache policy, for data that other workgroups reuse.
+PKV_DEVICE u32x4 buffer_load16_cached(__amdgpu_buffer_rsrc_t r, uint32_t offset) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, offset, 0, 0));
 }
 
 }  // namespace pkv

@@ -29,17 +29,34 @@
 
 #include <math.h>
 
+#include <algorithm>
+
+#include <type_traits>
+
 #include "abi_util.h"
 #include "common.h"
+#include "decode_mfma.h"
+#include "decode_sched.h"
 #include "prefill_args.h"
 
 namespace pkv {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRaiseThreshold = 8.0f;   // log2 units
+// Running max before any key: finite, so that a fully masked block gives
+// weights 2^-inf = 0 rather than 2^(-inf + inf).
+constexpr float kNoMax = -1e30f;
 
+#ifndef PKV_DECODE_DEPTH
+#define PKV_DECODE_DEPTH 1
+#endif
 #ifndef PKV_DECODE_MAX_HEADS_PER_WAVE
 #define PKV_DECODE_MAX_HEADS_PER_WAVE 4
+#endif
+// bf16 queries go to the matrix-core kernel (decode_mfma.hip); 0 keeps every
+// dtype on the vector kernel below.
+#ifndef PKV_DECODE_USE_MFMA
+#define PKV_DECODE_USE_MFMA 1
 #endif
 #ifndef PKV_DECODE_WAVES_PER_EU
 #define PKV_DECODE_WAVES_PER_EU 3
@@ -157,24 +174,43 @@ struct DecodeWave {
   }
   PKV_DEVICE float* plds() const { return reinterpret_cast<float*>(lds + kQBytes); }
 
-  PKV_DEVICE void init(const typename QT::storage* qrow[GW], char* wave_lds) {
+  PKV_DEVICE void init(char* wave_lds) {
     lane = lane_id();
     krow = lane / G::kKLanes;
     kq = lane % G::kKLanes;
     vrow0 = lane / G::kVLanesPerRow;
     vcol = lane % G::kVLanesPerRow;
     lds = wave_lds;
-    // q rows -> LDS, 16 bytes per lane per step
-    constexpr int kRowPieces = D * QT::bytes / 16;
 #pragma unroll
     for (int h = 0; h < GW; ++h) {
-      for (int pc = lane; pc < kRowPieces; pc += kWave)
-        *reinterpret_cast<u32x4*>(lds + h * D * QT::bytes + pc * 16) =
-            load16(reinterpret_cast<const char*>(qrow[h]) + pc * 16);
-      m[h] = -INFINITY;
+      m[h] = kNoMax;
       l[h] = 0.f;
 #pragma unroll
       for (int e = 0; e < G::kElems; ++e) acc[h][e] = 0.f;
+    }
+  }
+
+  // The wave's q rows in 16-byte pieces, a few per lane, fetched into
+  // registers and later staged to LDS (where they are read as fragments).
+  static constexpr int kQRowPieces = D * QT::bytes / 16;
+  static constexpr int kQLanePieces = (GW * kQRowPieces + kWave - 1) / kWave;
+  struct QFetch {
+    u32x4 v[kQLanePieces];
+  };
+  // `rows` points at the first of the wave's heads (consecutive in memory);
+  // pieces of heads past `heads` read as zeros through the buffer bounds.
+  PKV_DEVICE QFetch fetch_q(const typename QT::storage* rows, int heads) const {
+    const auto rq = tile_resource(rows, heads * kQRowPieces * 16);
+    QFetch f;
+#pragma unroll
+    for (int i = 0; i < kQLanePieces; ++i) f.v[i] = buffer_load16_cached(rq, (i * kWave + lane) * 16);
+    return f;
+  }
+  PKV_DEVICE void stage_q(const QFetch& f) {
+#pragma unroll
+    for (int i = 0; i < kQLanePieces; ++i) {
+      const int piece = i * kWave + lane;
+      if (piece < GW * kQRowPieces) *reinterpret_cast<u32x4*>(lds + piece * 16) = f.v[i];
     }
     __builtin_amdgcn_wave_barrier();
   }
@@ -308,6 +344,16 @@ template <>
 PKV_DEVICE void store_out<BF16>(uint16_t* p, float v) { *p = f32_to_bf16(v); }
 
 
+// The table entries of the first PKV_DECODE_DEPTH + 1 blocks from `first_block`
+// (-1 past the table's end), read before the range itself is known so that
+// these scalar loads overlap the others at the start of a kernel.
+PKV_DEVICE void prefetch_ids(const int32_t* table, int first_block, int max_blocks,
+                             int32_t (&ids)[PKV_DECODE_DEPTH + 1]) {
+#pragma unroll
+  for (int d = 0; d <= PKV_DECODE_DEPTH; ++d)
+    ids[d] = first_block + d < max_blocks ? table[first_block + d] : -1;
+}
+
 // Attend one wave's heads to tokens [start, end) of one sequence.
 template <typename QT, typename KVT, int D, int GW>
 PKV_DEVICE void attend_range(DecodeWave<QT, KVT, D, GW>& w,
@@ -315,7 +361,9 @@ PKV_DEVICE void attend_range(DecodeWave<QT, KVT, D, GW>& w,
                              const typename KVT::storage* v_cache,
                              int32_t num_blocks, const int32_t* table,
                              int32_t max_blocks, int kvh, int num_kv_heads,
-                             int start, int end, float scale_log2) {
+                             int start, int end, float scale_log2,
+                             const typename DecodeWave<QT, KVT, D, GW>::QFetch& qv,
+                             const int32_t (&first_ids)[PKV_DECODE_DEPTH + 1]) {
   using G = Geom<QT, KVT, D>;
   const int first_block = start / kBlock;
   const int nblocks = (end - start + kBlock - 1) / kBlock;
@@ -331,34 +379,53 @@ PKV_DEVICE void attend_range(DecodeWave<QT, KVT, D, GW>& w,
     return (blk < nblocks && lb < max_blocks) ? table[lb] : -1;
   };
   auto valid = [&](int32_t b) { return b >= 0 && b < num_blocks; };
-  // One K and one V buffer: a block's K pieces are replaced by the next
-  // block's as soon as its scores are computed, its V pieces as soon as they
-  // are accumulated, so the next tile is always in flight while the current
-  // one is worked on.  Past the last block (or for an invalid id) the loads
-  // re-read the current block, a cache hit, and the tile is fully masked:
-  // every step has the same loads in flight on every path.
-  u32x4 kt[G::kKLoads], vt[G::kVLoads];
-  int32_t id_cur = id_at(0);
-  int32_t id_nxt = id_at(1);
-  {
-    const int32_t b0 = valid(id_cur) ? id_cur : 0;
-    w.load_k(kt, tile_ptr(k_cache, b0));
-    // keep K ahead of V in the memory queue, as inside the loop
+  // kDepth K buffers and kDepth V buffers used in turn: a block's K pieces are
+  // replaced by those of the block kDepth ahead as soon as its scores are
+  // computed, its V pieces as soon as they are accumulated, so the next
+  // kDepth tiles are always in flight while the current one is worked on.
+  // Past the last block (or for an invalid id) the loads re-read a block
+  // already read, a cache hit, and the tile is fully masked: every step has
+  // the same loads in flight on every path, so every wait is exact.
+  constexpr int kDepth = PKV_DECODE_DEPTH;
+  u32x4 kt[kDepth][G::kKLoads], vt[kDepth][G::kVLoads];
+  int32_t ids[kDepth + 1];
+#pragma unroll
+  for (int d = 0; d <= kDepth; ++d) ids[d] = d < nblocks ? first_ids[d] : -1;
+  const int32_t b_first = valid(ids[0]) ? ids[0] : 0;
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d) {
+    const int32_t b = valid(ids[d]) ? ids[d] : b_first;
+    w.load_k(kt[d], tile_ptr(k_cache, b));
+    // keep each K ahead of its V in the memory queue, as inside the loop
     __builtin_amdgcn_sched_barrier(0);
-    w.load_v(vt, tile_ptr(v_cache, b0));
+    w.load_v(vt[d], tile_ptr(v_cache, b));
+    __builtin_amdgcn_sched_barrier(0);
   }
-  for (int i = 0; i < nblocks; ++i) {
-    const int32_t id_after = id_at(i + 2);
+  // q was fetched before the tiles: staging it waits only for its own load
+  w.stage_q(qv);
+  auto step = [&](auto slot_c, int i) {
+    constexpr int S = decltype(slot_c)::value;
+    // ids[0] is block i, ids[kDepth] block i + kDepth
+    const int32_t id_cur = ids[0];
     const int rows = valid(id_cur) ? (i + 1 < nblocks ? kBlock : last_rows) : 0;
-    const int32_t bn = valid(id_nxt) ? id_nxt : (valid(id_cur) ? id_cur : 0);
+    const int32_t bn = valid(ids[kDepth]) ? ids[kDepth] : (valid(id_cur) ? id_cur : b_first);
+    const int32_t id_new = id_at(i + kDepth + 1);
     float s[G::kKPasses][GW];
-    const bool raise = w.scores(kt, rows, scale_log2, s);
-    w.load_k(kt, tile_ptr(k_cache, bn));
+    const bool raise = w.scores(kt[S], rows, scale_log2, s);
+    w.load_k(kt[S], tile_ptr(k_cache, bn));
     w.weights(s, raise);
-    w.accumulate(vt, rows);
-    w.load_v(vt, tile_ptr(v_cache, bn));
-    id_cur = id_nxt;
-    id_nxt = id_after;
+    w.accumulate(vt[S], rows);
+    w.load_v(vt[S], tile_ptr(v_cache, bn));
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) ids[d] = ids[d + 1];
+    ids[kDepth] = id_new;
+  };
+  for (int i = 0; i < nblocks; i += kDepth) {
+    step(std::integral_constant<int, 0>{}, i);
+    if (kDepth > 1) {
+      if (i + 1 >= nblocks) break;
+      step(std::integral_constant<int, (kDepth > 1 ? 1 : 0)>{}, i + 1);
+    }
   }
   // merge the row groups that share a column slice, and the rows' sums
   using G = Geom<QT, KVT, D>;
@@ -375,64 +442,80 @@ PKV_DEVICE void attend_range(DecodeWave<QT, KVT, D, GW>& w,
   }
 }
 
-// Decode: grid (partition, kv head, sequence); writes per-partition partials.
+// Decode: one workgroup per (chunk, kv head); each wave owns up to GW query
+// heads of the kv head.
 template <typename QT, typename KVT, int D, int GW>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PKV_DECODE_WAVES_PER_EU))) void decode_partition_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PKV_DECODE_WAVES_PER_EU))) void decode_chunk_kernel(
+    typename QT::storage* __restrict__ out,
     const typename QT::storage* __restrict__ query,
     const typename KVT::storage* __restrict__ k_cache,
     const typename KVT::storage* __restrict__ v_cache, int32_t num_blocks,
     const int32_t* __restrict__ block_tables, int32_t max_blocks,
-    const int32_t* __restrict__ context_lens, int32_t num_q_heads,
-    int32_t num_kv_heads, int32_t group, float scale_log2,
-    int32_t partition_tokens, int32_t max_parts, float* __restrict__ part_out,
-    float* __restrict__ part_ml) {
+    const int32_t* __restrict__ context_lens, int32_t num_seqs, int32_t max_len,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t group, float scale_log2,
+    float v_scale, int32_t num_chunks, int32_t fixed_chunk, float* __restrict__ rec_out,
+    float* __restrict__ rec_ml) {
   using G = Geom<QT, KVT, D>;
   using W = DecodeWave<QT, KVT, D, GW>;
   __shared__ __align__(16) char lds_all[4][W::kLdsBytes];
-  // (sequence, kv head) pairs are the fastest grid dimension: consecutive
-  // workgroups are dealt to the eight XCDs in turn, so each XCD gets an even
-  // share of every partition index (partitions past a short sequence's end
-  // exit at once and would otherwise pile the work onto a few XCDs).
+  // kv heads are the fastest grid dimension: the workgroups of one chunk
+  // read neighbouring tiles of the same blocks
   const int kvh = blockIdx.x % num_kv_heads;
-  const int seq = blockIdx.x / num_kv_heads;
-  const int part = blockIdx.y;
-  const int wave = threadIdx.x / kWave;
-  const int len = min(context_lens[seq], max_parts * partition_tokens);
-  const int start = part * partition_tokens;
-  if (start >= len) return;
-  const int end = min(len, start + partition_tokens);
-
+  const int g = blockIdx.x / num_kv_heads;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int head0 = kvh * group + wave * GW;
   const int heads_here = min(GW, group - wave * GW);
-  const typename QT::storage* qrow[GW];
-#pragma unroll
-  for (int h = 0; h < GW; ++h)
-    qrow[h] = query + (int64_t(seq) * num_q_heads + head0 + (h < heads_here ? h : 0)) * D;
+
+  const BatchScan sc = scan_batch(context_lens, num_seqs, max_len);
+  const int c = chunk_blocks(sc.total, num_chunks, fixed_chunk);
+  const int b0 = g * c;
+  if (b0 >= sc.total) return;
+  const int b1 = min(b0 + c, sc.total);
+  int s, before;
+  locate(sc, context_lens, max_len, b0, s, before);
   W w;
-  w.init(qrow, lds_all[wave]);
-  attend_range(w, k_cache, v_cache, num_blocks, block_tables + int64_t(seq) * max_blocks,
-               max_blocks, kvh, num_kv_heads, start, end, scale_log2);
-  if (w.lane < G::kVLanesPerRow) {
+  for (;;) {
+    const int len = seq_len(sc, context_lens, s, max_len);
+    const int n = blocks_of(len);
+    const int lo = max(b0, before), hi = min(b1, before + n);
+    if (lo < hi) {
+      const bool whole = lo == before && hi == before + n;
+      w.init(lds_all[wave]);
+      const auto qv = w.fetch_q(query + (int64_t(s) * num_q_heads + head0) * D, heads_here);
+      const int32_t* table = block_tables + int64_t(s) * max_blocks;
+      int32_t ids[PKV_DECODE_DEPTH + 1];
+      prefetch_ids(table, lo - before, max_blocks, ids);
+      attend_range(w, k_cache, v_cache, num_blocks, table, max_blocks, kvh, num_kv_heads,
+                   (lo - before) * kBlock, min(len, (hi - before) * kBlock), scale_log2, qv,
+                   ids);
+      if (w.lane < G::kVLanesPerRow) {
 #pragma unroll
-    for (int h = 0; h < GW; ++h) {
-      if (h >= heads_here) break;
-      const int64_t idx = (int64_t(seq) * num_q_heads + head0 + h) * max_parts + part;
-      float* o = part_out + idx * D + w.vcol * G::kElems;
+        for (int h = 0; h < GW; ++h) {
+          if (h >= heads_here) break;
+          if (whole) {
+            typename QT::storage* o =
+                out + (int64_t(s) * num_q_heads + head0 + h) * D + w.vcol * G::kElems;
+            const float f = v_scale / w.l[h];
 #pragma unroll
-      for (int e = 0; e < G::kElems; e += 4)
-        *reinterpret_cast<float4*>(o + e) =
-            make_float4(w.acc[h][e], w.acc[h][e + 1], w.acc[h][e + 2], w.acc[h][e + 3]);
-      if (w.lane == 0) {
-        part_ml[2 * idx] = w.m[h];
-        part_ml[2 * idx + 1] = w.l[h];
+            for (int e = 0; e < G::kElems; ++e) store_out<QT>(o + e, w.acc[h][e] * f);
+          } else {
+            const int64_t idx = int64_t(g + s) * num_q_heads + head0 + h;
+            float* o = rec_out + idx * D + w.vcol * G::kElems;
+#pragma unroll
+            for (int e = 0; e < G::kElems; e += 4)
+              *reinterpret_cast<float4*>(o + e) =
+                  make_float4(w.acc[h][e], w.acc[h][e + 1], w.acc[h][e + 2], w.acc[h][e + 3]);
+            if (w.lane == 0) reinterpret_cast<float2*>(rec_ml)[idx] = make_float2(w.m[h], w.l[h]);
+          }
+        }
       }
     }
+    before += n;
+    ++s;
+    if (before >= b1 || s >= num_seqs) break;
   }
 }
 
-// Chunked prefill on the vector units (dtypes and head sizes without an
-// MFMA kernel): grid (1, kv head, query row); each query row attends to its
-// whole causal context, so the output is final.
 template <typename QT, typename KVT, int D, int GW>
 __global__ __launch_bounds__(256) void prefill_rows_kernel(
     typename QT::storage* __restrict__ out,
@@ -449,7 +532,7 @@ __global__ __launch_bounds__(256) void prefill_rows_kernel(
   __shared__ __align__(16) char lds_all[4][W::kLdsBytes];
   const int kvh = blockIdx.x % num_kv_heads;
   const int row = blockIdx.x / num_kv_heads;
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   // the request owning this row: last r with query_start_loc[r] <= row
   int lo = 0, hi = num_reqs - 1;
   while (lo < hi) {
@@ -460,16 +543,16 @@ __global__ __launch_bounds__(256) void prefill_rows_kernel(
   const int len = num_computed[r] + (row - query_start_loc[r]) + 1;
   const int head0 = kvh * group + wave * GW;
   const int heads_here = min(GW, group - wave * GW);
-  const typename QT::storage* qrow[GW];
-#pragma unroll
-  for (int h = 0; h < GW; ++h)
-    qrow[h] = query + (int64_t(row) * num_q_heads + head0 + (h < heads_here ? h : 0)) * D;
   W w;
-  w.init(qrow, lds_all[wave]);
+  w.init(lds_all[wave]);
+  const auto qv = w.fetch_q(query + (int64_t(row) * num_q_heads + head0) * D, heads_here);
+  const int32_t* table = block_tables + int64_t(r) * max_blocks;
+  int32_t ids[PKV_DECODE_DEPTH + 1];
+  prefetch_ids(table, 0, max_blocks, ids);
   const int cap = min(len, max_blocks * kBlock);
   if (cap > 0)
-    attend_range(w, k_cache, v_cache, num_blocks, block_tables + int64_t(r) * max_blocks,
-                 max_blocks, kvh, num_kv_heads, 0, cap, scale_log2);
+    attend_range(w, k_cache, v_cache, num_blocks, table, max_blocks, kvh, num_kv_heads, 0,
+                 cap, scale_log2, qv, ids);
   if (w.lane < G::kVLanesPerRow) {
 #pragma unroll
     for (int h = 0; h < GW; ++h) {
@@ -483,64 +566,77 @@ __global__ __launch_bounds__(256) void prefill_rows_kernel(
   }
 }
 
-// One workgroup (one wave) per (head, sequence): merge the partitions,
+// One workgroup (one wave) per (head, sequence): merge the partials of a
+// sequence that spans several chunks,
 //   out = sum_k e^{m_k - M} o_k / sum_k e^{m_k - M} l_k,   M = max_k m_k
-// (m in log2 units).  The weights of up to 64 partitions at a time are
-// computed one per lane and passed through LDS, so the partials' loads do not
-// wait on each other.
+// (m in log2 units).  Sequences inside one chunk were written by the chunk
+// kernel; empty ones get zeros here.  The weights of up to 64 partials at a
+// time are computed one per lane and passed through LDS, so the partials'
+// loads do not wait on each other.
 template <typename QT, int D>
-__global__ __launch_bounds__(64) void decode_reduce_kernel(
-    typename QT::storage* __restrict__ out, const float* __restrict__ part_out,
-    const float* __restrict__ part_ml, const int32_t* __restrict__ context_lens,
-    int32_t num_q_heads, int32_t partition_tokens, int32_t max_parts,
-    float v_scale) {
+__global__ __launch_bounds__(64) void decode_merge_kernel(
+    typename QT::storage* __restrict__ out, const float* __restrict__ rec_out,
+    const float* __restrict__ rec_ml, const int32_t* __restrict__ context_lens,
+    int32_t num_seqs, int32_t max_len, int32_t num_q_heads, int32_t num_chunks,
+    int32_t fixed_chunk, float v_scale) {
   constexpr int kPer = D / kWave;
   __shared__ float wts[kWave];
   const int h = blockIdx.x;
   const int seq = blockIdx.y;
   const int lane = threadIdx.x;
-  const int len = min(context_lens[seq], max_parts * partition_tokens);
+  const BatchScan sc = scan_batch(context_lens, num_seqs, max_len);
+  const int owner = seq / sc.k;
+  int before = __builtin_amdgcn_readlane(sc.first, owner);
+  for (int t = owner * sc.k; t < seq; ++t)
+    before += blocks_of(seq_len(sc, context_lens, t, max_len));
+  const int n = blocks_of(seq_len(sc, context_lens, seq, max_len));
   typename QT::storage* o = out + (int64_t(seq) * num_q_heads + h) * D;
-  if (len <= 0) {
+  if (n == 0) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) store_out<QT>(o + lane + i * kWave, 0.f);
     return;
   }
-  const int nparts = (len + partition_tokens - 1) / partition_tokens;
-  const int64_t base = (int64_t(seq) * num_q_heads + h) * max_parts;
-  const float2* ml = reinterpret_cast<const float2*>(part_ml) + base;
+  const int c = chunk_blocks(sc.total, num_chunks, fixed_chunk);
+  const int g0 = before / c, g1 = (before + n - 1) / c;
+  if (g0 == g1) return;
+  const int nparts = g1 - g0 + 1;
+  // the partial of chunk g sits in record g + seq
+  const int64_t base = int64_t(g0 + seq) * num_q_heads + h;
+  const int64_t stride = num_q_heads;
+  const float2* ml = reinterpret_cast<const float2*>(rec_ml) + base;
   float big = -INFINITY;
-  for (int k = lane; k < nparts; k += kWave) big = fmaxf(big, ml[k].x);
+  for (int k = lane; k < nparts; k += kWave) big = fmaxf(big, ml[k * stride].x);
   big = wave_max(big);
   float acc[kPer] = {};
   float den = 0.f;
   for (int k0 = 0; k0 < nparts; k0 += kWave) {
     const int k = k0 + lane;
-    float w = 0.f;
+    float wk = 0.f;
     if (k < nparts) {
-      const float2 x = ml[k];
-      w = fast_exp2(x.x - big);
-      den = fmaf(w, x.y, den);
+      const float2 x = ml[k * stride];
+      wk = fast_exp2(x.x - big);
+      den = fmaf(wk, x.y, den);
     }
-    wts[lane] = w;
+    wts[lane] = wk;
     __syncthreads();
-    const int n = min(kWave, nparts - k0);
-    const float* po = part_out + (base + k0) * D + lane;
+    const int cnt = min(kWave, nparts - k0);
+    const float* po = rec_out + (base + k0 * stride) * D + lane;
+    const int64_t step = stride * D;
     int j = 0;
-    for (; j + 4 <= n; j += 4) {
+    for (; j + 4 <= cnt; j += 4) {
       float x[4][kPer];
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int i = 0; i < kPer; ++i) x[u][i] = po[(j + u) * D + i * kWave];
+        for (int i = 0; i < kPer; ++i) x[u][i] = po[(j + u) * step + i * kWave];
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int i = 0; i < kPer; ++i) acc[i] = fmaf(wts[j + u], x[u][i], acc[i]);
     }
-    for (; j < n; ++j)
+    for (; j < cnt; ++j)
 #pragma unroll
-      for (int i = 0; i < kPer; ++i) acc[i] = fmaf(wts[j], po[j * D + i * kWave], acc[i]);
+      for (int i = 0; i < kPer; ++i) acc[i] = fmaf(wts[j], po[j * step + i * kWave], acc[i]);
     __syncthreads();
   }
   den = wave_sum(den);
@@ -551,67 +647,93 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(
 
 // ------------------------------------------------------------------ host
 
-// 512 tokens (32 blocks) per partition: long enough to amortise a
-// workgroup's start and the merge, short enough that the longest per-wave
-// chain of dependent block loads stays well under the kernel's duration.
-int32_t choose_partition(int32_t max_context_len, int32_t requested) {
-  (void)max_context_len;
-  return requested > 0 ? requested : 512;
-}
+// Chunks per kv head when the caller leaves the split to the library: enough
+// workgroups that every SIMD holds two to three waves (all resident at
+// once, so all finish together), never chunks below kMinChunkBlocks of the
+// largest possible batch.
+#ifndef PKV_DECODE_TARGET_WAVES
+#define PKV_DECODE_TARGET_WAVES 2048
+#endif
 
 static size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
-struct WorkspaceLayout {
-  int32_t part_tokens, max_parts;
+struct DecodePlan {
+  int32_t num_chunks;    // chunks per kv head (grid: num_chunks x num_kv_heads)
+  int32_t fixed_chunk;   // blocks per chunk, or 0: split the batch evenly
   size_t out_bytes, ml_bytes;
 };
 
-static WorkspaceLayout layout(int32_t s, int32_t hq, int32_t d, int32_t max_len,
-                              int32_t requested) {
-  WorkspaceLayout w;
-  w.part_tokens = choose_partition(max_len, requested);
-  w.max_parts = max_len <= 0 ? 1 : (max_len + w.part_tokens - 1) / w.part_tokens;
-  w.out_bytes = align256(size_t(s) * hq * w.max_parts * d * sizeof(float));
-  w.ml_bytes = align256(size_t(s) * hq * w.max_parts * 2 * sizeof(float));
-  return w;
+static bool make_plan(int32_t s, int32_t hq, int32_t hkv, int32_t d, int32_t max_len,
+                      int32_t partition_tokens, DecodePlan& p) {
+  if (s < 0 || hq <= 0 || hkv <= 0 || d <= 0 || max_len < 0 || hq % hkv != 0) return false;
+  const int64_t bound = int64_t(s) * ((max_len + kBlock - 1) / kBlock);
+  int64_t chunks;
+  if (partition_tokens > 0) {
+    p.fixed_chunk = partition_tokens / kBlock;
+    chunks = (bound + p.fixed_chunk - 1) / p.fixed_chunk;
+  } else {
+    p.fixed_chunk = 0;
+    const int waves_per_chunk = (hq / hkv + 3) / 4;
+    chunks = PKV_DECODE_TARGET_WAVES / (int64_t(hkv) * waves_per_chunk);
+    chunks = std::min<int64_t>(chunks, (bound + kMinChunkBlocks - 1) / kMinChunkBlocks);
+  }
+  chunks = std::max<int64_t>(chunks, 1);
+  if (chunks * hkv > 0x7fffffff) return false;
+  p.num_chunks = int32_t(chunks);
+  // partial of (chunk g, sequence s) -> record g + s
+  const size_t records = size_t(chunks) + size_t(s);
+  p.out_bytes = align256(records * hq * d * sizeof(float));
+  p.ml_bytes = align256(records * hq * 2 * sizeof(float));
+  return true;
+}
+
+template <typename QT, int D>
+static pkv_status launch_merge(void* out, const int32_t* lens, int32_t s, int32_t max_len,
+                               int32_t hq, float v_scale, const DecodePlan& plan, void* ws,
+                               hipStream_t st) {
+  const float* rec_out = static_cast<const float*>(ws);
+  const float* rec_ml =
+      reinterpret_cast<const float*>(static_cast<const char*>(ws) + plan.out_bytes);
+  hipLaunchKernelGGL((decode_merge_kernel<QT, D>), dim3(hq, s), dim3(kWave), 0, st,
+                     static_cast<typename QT::storage*>(out), rec_out, rec_ml, lens, s,
+                     max_len, hq, plan.num_chunks, plan.fixed_chunk, v_scale);
+  return launch_status();
 }
 
 template <typename QT, typename KVT, int D, int GW>
 static pkv_status launch_decode(void* out, const void* q, const void* kc,
                                 const void* vc, int32_t nb, const int32_t* bt,
                                 int32_t maxb, const int32_t* lens, int32_t s,
-                                int32_t hq, int32_t hkv, float scale_log2,
-                                float v_scale, const WorkspaceLayout& lay,
+                                int32_t max_len, int32_t hq, int32_t hkv,
+                                float scale_log2, float v_scale, const DecodePlan& plan,
                                 void* ws, hipStream_t st) {
   const int group = hq / hkv;
   const int waves = (group + GW - 1) / GW;
-  float* part_out = static_cast<float*>(ws);
-  float* part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + lay.out_bytes);
-  hipLaunchKernelGGL((decode_partition_kernel<QT, KVT, D, GW>),
-                     dim3(s * hkv, lay.max_parts), dim3(kWave * waves), 0, st,
+  float* rec_out = static_cast<float*>(ws);
+  float* rec_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + plan.out_bytes);
+  hipLaunchKernelGGL((decode_chunk_kernel<QT, KVT, D, GW>),
+                     dim3(plan.num_chunks * hkv), dim3(kWave * waves), 0, st,
+                     static_cast<typename QT::storage*>(out),
                      static_cast<const typename QT::storage*>(q),
                      static_cast<const typename KVT::storage*>(kc),
-                     static_cast<const typename KVT::storage*>(vc), nb, bt, maxb,
-                     lens, hq, hkv, group, scale_log2, lay.part_tokens,
-                     lay.max_parts, part_out, part_ml);
+                     static_cast<const typename KVT::storage*>(vc), nb, bt, maxb, lens, s,
+                     max_len, hq, hkv, group, scale_log2, v_scale, plan.num_chunks,
+                     plan.fixed_chunk, rec_out, rec_ml);
   if (launch_status() != PKV_OK) return PKV_ERR_LAUNCH;
-  hipLaunchKernelGGL((decode_reduce_kernel<QT, D>), dim3(hq, s), dim3(kWave), 0, st,
-                     static_cast<typename QT::storage*>(out), part_out, part_ml,
-                     lens, hq, lay.part_tokens, lay.max_parts, v_scale);
-  return launch_status();
+  return launch_merge<QT, D>(out, lens, s, max_len, hq, v_scale, plan, ws, st);
 }
 
 template <typename QT, typename KVT, int D>
 static pkv_status dispatch_gw(int gw, void* out, const void* q, const void* kc,
                               const void* vc, int32_t nb, const int32_t* bt,
                               int32_t maxb, const int32_t* lens, int32_t s,
-                              int32_t hq, int32_t hkv, float sl2, float vs,
-                              const WorkspaceLayout& lay, void* ws, hipStream_t st) {
+                              int32_t ml, int32_t hq, int32_t hkv, float sl2, float vs,
+                              const DecodePlan& lay, void* ws, hipStream_t st) {
   switch (gw) {
-    case 1: return launch_decode<QT, KVT, D, 1>(out, q, kc, vc, nb, bt, maxb, lens, s, hq, hkv, sl2, vs, lay, ws, st);
-    case 2: return launch_decode<QT, KVT, D, 2>(out, q, kc, vc, nb, bt, maxb, lens, s, hq, hkv, sl2, vs, lay, ws, st);
-    case 3: return launch_decode<QT, KVT, D, 3>(out, q, kc, vc, nb, bt, maxb, lens, s, hq, hkv, sl2, vs, lay, ws, st);
-    case 4: return launch_decode<QT, KVT, D, 4>(out, q, kc, vc, nb, bt, maxb, lens, s, hq, hkv, sl2, vs, lay, ws, st);
+    case 1: return launch_decode<QT, KVT, D, 1>(out, q, kc, vc, nb, bt, maxb, lens, s, ml, hq, hkv, sl2, vs, lay, ws, st);
+    case 2: return launch_decode<QT, KVT, D, 2>(out, q, kc, vc, nb, bt, maxb, lens, s, ml, hq, hkv, sl2, vs, lay, ws, st);
+    case 3: return launch_decode<QT, KVT, D, 3>(out, q, kc, vc, nb, bt, maxb, lens, s, ml, hq, hkv, sl2, vs, lay, ws, st);
+    case 4: return launch_decode<QT, KVT, D, 4>(out, q, kc, vc, nb, bt, maxb, lens, s, ml, hq, hkv, sl2, vs, lay, ws, st);
     default: return PKV_ERR_UNSUPPORTED;
   }
 }
@@ -664,13 +786,16 @@ pkv_status launch_prefill_rows(const PrefillArgs& a) {
 
 using namespace pkv;
 
-extern "C" int32_t paged_attention_decode_partition_tokens(int32_t num_seqs,
-                                                           int32_t num_kv_heads,
-                                                           int32_t max_context_len,
-                                                           int32_t partition_tokens) {
-  (void)num_seqs;
-  (void)num_kv_heads;
-  return choose_partition(max_context_len, partition_tokens);
+extern "C" int32_t paged_attention_decode_num_chunks(int32_t num_seqs,
+                                                     int32_t num_q_heads,
+                                                     int32_t num_kv_heads,
+                                                     int32_t max_context_len,
+                                                     int32_t partition_tokens) {
+  DecodePlan p;
+  if (partition_tokens < 0 || partition_tokens % kBlock != 0 ||
+      !make_plan(num_seqs, num_q_heads, num_kv_heads, 1, max_context_len, partition_tokens, p))
+    return -1;
+  return p.num_chunks;
 }
 
 extern "C" size_t paged_attention_decode_workspace_size(int32_t num_seqs,
@@ -679,12 +804,12 @@ extern "C" size_t paged_attention_decode_workspace_size(int32_t num_seqs,
                                                         int32_t head_dim,
                                                         int32_t max_context_len,
                                                         int32_t partition_tokens) {
-  (void)num_kv_heads;
-  if (num_seqs < 0 || num_q_heads < 0 || head_dim < 0 || max_context_len < 0)
+  DecodePlan p;
+  if (partition_tokens < 0 || partition_tokens % kBlock != 0 ||
+      !make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                 partition_tokens, p))
     return 0;
-  const WorkspaceLayout w =
-      layout(num_seqs, num_q_heads, head_dim, max_context_len, partition_tokens);
-  return w.out_bytes + w.ml_bytes;
+  return p.out_bytes + p.ml_bytes;
 }
 
 extern "C" pkv_status paged_attention_decode(
@@ -704,8 +829,7 @@ extern "C" pkv_status paged_attention_decode(
   const int group = num_q_heads / num_kv_heads;
   if (group > 8) return PKV_ERR_UNSUPPORTED;
   if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
-  if (partition_tokens < 0 || partition_tokens % kBlock != 0 || partition_tokens > 1024)
-    return PKV_ERR_SHAPE;
+  if (partition_tokens < 0 || partition_tokens % kBlock != 0) return PKV_ERR_SHAPE;
   const bool f32 = q_dtype == PKV_F32 && kv_dtype == PKV_F32;
   const bool bf16 = q_dtype == PKV_BF16 && kv_dtype == PKV_BF16;
   const bool fp8 = q_dtype == PKV_BF16 && kv_dtype == PKV_FP8_E4M3;
@@ -719,14 +843,33 @@ extern "C" pkv_status paged_attention_decode(
   if (!aligned(out, 16) || !aligned(query, 16) || !aligned(k_cache, 16) ||
       !aligned(v_cache, 16) || !aligned(block_tables, 4) || !aligned(context_lens, 4))
     return PKV_ERR_ALIGN;
-  const WorkspaceLayout lay =
-      layout(num_seqs, num_q_heads, head_dim, max_context_len, partition_tokens);
+  DecodePlan lay;
+  if (!make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                 partition_tokens, lay) ||
+      int64_t(num_seqs) * num_q_heads > 0x7fffffff)
+    return PKV_ERR_SHAPE;
   if (!workspace || workspace_bytes < lay.out_bytes + lay.ml_bytes)
     return PKV_ERR_WORKSPACE;
-  if (lay.max_parts > 65535 || int64_t(num_seqs) * num_kv_heads > 0x7fffffff)
-    return PKV_ERR_SHAPE;
   if (!aligned(workspace, 16)) return PKV_ERR_ALIGN;
 
+#if PKV_DECODE_USE_MFMA
+  if (decode_mfma_supported(q_dtype, kv_dtype, head_dim, group)) {
+    DecodeMfmaArgs a{out, query, k_cache, v_cache, num_blocks, block_tables,
+                     max_blocks_per_seq, context_lens, num_seqs, max_context_len,
+                     num_q_heads, num_kv_heads, head_dim, kv_dtype,
+                     softmax_scale * k_scale * kLog2e, v_scale, lay.num_chunks,
+                     lay.fixed_chunk, static_cast<float*>(workspace),
+                     reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.out_bytes),
+                     stream};
+    if (launch_decode_mfma(a) != PKV_OK) return PKV_ERR_LAUNCH;
+    hipStream_t st = as_stream(stream);
+    return head_dim == 64
+               ? launch_merge<BF16, 64>(out, context_lens, num_seqs, max_context_len,
+                                        num_q_heads, v_scale, lay, workspace, st)
+               : launch_merge<BF16, 128>(out, context_lens, num_seqs, max_context_len,
+                                         num_q_heads, v_scale, lay, workspace, st);
+  }
+#endif
   // fp32 q with head_dim 128 keeps at most two heads per wave (registers)
   const int max_gw = (f32 && head_dim == 128) ? 2 : PKV_DECODE_MAX_HEADS_PER_WAVE;
   const int waves = (group + max_gw - 1) / max_gw;
@@ -735,7 +878,7 @@ extern "C" pkv_status paged_attention_decode(
   hipStream_t st = as_stream(stream);
   const int32_t nb = num_blocks, maxb = max_blocks_per_seq;
 #define PKV_DECODE_ARGS gw, out, query, k_cache, v_cache, nb, block_tables, maxb, \
-    context_lens, num_seqs, num_q_heads, num_kv_heads, scale_log2, v_scale, lay, workspace, st
+    context_lens, num_seqs, max_context_len, num_q_heads, num_kv_heads, scale_log2, v_scale, lay, workspace, st
   if (f32) {
     return head_dim == 64 ? dispatch_gw<F32, F32, 64>(PKV_DECODE_ARGS)
                           : dispatch_gw<F32, F32, 128>(PKV_DECODE_ARGS);

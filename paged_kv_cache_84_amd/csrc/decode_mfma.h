@@ -1,0 +1,34 @@
+// Arguments of the matrix-core decode kernel, validated on the host.
+#pragma once
+
+#include <stdint.h>
+
+#include "pagedkv.h"
+
+namespace pkv {
+
+struct DecodeMfmaArgs {
+  void* out;
+  const void* query;
+  const void* k_cache;
+  const void* v_cache;
+  int32_t num_blocks;
+  const int32_t* block_tables;
+  int32_t max_blocks;
+  const int32_t* context_lens;
+  int32_t num_seqs, max_len;
+  int32_t num_q_heads, num_kv_heads, head_dim;
+  pkv_dtype kv_dtype;
+  float scale_log2, v_scale;
+  int32_t num_chunks, fixed_chunk;   // the work split (see decode_sched.h)
+  float* rec_out;                    // partials of sequences that span chunks
+  float* rec_ml;
+  void* stream;
+};
+
+// bf16 queries with a bf16 or fp8 E4M3 cache, head_dim 64 or 128, group <= 16.
+bool decode_mfma_supported(pkv_dtype q_dtype, pkv_dtype kv_dtype, int head_dim, int group);
+// Launches the chunk kernel only; the caller launches the merge.
+pkv_status launch_decode_mfma(const DecodeMfmaArgs& a);
+
+}  // namespace pkv

@@ -1,0 +1,350 @@
+// Paged decode attention on the matrix cores of gfx950 (bf16 queries; bf16
+// or fp8 E4M3 cache).
+//
+// Decode reads every K/V block of a sequence once per step and is bound by
+// HBM bandwidth ("vLLM 引擎解剖", section "预填充、解码与三个时延指标"); the
+// blocks are reached through the sequence's block table (section
+// "PagedAttention：为 KV 缓存分页", Fig. 2).  What this kernel minimises is
+// the vector-unit work per block, so that the wave is back to issuing loads
+// as soon as a tile arrives.
+//
+// One wave per (work chunk, kv head) holds all query heads of the kv head's
+// group as the 16 columns of MFMA tiles (unused columns carry zero queries).
+// Per 16-token block:
+//   S^T (16 keys x 16 heads) = K (16 x D) . Q^T      D/32 v_mfma_f32_16x16x32_bf16
+//     K is loaded straight into A-operand registers: lane l holds 16 bytes of
+//     key row l%16; Q^T lives in B-operand registers for the whole segment.
+//   online softmax on S^T: lane l holds keys 4(l/16)..+3 of head l%16, so the
+//     running max and sum are per lane (one head each), no cross-lane work
+//     except on the rare raise of the max;
+//   O^T (D x 16 heads) += V^T (D x 16 keys) . P^T   2 D/16 v_mfma_f32_16x16x16_bf16
+//     P^T is the S^T register layout itself (the B operand of a 16x16x16
+//     product holds keys 4(l/16)..+3 of column l%16), split into a bf16 high
+//     part and a bf16 remainder so the product keeps fp32-level accuracy.
+//     V^T comes from the V tile staged in LDS (row per key) through the
+//     transposing LDS read ds_read_b64_tr_b16: within each 16-lane group,
+//     lane j receives element j%4 of the 4-element rows addressed by lanes
+//     4e + j/4 (e = 0..3), so lane 4k + q addressing key k, dims 4q..4q+3 of
+//     a 16-dim slice hands every lane the 4 keys of its dim.
+// fp8 tiles are widened to bf16 in registers (exact); k_scale is folded into
+// the softmax scale and v_scale into the final normalisation.
+
+#include <math.h>
+
+#include "abi_util.h"
+#include "common.h"
+#include "decode_mfma.h"
+#include "decode_sched.h"
+
+namespace pkv {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+constexpr float kRaiseM = 8.0f;   // log2 units, as in the vector kernel
+constexpr float kNoMax = -1e30f;
+
+PKV_DEVICE f32x4_t mfma_k32(u32x4 a, u32x4 b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+PKV_DEVICE f32x4_t mfma_k16(i16x4_t a, i16x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+PKV_DEVICE uint32_t pack_bf16_rne(float a, float b) {
+  bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+template <typename KVT, int D>
+struct MGeom {
+  static constexpr int kKSteps = D / 32;               // QK products per block
+  static constexpr int kMTiles = D / 16;               // 16-dim slices of V
+  static constexpr int kRowBytes = D * KVT::bytes;     // one cache row
+  static constexpr int kTileBytes = kBlock * kRowBytes;
+  static constexpr int kVLoads = kTileBytes / (kWave * 16);  // 16-byte V pieces per lane
+  static constexpr int kKLoads = KVT::bytes == 2 ? kKSteps : kKSteps / 2;
+  static constexpr int kVStride = D * 2 + 32;          // LDS bytes per staged bf16 V row
+  static_assert(kKSteps >= 2 && kVLoads >= 1, "unsupported head size");
+};
+
+// First dim of the 8 consecutive dims that lane group j feeds to QK product ks
+// (any assignment works as long as K and Q use the same one; for fp8 it makes
+// each lane's 16-byte load cover two products).
+template <typename KVT>
+PKV_DEVICE int qk_dim(int j, int ks) {
+  return KVT::bytes == 2 ? 8 * j + 32 * ks : 16 * j + 64 * (ks / 2) + 8 * (ks % 2);
+}
+
+template <typename KVT, int D>
+struct KRegs {
+  u32x4 v[MGeom<KVT, D>::kKLoads];
+};
+template <typename KVT, int D>
+struct VRegs {
+  u32x4 v[MGeom<KVT, D>::kVLoads];
+};
+
+template <typename KVT, int D>
+PKV_DEVICE void load_k(KRegs<KVT, D>& r, const typename KVT::storage* tile, int lane) {
+  using M = MGeom<KVT, D>;
+  const auto rs = tile_resource(tile, M::kTileBytes);
+  const uint32_t off = uint32_t((lane % 16) * M::kRowBytes + (lane / 16) * 16);
+#pragma unroll
+  for (int i = 0; i < M::kKLoads; ++i) r.v[i] = buffer_load16(rs, off, i * 64);
+}
+
+template <typename KVT, int D>
+PKV_DEVICE void load_v(VRegs<KVT, D>& r, const typename KVT::storage* tile, int lane) {
+  using M = MGeom<KVT, D>;
+  const auto rs = tile_resource(tile, M::kTileBytes);
+#pragma unroll
+  for (int i = 0; i < M::kVLoads; ++i) r.v[i] = buffer_load16(rs, uint32_t(lane * 16), i * 1024);
+}
+
+// The A operand of QK product ks from the K registers.
+template <typename KVT, int D>
+PKV_DEVICE u32x4 k_operand(const KRegs<KVT, D>& r, int ks) {
+  if constexpr (KVT::bytes == 2) {
+    return r.v[ks];
+  } else {
+    const u32x4 x = r.v[ks / 2];
+    const uint32_t w0 = (ks % 2) ? x[2] : x[0];
+    const uint32_t w1 = (ks % 2) ? x[3] : x[1];
+    return u32x4{fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0),
+                 fp8x2_to_bf16x2<false>(w1), fp8x2_to_bf16x2<true>(w1)};
+  }
+}
+
+// V tile -> LDS as bf16 rows; rows at or past `rows` (unused slots of a last
+// block, whose bytes may be anything) become zeros, since 0 * NaN would
+// reach the accumulators.
+template <typename KVT, int D>
+PKV_DEVICE void stage_v(VRegs<KVT, D>& r, char* vl, int lane, int rows) {
+  using M = MGeom<KVT, D>;
+  if (rows < kBlock) {
+#pragma unroll
+    for (int i = 0; i < M::kVLoads; ++i)
+      if ((lane * 16 + i * 1024) / M::kRowBytes >= rows) r.v[i] = u32x4{0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int i = 0; i < M::kVLoads; ++i) {
+    const int o = lane * 16 + i * 1024;         // byte offset in the cache tile
+    const int row = o / M::kRowBytes;
+    const int col = (o % M::kRowBytes) / KVT::bytes;
+    char* dst = vl + row * M::kVStride + col * 2;
+    if constexpr (KVT::bytes == 2) {
+      *reinterpret_cast<u32x4*>(dst) = r.v[i];
+    } else {
+      const u32x4 x = r.v[i];
+      *reinterpret_cast<u32x4*>(dst) =
+          u32x4{fp8x2_to_bf16x2<false>(x[0]), fp8x2_to_bf16x2<true>(x[0]),
+                fp8x2_to_bf16x2<false>(x[1]), fp8x2_to_bf16x2<true>(x[1])};
+      *reinterpret_cast<u32x4*>(dst + 16) =
+          u32x4{fp8x2_to_bf16x2<false>(x[2]), fp8x2_to_bf16x2<true>(x[2]),
+                fp8x2_to_bf16x2<false>(x[3]), fp8x2_to_bf16x2<true>(x[3])};
+    }
+  }
+}
+
+}  // namespace
+
+template <typename KVT, int D>
+__global__ __launch_bounds__(64) void decode_mfma_kernel(
+    uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
+    const typename KVT::storage* __restrict__ k_cache,
+    const typename KVT::storage* __restrict__ v_cache, int32_t num_blocks,
+    const int32_t* __restrict__ block_tables, int32_t max_blocks,
+    const int32_t* __restrict__ context_lens, int32_t num_seqs, int32_t max_len,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t group, float scale_log2,
+    float v_scale, int32_t num_chunks, int32_t fixed_chunk, float* __restrict__ rec_out,
+    float* __restrict__ rec_ml) {
+  using M = MGeom<KVT, D>;
+  __shared__ __align__(16) char vl[kBlock * M::kVStride];
+  const int kvh = blockIdx.x % num_kv_heads;
+  const int g = blockIdx.x / num_kv_heads;
+  const int lane = lane_id();
+  const int n16 = lane % 16;          // head column of this lane
+  const int j = lane / 16;            // lane group
+  const bool head_ok = n16 < group;
+  const int head = kvh * group + (head_ok ? n16 : 0);
+
+  const BatchScan sc = scan_batch(context_lens, num_seqs, max_len);
+  const int c = chunk_blocks(sc.total, num_chunks, fixed_chunk);
+  const int b0 = g * c;
+  if (b0 >= sc.total) return;
+  const int b1 = min(b0 + c, sc.total);
+  int s, before;
+  locate(sc, context_lens, max_len, b0, s, before);
+
+  const int64_t head_stride = int64_t(kBlock) * D;
+  const int64_t block_stride = int64_t(num_kv_heads) * head_stride;
+  auto tile = [&](const typename KVT::storage* base, int32_t b) {
+    return base + int64_t(b) * block_stride + int64_t(kvh) * head_stride;
+  };
+  auto valid = [&](int32_t b) { return b >= 0 && b < num_blocks; };
+  // tr-read address of this lane: key lane/4, dims 4 (lane%4) of each slice
+  typedef __attribute__((address_space(3))) char lds_char_t;
+  lds_i16x4_t* const vt_base = reinterpret_cast<lds_i16x4_t*>(
+      (lds_char_t*)vl + (lane / 4) * M::kVStride + (lane % 4) * 8);
+
+  for (;;) {
+    const int len = seq_len(sc, context_lens, s, max_len);
+    const int n = blocks_of(len);
+    const int lo = max(b0, before), hi = min(b1, before + n);
+    if (lo < hi) {
+      const bool whole = lo == before && hi == before + n;
+      const int first = lo - before;
+      const int nblk = hi - lo;
+      const int last_rows = min(len, (hi - before) * kBlock) - (first + nblk - 1) * kBlock;
+      const int32_t* table = block_tables + int64_t(s) * max_blocks;
+      // scalar block ids, one block ahead of their use
+      int32_t id_cur = table[first];
+      int32_t id_next = nblk > 1 ? table[first + 1] : -1;
+      // Q^T as B operands (zero columns past the group)
+      u32x4 qb[M::kKSteps];
+      {
+        const auto rq = tile_resource(query + (int64_t(s) * num_q_heads + head) * D,
+                                      head_ok ? D * 2 : 0);
+#pragma unroll
+        for (int ks = 0; ks < M::kKSteps; ++ks)
+          qb[ks] = buffer_load16_cached(rq, uint32_t(qk_dim<KVT>(j, ks) * 2));
+      }
+      const int32_t b_first = valid(id_cur) ? id_cur : 0;
+      KRegs<KVT, D> kr;
+      VRegs<KVT, D> vr;
+      // V before K, the order of the loop's own loads, so that each wait
+      // inside the loop covers exactly the pieces it needs
+      load_v<KVT, D>(vr, tile(v_cache, b_first), lane);
+      __builtin_amdgcn_sched_barrier(0);
+      load_k<KVT, D>(kr, tile(k_cache, b_first), lane);
+      __builtin_amdgcn_sched_barrier(0);
+
+      f32x4_t acc[M::kMTiles];
+#pragma unroll
+      for (int mt = 0; mt < M::kMTiles; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      // running max starts finite: a fully masked block then gives weights
+      // 2^-inf = 0 instead of 2^(-inf + inf)
+      float m = kNoMax, l = 0.f;
+
+      for (int i = 0; i < nblk; ++i) {
+        const int rows = valid(id_cur) ? (i + 1 < nblk ? kBlock : last_rows) : 0;
+        // the block after this one, or a re-read of a block already read, so
+        // that every step has the same loads in flight
+        const int32_t bn = valid(id_next) ? id_next : (valid(id_cur) ? id_cur : b_first);
+        const int32_t id_new =
+            (i + 2 < nblk && first + i + 2 < max_blocks) ? table[first + i + 2] : -1;
+        stage_v<KVT, D>(vr, vl, lane, rows);
+        __builtin_amdgcn_sched_barrier(0);
+        load_v<KVT, D>(vr, tile(v_cache, bn), lane);
+        __builtin_amdgcn_sched_barrier(0);
+        // S^T = K . Q^T
+        f32x4_t st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < M::kKSteps; ++ks) st = mfma_k32(k_operand<KVT, D>(kr, ks), qb[ks], st);
+        load_k<KVT, D>(kr, tile(k_cache, bn), lane);
+        // online softmax over this lane's 4 keys of its head
+        float sv[4];
+        bool raise = false;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float t = st[r] * scale_log2;
+          sv[r] = 4 * j + r < rows ? t : -INFINITY;
+          raise |= sv[r] > m + kRaiseM;
+        }
+        if (__builtin_expect(__ballot(raise) != 0, 0)) {
+          float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+          bm = fmaxf(bm, shfl_xor(bm, 16));
+          bm = fmaxf(bm, shfl_xor(bm, 32));
+          const float mn = fmaxf(m, bm);
+          const float alpha = fast_exp2(m - mn);
+          m = mn;
+          l *= alpha;
+#pragma unroll
+          for (int mt = 0; mt < M::kMTiles; ++mt) acc[mt] *= alpha;
+        }
+        float p[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p[r] = fast_exp2(sv[r] - m);
+        l += (p[0] + p[1]) + (p[2] + p[3]);
+        // P^T = hi + lo, both bf16
+        uint32_t hi[2], lo[2];
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+          const uint32_t a = __float_as_uint(p[2 * w]), b = __float_as_uint(p[2 * w + 1]);
+          hi[w] = (b & 0xffff0000u) | (a >> 16);
+          lo[w] = pack_bf16_rne(p[2 * w] - __uint_as_float(a & 0xffff0000u),
+                                p[2 * w + 1] - __uint_as_float(b & 0xffff0000u));
+        }
+        const i16x4_t phi = __builtin_bit_cast(i16x4_t, uint2{hi[0], hi[1]});
+        const i16x4_t plo = __builtin_bit_cast(i16x4_t, uint2{lo[0], lo[1]});
+        // O^T += V^T . P^T
+#pragma unroll
+        for (int mt = 0; mt < M::kMTiles; ++mt) {
+          const i16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(vt_base + mt * 4);
+          acc[mt] = mfma_k16(a, phi, acc[mt]);
+          acc[mt] = mfma_k16(a, plo, acc[mt]);
+        }
+        id_cur = id_next;
+        id_next = id_new;
+      }
+      // sum of weights of each head over the four lane groups
+      float lt = l + shfl_xor(l, 16);
+      lt += shfl_xor(lt, 32);
+      if (head_ok) {
+        if (whole) {
+          const float f = v_scale / lt;
+          uint16_t* o = out + (int64_t(s) * num_q_heads + head) * D + 4 * j;
+#pragma unroll
+          for (int mt = 0; mt < M::kMTiles; ++mt) {
+            const uint2 w = {pack_bf16_rne(acc[mt][0] * f, acc[mt][1] * f),
+                             pack_bf16_rne(acc[mt][2] * f, acc[mt][3] * f)};
+            *reinterpret_cast<uint2*>(o + mt * 16) = w;
+          }
+        } else {
+          const int64_t idx = int64_t(g + s) * num_q_heads + head;
+          float* o = rec_out + idx * D + 4 * j;
+#pragma unroll
+          for (int mt = 0; mt < M::kMTiles; ++mt)
+            *reinterpret_cast<float4*>(o + mt * 16) =
+                make_float4(acc[mt][0], acc[mt][1], acc[mt][2], acc[mt][3]);
+          if (j == 0) reinterpret_cast<float2*>(rec_ml)[idx] = make_float2(m, lt);
+        }
+      }
+    }
+    before += n;
+    ++s;
+    if (before >= b1 || s >= num_seqs) break;
+  }
+}
+
+template <typename KVT, int D>
+static pkv_status launch_one(const DecodeMfmaArgs& a) {
+  hipLaunchKernelGGL((decode_mfma_kernel<KVT, D>), dim3(a.num_chunks * a.num_kv_heads),
+                     dim3(kWave), 0, as_stream(a.stream), static_cast<uint16_t*>(a.out),
+                     static_cast<const uint16_t*>(a.query),
+                     static_cast<const typename KVT::storage*>(a.k_cache),
+                     static_cast<const typename KVT::storage*>(a.v_cache), a.num_blocks,
+                     a.block_tables, a.max_blocks, a.context_lens, a.num_seqs, a.max_len,
+                     a.num_q_heads, a.num_kv_heads, a.num_q_heads / a.num_kv_heads,
+                     a.scale_log2, a.v_scale, a.num_chunks, a.fixed_chunk, a.rec_out,
+                     a.rec_ml);
+  return launch_status();
+}
+
+bool decode_mfma_supported(pkv_dtype q_dtype, pkv_dtype kv_dtype, int head_dim, int group) {
+  return q_dtype == PKV_BF16 && (kv_dtype == PKV_BF16 || kv_dtype == PKV_FP8_E4M3) &&
+         (head_dim == 64 || head_dim == 128) && group >= 1 && group <= 16;
+}
+
+pkv_status launch_decode_mfma(const DecodeMfmaArgs& a) {
+  if (a.kv_dtype == PKV_BF16)
+    return a.head_dim == 64 ? launch_one<BF16, 64>(a) : launch_one<BF16, 128>(a);
+  return a.head_dim == 64 ? launch_one<FP8, 64>(a) : launch_one<FP8, 128>(a);
+}
+
+}  // namespace pkv

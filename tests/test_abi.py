@@ -120,16 +120,20 @@ def test_decode_errors(lib):
     assert _decode(lib, qd=FP8, kvd=FP8) == UNSUP
     assert _decode(lib, maxb=10) == SHAPE                  # 160 tokens < max_context_len
     assert _decode(lib, part=100) == SHAPE                 # not a multiple of 16
-    assert _decode(lib, part=2048) == SHAPE
+    assert _decode(lib, part=-16) == SHAPE
     assert _decode(lib, kvd=FP8, ks=0.0) == SHAPE
     assert _decode(lib, nb=0) == SHAPE
     need = lib.paged_attention_decode_workspace_size(4, 32, 8, 128, 1000, 0)
-    pt = lib.paged_attention_decode_partition_tokens(4, 8, 1000, 0)
-    assert need >= 4 * 32 * -(-1000 // pt) * (128 + 2) * 4
+    chunks = lib.paged_attention_decode_num_chunks(4, 32, 8, 1000, 0)
+    # one partial per (chunk, sequence) pair that overlaps: at most chunks + seqs
+    assert need >= (chunks + 4) * 32 * (128 + 2) * 4
     assert _decode(lib, wsb=need - 1) == WS
     assert _decode(lib, ws=None) == WS
-    assert lib.paged_attention_decode_partition_tokens(4, 8, 1000, 0) in (256, 512)
-    assert lib.paged_attention_decode_partition_tokens(4, 8, 1000, 64) == 64
+    # 4 x 63 blocks at most; chunks of at least 4 blocks
+    assert 1 <= chunks <= 63
+    assert lib.paged_attention_decode_num_chunks(4, 32, 8, 1000, 64) == 63
+    assert lib.paged_attention_decode_num_chunks(4, 32, 8, 1000, 48) == 84
+    assert lib.paged_attention_decode_num_chunks(4, 32, 8, 1000, 40) == -1
 
 
 def test_prefill_errors(lib):

@@ -43,7 +43,7 @@ def test_fig2_toy_step(placement):
 def _random_decode(hq, hkv, d, q_dtype, kv_dtype, lengths, seed, std=1.0):
     """A decode batch with a shuffled pool and NaN-free random caches."""
     rng = np.random.default_rng(seed)
-    nb = sum(P.blocks_needed(L) for L in lengths) + 3
+    nb = sum(P.blocks_needed(max(L, 1)) for L in lengths) + 3
     pool = BlockPool(nb, rng.permutation(nb))
     seqs = [Sequence.fresh(pool, max(L, 1)) for L in lengths]
     tables = tables_array(seqs)
@@ -192,7 +192,9 @@ def test_poisoned_unused_slots_do_not_leak():
 
 def test_shared_prefix_rows_are_identical():
     """Two sequences on the same 125 shared blocks with byte-equal tails and
-    equal queries give bitwise-equal outputs."""
+    equal queries: bitwise-equal outputs when each sequence is one work chunk
+    (same summation order), and equal to rounding under the library's split,
+    which cuts the two sequences at different points."""
     announce("decode shared prefix")
     nb, hkv, d = 130, 8, 128
     kc = R.normal((nb, hkv, 16, d), F.BF16, 77, 1, DEV)
@@ -202,9 +204,12 @@ def test_shared_prefix_rows_are_identical():
     tables = torch.tensor([shared + [127], shared + [128]], dtype=torch.int32, device=DEV)
     q = R.normal((1, 32, d), F.BF16, 77, 3, DEV).repeat(2, 1, 1)
     L = torch.tensor([2010, 2010], dtype=torch.int32, device=DEV)
-    out = pk.paged_attention_decode(q, kc, vc, tables, L, 2010, 0.088)
+    out = pk.paged_attention_decode(q, kc, vc, tables, L, 2010, 0.088, partition_tokens=126 * 16)
+    auto = pk.paged_attention_decode(q, kc, vc, tables, L, 2010, 0.088)
     torch.cuda.synchronize()
     assert torch.equal(out[0], out[1])
+    diff = (auto[0].float() - auto[1].float()).abs()
+    assert float(diff.max()) <= 2.0 ** -8 * float(auto.float().abs().max())
 
 
 def test_llama2_mha_two_layers_reduced():
@@ -227,3 +232,38 @@ def test_llama70b_fp8_reduced():
     rk, rv, _ = oracle_caches_after_step(s)
     ref = oracle_decode(s, rk, rv)
     assert_attention_close(as_f64(ds.out[0]), ref, kind_of(s), "config5 reduced")
+
+
+@pytest.mark.parametrize("num_seqs", [65, 150, 300])
+@pytest.mark.parametrize("partition", [0, 16, 48, 256])
+def test_decode_chunks_over_many_sequences(num_seqs, partition):
+    """Work chunks that end inside sequences, cover several short ones, and
+    batches wider than one wave (each lane then counts several sequences);
+    empty sequences at the start, in the middle and at the end."""
+    announce("decode chunking", num_seqs, "partition", partition)
+    rng = np.random.default_rng(num_seqs + partition)
+    lengths = [int(x) for x in rng.integers(0, 120, num_seqs)]
+    for i in (0, 1, num_seqs // 2, num_seqs - 1):
+        lengths[i] = 0
+    lengths[num_seqs // 3] = 700
+    q, kc, vc, tables, lens, ks, vs = _random_decode(16, 4, 128, F.BF16, F.BF16, lengths,
+                                                     seed=num_seqs)
+    out = pk.paged_attention_decode(q, kc, vc, torch.as_tensor(tables, device=DEV),
+                                    torch.as_tensor(lens, device=DEV), int(lens.max()),
+                                    0.088, 1.0, 1.0, partition)
+    torch.cuda.synchronize()
+    ref = P.decode_attention(host(q), F.BF16, host(kc), host(vc), F.BF16, tables, lens,
+                             0.088, 1.0, 1.0)
+    got = as_f64(out)
+    assert np.all(got[lens == 0] == 0.0)
+    assert_attention_close(got, ref, "bf16", f"chunks S{num_seqs} p{partition}")
+
+
+def test_decode_all_sequences_empty():
+    announce("decode all empty")
+    q, kc, vc, tables, lens, _, _ = _random_decode(8, 2, 64, F.BF16, F.BF16, [0, 0, 0], seed=3)
+    out = torch.full_like(q, float("nan"))
+    pk.paged_attention_decode(q, kc, vc, torch.as_tensor(tables, device=DEV),
+                              torch.as_tensor(lens, device=DEV), 16, 0.1, out=out)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0)
