@@ -182,7 +182,7 @@ def paged_attention_decode(query, k_cache, v_cache, block_tables, context_lens,
         out = torch.empty_like(query)
     need = decode_workspace_size(s, hq, hkv, d, max_context_len, partition_tokens)
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=query.device)
+        workspace = torch.zeros(max(need, 16), dtype=torch.uint8, device=query.device)
     assert block_tables.shape[0] >= s and context_lens.shape[0] >= s
     st = library().paged_attention_decode(
         _dev(out, "out", query.dtype), _dev(query, "query"), _dev(k_cache, "k_cache"),

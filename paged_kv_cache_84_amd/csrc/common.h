@@ -124,6 +124,13 @@ PKV_DEVICE float wave_sum(float v) {
   return v;
 }
 
+// A wave-uniform read of read-only memory through the constant address
+// space, which keeps it on the scalar unit (s_load) wherever it appears.
+typedef __attribute__((address_space(4))) const int32_t const_i32_t;
+PKV_DEVICE int32_t load_scalar(const int32_t* p, int64_t i) {
+  return ((const_i32_t*)p)[i];
+}
+
 // Sum of v over the lanes below this one.
 PKV_DEVICE int wave_exclusive_sum(int v) {
   const int lane = lane_id();

@@ -647,12 +647,14 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
 
 // ------------------------------------------------------------------ host
 
-// Chunks per kv head when the caller leaves the split to the library: enough
-// workgroups that every SIMD holds two to three waves (all resident at
-// once, so all finish together), never chunks below kMinChunkBlocks of the
-// largest possible batch.
+// Chunks per kv head when the caller leaves the split to the library: about
+// one wave per SIMD (1024 on 256 CUs).  All waves are then resident at once
+// and none shares its SIMD: when two decode waves share one, the older is
+// served first and the younger's chunk finishes a third later, which leaves
+// the end of the kernel to half the waves.  Never chunks below
+// kMinChunkBlocks of the largest possible batch.
 #ifndef PKV_DECODE_TARGET_WAVES
-#define PKV_DECODE_TARGET_WAVES 2048
+#define PKV_DECODE_TARGET_WAVES 1024
 #endif
 
 static size_t align256(size_t n) { return (n + 255) & ~size_t(255); }

@@ -31,6 +31,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 #include "abi_util.h"
 #include "common.h"
 #include "decode_mfma.h"
@@ -47,6 +49,12 @@ typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 constexpr float kRaiseM = 8.0f;   // log2 units, as in the vector kernel
 constexpr float kNoMax = -1e30f;
+
+// Blocks in flight per wave (1 or 2).
+#ifndef PKV_MFMA_DEPTH
+#define PKV_MFMA_DEPTH 1
+#endif
+static_assert(PKV_MFMA_DEPTH == 1 || PKV_MFMA_DEPTH == 2, "depth 1 or 2");
 
 PKV_DEVICE f32x4_t mfma_k32(u32x4 a, u32x4 b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -202,9 +210,6 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
       const int nblk = hi - lo;
       const int last_rows = min(len, (hi - before) * kBlock) - (first + nblk - 1) * kBlock;
       const int32_t* table = block_tables + int64_t(s) * max_blocks;
-      // scalar block ids, one block ahead of their use
-      int32_t id_cur = table[first];
-      int32_t id_next = nblk > 1 ? table[first + 1] : -1;
       // Q^T as B operands (zero columns past the group)
       u32x4 qb[M::kKSteps];
       {
@@ -214,15 +219,27 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
         for (int ks = 0; ks < M::kKSteps; ++ks)
           qb[ks] = buffer_load16_cached(rq, uint32_t(qk_dim<KVT>(j, ks) * 2));
       }
-      const int32_t b_first = valid(id_cur) ? id_cur : 0;
-      KRegs<KVT, D> kr;
-      VRegs<KVT, D> vr;
+      // kDepth K and V register sets used in turn: a block's pieces are
+      // replaced by those of the block kDepth ahead as soon as they are
+      // consumed (V when staged to LDS, K when its products are issued).
+      // Block ids come through the scalar cache one step ahead of that.
+      constexpr int kDepth = PKV_MFMA_DEPTH;
+      int32_t ids[kDepth + 1];
+#pragma unroll
+      for (int d = 0; d <= kDepth; ++d) ids[d] = d < nblk ? load_scalar(table, first + d) : -1;
+      const int32_t b_first = valid(ids[0]) ? ids[0] : 0;
+      KRegs<KVT, D> kr[kDepth];
+      VRegs<KVT, D> vr[kDepth];
       // V before K, the order of the loop's own loads, so that each wait
       // inside the loop covers exactly the pieces it needs
-      load_v<KVT, D>(vr, tile(v_cache, b_first), lane);
-      __builtin_amdgcn_sched_barrier(0);
-      load_k<KVT, D>(kr, tile(k_cache, b_first), lane);
-      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int d = 0; d < kDepth; ++d) {
+        const int32_t b = valid(ids[d]) ? ids[d] : b_first;
+        load_v<KVT, D>(vr[d], tile(v_cache, b), lane);
+        __builtin_amdgcn_sched_barrier(0);
+        load_k<KVT, D>(kr[d], tile(k_cache, b), lane);
+        __builtin_amdgcn_sched_barrier(0);
+      }
 
       f32x4_t acc[M::kMTiles];
 #pragma unroll
@@ -231,22 +248,24 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
       // 2^-inf = 0 instead of 2^(-inf + inf)
       float m = kNoMax, l = 0.f;
 
-      for (int i = 0; i < nblk; ++i) {
-        const int rows = valid(id_cur) ? (i + 1 < nblk ? kBlock : last_rows) : 0;
-        // the block after this one, or a re-read of a block already read, so
+      auto step = [&](auto slot_c, int i) {
+        constexpr int S = decltype(slot_c)::value;
+        const int rows = valid(ids[0]) ? (i + 1 < nblk ? kBlock : last_rows) : 0;
+        // the block kDepth ahead, or a re-read of a block already read, so
         // that every step has the same loads in flight
-        const int32_t bn = valid(id_next) ? id_next : (valid(id_cur) ? id_cur : b_first);
+        const int32_t bn = valid(ids[kDepth]) ? ids[kDepth] : (valid(ids[0]) ? ids[0] : b_first);
         const int32_t id_new =
-            (i + 2 < nblk && first + i + 2 < max_blocks) ? table[first + i + 2] : -1;
-        stage_v<KVT, D>(vr, vl, lane, rows);
+            i + kDepth + 1 < nblk ? load_scalar(table, first + i + kDepth + 1) : -1;
+        stage_v<KVT, D>(vr[S], vl, lane, rows);
         __builtin_amdgcn_sched_barrier(0);
-        load_v<KVT, D>(vr, tile(v_cache, bn), lane);
+        load_v<KVT, D>(vr[S], tile(v_cache, bn), lane);
         __builtin_amdgcn_sched_barrier(0);
         // S^T = K . Q^T
         f32x4_t st = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < M::kKSteps; ++ks) st = mfma_k32(k_operand<KVT, D>(kr, ks), qb[ks], st);
-        load_k<KVT, D>(kr, tile(k_cache, bn), lane);
+        for (int ks = 0; ks < M::kKSteps; ++ks)
+          st = mfma_k32(k_operand<KVT, D>(kr[S], ks), qb[ks], st);
+        load_k<KVT, D>(kr[S], tile(k_cache, bn), lane);
         // online softmax over this lane's 4 keys of its head
         float sv[4];
         bool raise = false;
@@ -289,8 +308,16 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
           acc[mt] = mfma_k16(a, phi, acc[mt]);
           acc[mt] = mfma_k16(a, plo, acc[mt]);
         }
-        id_cur = id_next;
-        id_next = id_new;
+#pragma unroll
+        for (int d = 0; d < kDepth; ++d) ids[d] = ids[d + 1];
+        ids[kDepth] = id_new;
+      };
+      for (int i = 0; i < nblk; i += kDepth) {
+        step(std::integral_constant<int, 0>{}, i);
+        if constexpr (kDepth > 1) {
+          if (i + 1 >= nblk) break;
+          step(std::integral_constant<int, 1>{}, i + 1);
+        }
       }
       // sum of weights of each head over the four lane groups
       float lt = l + shfl_xor(l, 16);

@@ -58,7 +58,7 @@ class DeviceStep:
             hq, hkv, d = step.num_q_heads, step.num_kv_heads, step.head_dim
             need = B.decode_workspace_size(self.num_decode, hq, hkv, d,
                                            self.max_context_len, partition_tokens)
-            self.workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+            self.workspace = torch.zeros(max(need, 16), dtype=torch.uint8, device=dev)
         else:
             self.workspace = None
 
