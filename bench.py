@@ -87,7 +87,7 @@ def _cpu_unit(seq):
                               d["lens"][seq:seq + 1], d["scale"])
 
 
-def cpu_baseline(step, budget_s=12.0):
+def cpu_baseline(step, budget_s=15.0):
     """The fp64 oracle, as written, over a sample of the decode batch's
     sequences, one process per core with one BLAS thread each."""
     from synth import rng as R
@@ -105,7 +105,7 @@ def cpu_baseline(step, budget_s=12.0):
         _cpu_unit(0)
         one = time.perf_counter() - t0
     per_pass = one * nseq / workers
-    passes = int(max(1, min(50, round(budget_s / max(per_pass, 1e-3)))))
+    passes = int(max(1, min(2000, round(budget_s / max(per_pass, 1e-3)))))
     units = list(range(nseq)) * passes
     ctx = mp.get_context("fork")
     t0 = time.perf_counter()
