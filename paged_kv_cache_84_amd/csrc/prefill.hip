@@ -44,7 +44,8 @@ extern "C" pkv_status paged_attention_prefill_chunk(
                 num_q_tokens, max_query_len, num_q_heads, num_kv_heads, head_dim,
                 softmax_scale, q_dtype, kv_dtype, k_scale, v_scale, stream};
   const int group = num_q_heads / num_kv_heads;
-  if (bf16 && head_dim == 128 && (group == 1 || group == 2 || group == 4 || group == 8))
+  if (bf16 && head_dim == 128 && softmax_scale > 0.f &&
+      (group == 1 || group == 2 || group == 4 || group == 8))
     return launch_prefill_mfma(a);
   return launch_prefill_rows(a);
 }
