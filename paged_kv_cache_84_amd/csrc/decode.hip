@@ -675,8 +675,10 @@ static bool make_plan(int32_t s, int32_t hq, int32_t hkv, int32_t d, int32_t max
     chunks = (bound + p.fixed_chunk - 1) / p.fixed_chunk;
   } else {
     p.fixed_chunk = 0;
-    const int waves_per_chunk = (hq / hkv + 3) / 4;
-    chunks = PKV_DECODE_TARGET_WAVES / (int64_t(hkv) * waves_per_chunk);
+    // one chunk per wave slot and kv head (the matrix-core kernel runs a
+    // whole query group in one wave; the vector kernel's second wave for
+    // groups above four shares its chunk's tiles through the cache)
+    chunks = PKV_DECODE_TARGET_WAVES / int64_t(hkv);
     chunks = std::min<int64_t>(chunks, (bound + kMinChunkBlocks - 1) / kMinChunkBlocks);
   }
   chunks = std::max<int64_t>(chunks, 1);
