@@ -566,24 +566,29 @@ __global__ __launch_bounds__(256) void prefill_rows_kernel(
   }
 }
 
-// One workgroup (one wave) per (head, sequence): merge the partials of a
+// One workgroup of W waves per (head, sequence): merge the partials of a
 // sequence that spans several chunks,
 //   out = sum_k e^{m_k - M} o_k / sum_k e^{m_k - M} l_k,   M = max_k m_k
 // (m in log2 units).  Sequences inside one chunk were written by the chunk
-// kernel; empty ones get zeros here.  The weights of up to 64 partials at a
-// time are computed one per lane and passed through LDS, so the partials'
-// loads do not wait on each other.
-template <typename QT, int D>
-__global__ __launch_bounds__(64) void decode_merge_kernel(
+// kernel; empty ones get zeros here.  Each wave takes every W-th group of
+// 64 partials; within a group the weights are computed one per lane and
+// passed through LDS, so the partials' loads do not wait on each other.  The
+// waves' sums meet in LDS at the end.  (W = 4 for fixed partitions, which
+// leave hundreds of partials per sequence; 1 for the library's own split,
+// which leaves a few.)
+template <typename QT, int D, int W>
+__global__ __launch_bounds__(kWave * W) void decode_merge_kernel(
     typename QT::storage* __restrict__ out, const float* __restrict__ rec_out,
     const float* __restrict__ rec_ml, const int32_t* __restrict__ context_lens,
     int32_t num_seqs, int32_t max_len, int32_t num_q_heads, int32_t num_chunks,
     int32_t fixed_chunk, float v_scale) {
   constexpr int kPer = D / kWave;
-  __shared__ float wts[kWave];
+  __shared__ float wts[W][kWave];
+  __shared__ float part[W][D + 1];
   const int h = blockIdx.x;
   const int seq = blockIdx.y;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
   const BatchScan sc = scan_batch(context_lens, num_seqs, max_len);
   const int owner = seq / sc.k;
   int before = __builtin_amdgcn_readlane(sc.first, owner);
@@ -592,8 +597,10 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
   const int n = blocks_of(seq_len(sc, context_lens, seq, max_len));
   typename QT::storage* o = out + (int64_t(seq) * num_q_heads + h) * D;
   if (n == 0) {
+    if (wave == 0) {
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) store_out<QT>(o + lane + i * kWave, 0.f);
+      for (int i = 0; i < kPer; ++i) store_out<QT>(o + lane + i * kWave, 0.f);
+    }
     return;
   }
   const int c = chunk_blocks(sc.total, num_chunks, fixed_chunk);
@@ -609,7 +616,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
   big = wave_max(big);
   float acc[kPer] = {};
   float den = 0.f;
-  for (int k0 = 0; k0 < nparts; k0 += kWave) {
+  for (int k0 = wave * kWave; k0 < nparts; k0 += kWave * W) {
     const int k = k0 + lane;
     float wk = 0.f;
     if (k < nparts) {
@@ -617,8 +624,8 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
       wk = fast_exp2(x.x - big);
       den = fmaf(wk, x.y, den);
     }
-    wts[lane] = wk;
-    __syncthreads();
+    wts[wave][lane] = wk;
+    __builtin_amdgcn_wave_barrier();
     const int cnt = min(kWave, nparts - k0);
     const float* po = rec_out + (base + k0 * stride) * D + lane;
     const int64_t step = stride * D;
@@ -632,17 +639,30 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int i = 0; i < kPer; ++i) acc[i] = fmaf(wts[j + u], x[u][i], acc[i]);
+        for (int i = 0; i < kPer; ++i) acc[i] = fmaf(wts[wave][j + u], x[u][i], acc[i]);
     }
     for (; j < cnt; ++j)
 #pragma unroll
-      for (int i = 0; i < kPer; ++i) acc[i] = fmaf(wts[j], po[j * step + i * kWave], acc[i]);
-    __syncthreads();
+      for (int i = 0; i < kPer; ++i) acc[i] = fmaf(wts[wave][j], po[j * step + i * kWave], acc[i]);
+    __builtin_amdgcn_wave_barrier();
   }
   den = wave_sum(den);
-  const float f = v_scale / den;
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) store_out<QT>(o + lane + i * kWave, acc[i] * f);
+  for (int i = 0; i < kPer; ++i) part[wave][lane + i * kWave] = acc[i];
+  if (lane == 0) part[wave][D] = den;
+  __syncthreads();
+  if (wave != 0) return;
+  float dsum = 0.f;
+#pragma unroll
+  for (int w = 0; w < W; ++w) dsum += part[w][D];
+  const float f = v_scale / dsum;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    float a = 0.f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) a += part[w][lane + i * kWave];
+    store_out<QT>(o + lane + i * kWave, a * f);
+  }
 }
 
 // ------------------------------------------------------------------ host
@@ -698,9 +718,14 @@ static pkv_status launch_merge(void* out, const int32_t* lens, int32_t s, int32_
   const float* rec_out = static_cast<const float*>(ws);
   const float* rec_ml =
       reinterpret_cast<const float*>(static_cast<const char*>(ws) + plan.out_bytes);
-  hipLaunchKernelGGL((decode_merge_kernel<QT, D>), dim3(hq, s), dim3(kWave), 0, st,
-                     static_cast<typename QT::storage*>(out), rec_out, rec_ml, lens, s,
-                     max_len, hq, plan.num_chunks, plan.fixed_chunk, v_scale);
+  if (plan.fixed_chunk > 0)
+    hipLaunchKernelGGL((decode_merge_kernel<QT, D, 4>), dim3(hq, s), dim3(kWave * 4), 0, st,
+                       static_cast<typename QT::storage*>(out), rec_out, rec_ml, lens, s,
+                       max_len, hq, plan.num_chunks, plan.fixed_chunk, v_scale);
+  else
+    hipLaunchKernelGGL((decode_merge_kernel<QT, D, 1>), dim3(hq, s), dim3(kWave), 0, st,
+                       static_cast<typename QT::storage*>(out), rec_out, rec_ml, lens, s,
+                       max_len, hq, plan.num_chunks, plan.fixed_chunk, v_scale);
   return launch_status();
 }
 
@@ -858,11 +883,25 @@ extern "C" pkv_status paged_attention_decode(
 
 #if PKV_DECODE_USE_MFMA
   if (decode_mfma_supported(q_dtype, kv_dtype, head_dim, group)) {
+    // Fixed partitions are walked several to a wave, so that a short
+    // partition does not cost a wave start (and the wave's loads run on
+    // across the partitions' boundaries).  A bf16 block keeps one wave per
+    // SIMD busy; an fp8 block carries half the bytes for the same products,
+    // so fp8 caches get PKV_FP8_WAVES_PER_SIMD waves per SIMD.
+#ifndef PKV_FP8_WAVES_PER_SIMD
+#define PKV_FP8_WAVES_PER_SIMD 3
+#endif
+    const int64_t target = int64_t(PKV_DECODE_TARGET_WAVES) *
+                           (kv_dtype == PKV_FP8_E4M3 ? PKV_FP8_WAVES_PER_SIMD : 1);
+    const int64_t per_wave =
+        lay.fixed_chunk > 0
+            ? std::max<int64_t>(1, (int64_t(lay.num_chunks) * num_kv_heads + target - 1) / target)
+            : 1;
     DecodeMfmaArgs a{out, query, k_cache, v_cache, num_blocks, block_tables,
                      max_blocks_per_seq, context_lens, num_seqs, max_context_len,
                      num_q_heads, num_kv_heads, head_dim, kv_dtype,
                      softmax_scale * k_scale * kLog2e, v_scale, lay.num_chunks,
-                     lay.fixed_chunk, static_cast<float*>(workspace),
+                     lay.fixed_chunk, int32_t(per_wave), static_cast<float*>(workspace),
                      reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.out_bytes),
                      stream};
     if (launch_decode_mfma(a) != PKV_OK) return PKV_ERR_LAUNCH;

@@ -21,6 +21,7 @@ struct DecodeMfmaArgs {
   pkv_dtype kv_dtype;
   float scale_log2, v_scale;
   int32_t num_chunks, fixed_chunk;   // the work split (see decode_sched.h)
+  int32_t chunks_per_wave;           // consecutive chunks one wave walks
   float* rec_out;                    // partials of sequences that span chunks
   float* rec_ml;
   void* stream;

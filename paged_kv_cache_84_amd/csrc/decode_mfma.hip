@@ -50,12 +50,6 @@ typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 constexpr float kRaiseM = 8.0f;   // log2 units, as in the vector kernel
 constexpr float kNoMax = -1e30f;
 
-// Blocks in flight per wave (1 or 2).
-#ifndef PKV_MFMA_DEPTH
-#define PKV_MFMA_DEPTH 1
-#endif
-static_assert(PKV_MFMA_DEPTH == 1 || PKV_MFMA_DEPTH == 2, "depth 1 or 2");
-
 PKV_DEVICE f32x4_t mfma_k32(u32x4 a, u32x4 b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
@@ -161,6 +155,24 @@ PKV_DEVICE void stage_v(VRegs<KVT, D>& r, char* vl, int lane, int rows) {
 
 }  // namespace
 
+// Where a block-range cursor stands: sequence s holds the n blocks
+// [before, before + n) of the flattened batch.
+struct SeqCursor {
+  int s, before, n, len;
+};
+
+// Move the cursor forward to the sequence holding block x (x below the
+// batch's block count, so the walk ends inside the batch).
+PKV_DEVICE void cursor_to(SeqCursor& c, int x, const BatchScan& sc, const int32_t* lens,
+                          int max_len) {
+  while (x >= c.before + c.n) {
+    c.before += c.n;
+    ++c.s;
+    c.len = seq_len(sc, lens, c.s, max_len);
+    c.n = blocks_of(c.len);
+  }
+}
+
 template <typename KVT, int D>
 __global__ __launch_bounds__(64) void decode_mfma_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
@@ -169,25 +181,25 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
     const int32_t* __restrict__ block_tables, int32_t max_blocks,
     const int32_t* __restrict__ context_lens, int32_t num_seqs, int32_t max_len,
     int32_t num_q_heads, int32_t num_kv_heads, int32_t group, float scale_log2,
-    float v_scale, int32_t num_chunks, int32_t fixed_chunk, float* __restrict__ rec_out,
-    float* __restrict__ rec_ml) {
+    float v_scale, int32_t num_chunks, int32_t fixed_chunk, int32_t chunks_per_wave,
+    float* __restrict__ rec_out, float* __restrict__ rec_ml) {
   using M = MGeom<KVT, D>;
   __shared__ __align__(16) char vl[kBlock * M::kVStride];
   const int kvh = blockIdx.x % num_kv_heads;
-  const int g = blockIdx.x / num_kv_heads;
+  const int wg = blockIdx.x / num_kv_heads;
   const int lane = lane_id();
   const int n16 = lane % 16;          // head column of this lane
   const int j = lane / 16;            // lane group
   const bool head_ok = n16 < group;
   const int head = kvh * group + (head_ok ? n16 : 0);
 
+  // This wave walks the blocks [b0, b1) of the flattened batch: chunks
+  // wg * chunks_per_wave .. + chunks_per_wave - 1, each of c blocks.
   const BatchScan sc = scan_batch(context_lens, num_seqs, max_len);
   const int c = chunk_blocks(sc.total, num_chunks, fixed_chunk);
-  const int b0 = g * c;
+  const int b0 = wg * chunks_per_wave * c;
   if (b0 >= sc.total) return;
-  const int b1 = min(b0 + c, sc.total);
-  int s, before;
-  locate(sc, context_lens, max_len, b0, s, before);
+  const int b1 = min(b0 + chunks_per_wave * c, sc.total);
 
   const int64_t head_stride = int64_t(kBlock) * D;
   const int64_t block_stride = int64_t(num_kv_heads) * head_stride;
@@ -195,137 +207,144 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
     return base + int64_t(b) * block_stride + int64_t(kvh) * head_stride;
   };
   auto valid = [&](int32_t b) { return b >= 0 && b < num_blocks; };
+  auto table_id = [&](const SeqCursor& q, int x) -> int32_t {
+    const int i = x - q.before;
+    return i < max_blocks ? load_scalar(block_tables, int64_t(q.s) * max_blocks + i) : -1;
+  };
+  // Q^T of sequence s as B operands (zero columns past the group)
+  auto load_q = [&](int s, u32x4 (&qb)[M::kKSteps]) {
+    const auto rq = tile_resource(query + (int64_t(s) * num_q_heads + head) * D,
+                                  head_ok ? D * 2 : 0);
+#pragma unroll
+    for (int ks = 0; ks < M::kKSteps; ++ks)
+      qb[ks] = buffer_load16_cached(rq, uint32_t(qk_dim<KVT>(j, ks) * 2));
+  };
   // tr-read address of this lane: key lane/4, dims 4 (lane%4) of each slice
   typedef __attribute__((address_space(3))) char lds_char_t;
   lds_i16x4_t* const vt_base = reinterpret_cast<lds_i16x4_t*>(
       (lds_char_t*)vl + (lane / 4) * M::kVStride + (lane % 4) * 8);
 
-  for (;;) {
-    const int len = seq_len(sc, context_lens, s, max_len);
-    const int n = blocks_of(len);
-    const int lo = max(b0, before), hi = min(b1, before + n);
-    if (lo < hi) {
-      const bool whole = lo == before && hi == before + n;
-      const int first = lo - before;
-      const int nblk = hi - lo;
-      const int last_rows = min(len, (hi - before) * kBlock) - (first + nblk - 1) * kBlock;
-      const int32_t* table = block_tables + int64_t(s) * max_blocks;
-      // Q^T as B operands (zero columns past the group)
-      u32x4 qb[M::kKSteps];
-      {
-        const auto rq = tile_resource(query + (int64_t(s) * num_q_heads + head) * D,
-                                      head_ok ? D * 2 : 0);
-#pragma unroll
-        for (int ks = 0; ks < M::kKSteps; ++ks)
-          qb[ks] = buffer_load16_cached(rq, uint32_t(qk_dim<KVT>(j, ks) * 2));
-      }
-      // kDepth K and V register sets used in turn: a block's pieces are
-      // replaced by those of the block kDepth ahead as soon as they are
-      // consumed (V when staged to LDS, K when its products are issued).
-      // Block ids come through the scalar cache one step ahead of that.
-      constexpr int kDepth = PKV_MFMA_DEPTH;
-      int32_t ids[kDepth + 1];
-#pragma unroll
-      for (int d = 0; d <= kDepth; ++d) ids[d] = d < nblk ? load_scalar(table, first + d) : -1;
-      const int32_t b_first = valid(ids[0]) ? ids[0] : 0;
-      KRegs<KVT, D> kr[kDepth];
-      VRegs<KVT, D> vr[kDepth];
-      // V before K, the order of the loop's own loads, so that each wait
-      // inside the loop covers exactly the pieces it needs
-#pragma unroll
-      for (int d = 0; d < kDepth; ++d) {
-        const int32_t b = valid(ids[d]) ? ids[d] : b_first;
-        load_v<KVT, D>(vr[d], tile(v_cache, b), lane);
-        __builtin_amdgcn_sched_barrier(0);
-        load_k<KVT, D>(kr[d], tile(k_cache, b), lane);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+  // Three cursors walk the range: `cc` at the block being multiplied, `lc`
+  // one block ahead (its K/V pieces and, on entering a sequence, its Q are
+  // in flight) and `ic` two blocks ahead (its block id is in flight through
+  // the scalar cache).  Loads therefore cross sequence and chunk boundaries
+  // without a pause; past b1 they re-read a block already read.
+  SeqCursor cc;
+  locate(sc, context_lens, max_len, b0, cc.s, cc.before);
+  cc.len = seq_len(sc, context_lens, cc.s, max_len);
+  cc.n = blocks_of(cc.len);
+  SeqCursor lc = cc, ic = cc;
+  u32x4 qb[M::kKSteps], qn[M::kKSteps];
+  load_q(cc.s, qb);
+  int32_t id_cur = table_id(cc, b0);
+  int32_t id_next = -1;
+  if (b0 + 1 < b1) {
+    cursor_to(ic, b0 + 1, sc, context_lens, max_len);
+    id_next = table_id(ic, b0 + 1);
+  }
+  const int32_t b_any = valid(id_cur) ? id_cur : 0;   // a block to re-read
+  KRegs<KVT, D> kr;
+  VRegs<KVT, D> vr;
+  // V before K, the order of the loop's own loads, so that each wait inside
+  // the loop covers exactly the pieces it needs
+  load_v<KVT, D>(vr, tile(v_cache, b_any), lane);
+  __builtin_amdgcn_sched_barrier(0);
+  load_k<KVT, D>(kr, tile(k_cache, b_any), lane);
+  __builtin_amdgcn_sched_barrier(0);
 
-      f32x4_t acc[M::kMTiles];
+  f32x4_t acc[M::kMTiles];
 #pragma unroll
-      for (int mt = 0; mt < M::kMTiles; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      // running max starts finite: a fully masked block then gives weights
-      // 2^-inf = 0 instead of 2^(-inf + inf)
-      float m = kNoMax, l = 0.f;
+  for (int mt = 0; mt < M::kMTiles; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // running max starts finite: a fully masked block then gives weights
+  // 2^-inf = 0 instead of 2^(-inf + inf)
+  float m = kNoMax, l = 0.f;
+  int seg_start = b0;
+  int chunk = b0 / c;                 // chunk of the current segment
+  int chunk_end = b0 + c;             // its end
 
-      auto step = [&](auto slot_c, int i) {
-        constexpr int S = decltype(slot_c)::value;
-        const int rows = valid(ids[0]) ? (i + 1 < nblk ? kBlock : last_rows) : 0;
-        // the block kDepth ahead, or a re-read of a block already read, so
-        // that every step has the same loads in flight
-        const int32_t bn = valid(ids[kDepth]) ? ids[kDepth] : (valid(ids[0]) ? ids[0] : b_first);
-        const int32_t id_new =
-            i + kDepth + 1 < nblk ? load_scalar(table, first + i + kDepth + 1) : -1;
-        stage_v<KVT, D>(vr[S], vl, lane, rows);
-        __builtin_amdgcn_sched_barrier(0);
-        load_v<KVT, D>(vr[S], tile(v_cache, bn), lane);
-        __builtin_amdgcn_sched_barrier(0);
-        // S^T = K . Q^T
-        f32x4_t st = {0.f, 0.f, 0.f, 0.f};
+  for (int x = b0; x < b1; ++x) {
+    const int i = x - cc.before;                       // block of sequence cc.s
+    const int rows = valid(id_cur) ? min(kBlock, cc.len - i * kBlock) : 0;
+    // the next block (possibly of the next sequence), or a re-read past b1
+    const bool more = x + 1 < b1;
+    const int32_t bn = (more && valid(id_next)) ? id_next : b_any;
+    stage_v<KVT, D>(vr, vl, lane, rows);
+    __builtin_amdgcn_sched_barrier(0);
+    load_v<KVT, D>(vr, tile(v_cache, bn), lane);
+    __builtin_amdgcn_sched_barrier(0);
+    // Q of a sequence entered by the next block
+    const bool new_seq = more && x + 1 >= lc.before + lc.n;
+    if (new_seq) {
+      cursor_to(lc, x + 1, sc, context_lens, max_len);
+      load_q(lc.s, qn);
+    }
+    // the id two blocks ahead, requested only once bn has been consumed:
+    // waiting for one scalar load waits for all of them
+    int32_t id_new = -1;
+    if (x + 2 < b1) {
+      cursor_to(ic, x + 2, sc, context_lens, max_len);
+      id_new = table_id(ic, x + 2);
+    }
+    // S^T = K . Q^T
+    f32x4_t st = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < M::kKSteps; ++ks)
-          st = mfma_k32(k_operand<KVT, D>(kr[S], ks), qb[ks], st);
-        load_k<KVT, D>(kr[S], tile(k_cache, bn), lane);
-        // online softmax over this lane's 4 keys of its head
-        float sv[4];
-        bool raise = false;
+    for (int ks = 0; ks < M::kKSteps; ++ks) st = mfma_k32(k_operand<KVT, D>(kr, ks), qb[ks], st);
+    load_k<KVT, D>(kr, tile(k_cache, bn), lane);
+    // online softmax over this lane's 4 keys of its head
+    float sv[4];
+    bool raise = false;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float t = st[r] * scale_log2;
-          sv[r] = 4 * j + r < rows ? t : -INFINITY;
-          raise |= sv[r] > m + kRaiseM;
-        }
-        if (__builtin_expect(__ballot(raise) != 0, 0)) {
-          float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-          bm = fmaxf(bm, shfl_xor(bm, 16));
-          bm = fmaxf(bm, shfl_xor(bm, 32));
-          const float mn = fmaxf(m, bm);
-          const float alpha = fast_exp2(m - mn);
-          m = mn;
-          l *= alpha;
+    for (int r = 0; r < 4; ++r) {
+      const float t = st[r] * scale_log2;
+      sv[r] = 4 * j + r < rows ? t : -INFINITY;
+      raise |= sv[r] > m + kRaiseM;
+    }
+    if (__builtin_expect(__ballot(raise) != 0, 0)) {
+      float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+      bm = fmaxf(bm, shfl_xor(bm, 16));
+      bm = fmaxf(bm, shfl_xor(bm, 32));
+      const float mn = fmaxf(m, bm);
+      const float alpha = fast_exp2(m - mn);
+      m = mn;
+      l *= alpha;
 #pragma unroll
-          for (int mt = 0; mt < M::kMTiles; ++mt) acc[mt] *= alpha;
-        }
-        float p[4];
+      for (int mt = 0; mt < M::kMTiles; ++mt) acc[mt] *= alpha;
+    }
+    float p[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) p[r] = fast_exp2(sv[r] - m);
-        l += (p[0] + p[1]) + (p[2] + p[3]);
-        // P^T = hi + lo, both bf16
-        uint32_t hi[2], lo[2];
+    for (int r = 0; r < 4; ++r) p[r] = fast_exp2(sv[r] - m);
+    l += (p[0] + p[1]) + (p[2] + p[3]);
+    // P^T = hi + lo, both bf16
+    uint32_t hi[2], lo[2];
 #pragma unroll
-        for (int w = 0; w < 2; ++w) {
-          const uint32_t a = __float_as_uint(p[2 * w]), b = __float_as_uint(p[2 * w + 1]);
-          hi[w] = (b & 0xffff0000u) | (a >> 16);
-          lo[w] = pack_bf16_rne(p[2 * w] - __uint_as_float(a & 0xffff0000u),
-                                p[2 * w + 1] - __uint_as_float(b & 0xffff0000u));
-        }
-        const i16x4_t phi = __builtin_bit_cast(i16x4_t, uint2{hi[0], hi[1]});
-        const i16x4_t plo = __builtin_bit_cast(i16x4_t, uint2{lo[0], lo[1]});
-        // O^T += V^T . P^T
+    for (int w = 0; w < 2; ++w) {
+      const uint32_t a = __float_as_uint(p[2 * w]), b = __float_as_uint(p[2 * w + 1]);
+      hi[w] = (b & 0xffff0000u) | (a >> 16);
+      lo[w] = pack_bf16_rne(p[2 * w] - __uint_as_float(a & 0xffff0000u),
+                            p[2 * w + 1] - __uint_as_float(b & 0xffff0000u));
+    }
+    const i16x4_t phi = __builtin_bit_cast(i16x4_t, uint2{hi[0], hi[1]});
+    const i16x4_t plo = __builtin_bit_cast(i16x4_t, uint2{lo[0], lo[1]});
+    // O^T += V^T . P^T
 #pragma unroll
-        for (int mt = 0; mt < M::kMTiles; ++mt) {
-          const i16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(vt_base + mt * 4);
-          acc[mt] = mfma_k16(a, phi, acc[mt]);
-          acc[mt] = mfma_k16(a, plo, acc[mt]);
-        }
-#pragma unroll
-        for (int d = 0; d < kDepth; ++d) ids[d] = ids[d + 1];
-        ids[kDepth] = id_new;
-      };
-      for (int i = 0; i < nblk; i += kDepth) {
-        step(std::integral_constant<int, 0>{}, i);
-        if constexpr (kDepth > 1) {
-          if (i + 1 >= nblk) break;
-          step(std::integral_constant<int, 1>{}, i + 1);
-        }
-      }
+    for (int mt = 0; mt < M::kMTiles; ++mt) {
+      const i16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(vt_base + mt * 4);
+      acc[mt] = mfma_k16(a, phi, acc[mt]);
+      acc[mt] = mfma_k16(a, plo, acc[mt]);
+    }
+    id_cur = id_next;
+    id_next = id_new;
+
+    // A segment ends with its sequence, at a chunk boundary, or at b1.
+    const int seq_end = cc.before + cc.n;
+    if (x + 1 == seq_end || x + 1 == chunk_end || !more) {
       // sum of weights of each head over the four lane groups
       float lt = l + shfl_xor(l, 16);
       lt += shfl_xor(lt, 32);
       if (head_ok) {
-        if (whole) {
+        if (seg_start == cc.before && x + 1 == seq_end) {
           const float f = v_scale / lt;
-          uint16_t* o = out + (int64_t(s) * num_q_heads + head) * D + 4 * j;
+          uint16_t* o = out + (int64_t(cc.s) * num_q_heads + head) * D + 4 * j;
 #pragma unroll
           for (int mt = 0; mt < M::kMTiles; ++mt) {
             const uint2 w = {pack_bf16_rne(acc[mt][0] * f, acc[mt][1] * f),
@@ -333,7 +352,8 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
             *reinterpret_cast<uint2*>(o + mt * 16) = w;
           }
         } else {
-          const int64_t idx = int64_t(g + s) * num_q_heads + head;
+          // the partial of (chunk seg_start / c, sequence) -> record chunk + sequence
+          const int64_t idx = int64_t(chunk + cc.s) * num_q_heads + head;
           float* o = rec_out + idx * D + 4 * j;
 #pragma unroll
           for (int mt = 0; mt < M::kMTiles; ++mt)
@@ -342,24 +362,36 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
           if (j == 0) reinterpret_cast<float2*>(rec_ml)[idx] = make_float2(m, lt);
         }
       }
+#pragma unroll
+      for (int mt = 0; mt < M::kMTiles; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      m = kNoMax;
+      l = 0.f;
+      seg_start = x + 1;
+      if (x + 1 == chunk_end) {
+        ++chunk;
+        chunk_end += c;
+      }
+      if (x + 1 == seq_end && more) {
+        cursor_to(cc, x + 1, sc, context_lens, max_len);
+#pragma unroll
+        for (int ks = 0; ks < M::kKSteps; ++ks) qb[ks] = qn[ks];
+      }
     }
-    before += n;
-    ++s;
-    if (before >= b1 || s >= num_seqs) break;
   }
 }
 
 template <typename KVT, int D>
 static pkv_status launch_one(const DecodeMfmaArgs& a) {
-  hipLaunchKernelGGL((decode_mfma_kernel<KVT, D>), dim3(a.num_chunks * a.num_kv_heads),
+  const int waves = (a.num_chunks + a.chunks_per_wave - 1) / a.chunks_per_wave;
+  hipLaunchKernelGGL((decode_mfma_kernel<KVT, D>), dim3(waves * a.num_kv_heads),
                      dim3(kWave), 0, as_stream(a.stream), static_cast<uint16_t*>(a.out),
                      static_cast<const uint16_t*>(a.query),
                      static_cast<const typename KVT::storage*>(a.k_cache),
                      static_cast<const typename KVT::storage*>(a.v_cache), a.num_blocks,
                      a.block_tables, a.max_blocks, a.context_lens, a.num_seqs, a.max_len,
                      a.num_q_heads, a.num_kv_heads, a.num_q_heads / a.num_kv_heads,
-                     a.scale_log2, a.v_scale, a.num_chunks, a.fixed_chunk, a.rec_out,
-                     a.rec_ml);
+                     a.scale_log2, a.v_scale, a.num_chunks, a.fixed_chunk,
+                     a.chunks_per_wave, a.rec_out, a.rec_ml);
   return launch_status();
 }
 
