@@ -1,7 +1,9 @@
 """Benchmark of the paged-attention hot path on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
-                    [--no-mixed]
+                    [--no-mixed] [--no-longctx] [--no-mha]
+    python bench.py --copy-calibration     (a plain 1 GiB device copy, for
+                                            the HBM byte counters' scale)
 
 A step is one pass of the hot path over one batch: the Llama-3.1-8B-shaped
 decode layer (64 sequences, context 512..4096, 32 q / 8 kv heads, head_dim
@@ -11,12 +13,17 @@ in HBM before timing starts; two copies of the KV pool alternate between
 steps so that the 256 MB last-level cache cannot serve a re-read.
 
 Prints one JSON line (rank 0): whole-step throughput in algorithmic KV GB/s,
-KV tokens/s, the decode kernel's roofline fraction, the oracle's CPU rate on a
-bounded sample, and (unless --no-mixed) the mixed unified step with chunked
-prefill (MFMA utilisation of the prefill call).
+KV tokens/s, the decode call's roofline fraction, the oracle's CPU rate on a
+bounded sample, the mixed unified step with chunked prefill (MFMA
+utilisation of the prefill call), the fp8 long-context decode and the
+32-layer MHA decode step.  The roofline's "traffic" is the HBM bytes per
+decode call that rocprofv3's FETCH_SIZE and WRITE_SIZE counters measured
+(profiles/decode_llama3_8b_64seq_traffic.md), used only while the decode
+sources are the ones those counters were taken on.
 """
 
 import argparse
+import hashlib
 import json
 import multiprocessing as mp
 import os
@@ -55,6 +62,50 @@ def prefill_flops(step):
         c = int(comp[r])
         pairs += n * c + n * (n + 1) // 2
     return 4.0 * step.head_dim * step.num_q_heads * pairs, pairs
+
+
+# Sources whose kernels the decode call runs; the traffic counters in
+# profiles/ are used only while these hash to the value recorded with them.
+DECODE_SOURCES = ("paged_kv_cache_84_amd/csrc/decode.hip",
+                  "paged_kv_cache_84_amd/csrc/decode_mfma.hip",
+                  "paged_kv_cache_84_amd/csrc/decode_sched.h",
+                  "paged_kv_cache_84_amd/csrc/common.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_llama3_8b_64seq_traffic.md")
+
+
+def decode_source_hash():
+    h = hashlib.sha256()
+    for rel in DECODE_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per decode call from the committed counter summary (the
+    line starting 'traffic-json:'), or None if absent or taken on other
+    decode sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if line.startswith("traffic-json:"):
+                    rec = json.loads(line.split(":", 1)[1])
+                    if rec.get("decode_source_hash") == decode_source_hash():
+                        return rec
+    except (OSError, ValueError):
+        pass
+    return None
+
+
+def copy_calibration(nbytes=1 << 30, reps=5):
+    """A plain device-to-device copy of known size, for scaling the HBM
+    byte counters (run under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
 
 
 def time_region(fn, iters, stream):
@@ -212,16 +263,22 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mixed", action="store_true")
-    ap.add_argument("--longctx", action="store_true",
-                    help="also time the fp8 long-context decode (1.6 GB of KV)")
-    ap.add_argument("--mha", action="store_true",
-                    help="also time the 32-layer MHA decode step (128 GiB of KV)")
+    ap.add_argument("--no-longctx", action="store_true",
+                    help="skip the fp8 long-context decode (1.6 GB of KV)")
+    ap.add_argument("--no-mha", action="store_true",
+                    help="skip the 32-layer MHA decode step (128 GiB of KV)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter scale)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the paged-attention path here is "
               "built and measured on a single MI355X (no collectives); run with --gpus 1",
               file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        torch.cuda.set_device(0)
+        copy_calibration()
+        return
     import paged_kv_cache_84_amd as pk
     from synth import configs as C
     # The workload is built on the host; the CPU baseline runs before the GPU
@@ -264,11 +321,15 @@ def main():
                      "frac": round(gbs_decode / HBM_PEAK_GBS, 4), "traffic": None,
                      "launch_ms": round(r["ms_decode"], 4)},
     }
+    tr = measured_traffic()
+    if tr is not None:
+        line["roofline"]["traffic"] = tr["bytes_per_call"]
+        line["roofline"]["traffic_over_algorithmic"] = round(tr["bytes_per_call"] / r["bytes"], 3)
     if not args.no_mixed:
         line["mixed_step"] = bench_mixed(args, pk, C)
-    if args.longctx:
+    if not args.no_longctx:
         line["longctx_decode"] = bench_extra_decode(args, pk, C, "longctx")
-    if args.mha:
+    if not args.no_mha:
         line["mha_decode"] = bench_extra_decode(args, pk, C, "mha")
     if cpu is not None:
         line["cpu_baseline"] = cpu
