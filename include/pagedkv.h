@@ -160,14 +160,17 @@ pkv_status copy_blocks(void* const* k_caches, void* const* v_caches,
  * c stands for value(c) * k_scale (v_scale for V).  L == 0 gives zeros.
  *
  * Work split: the blocks of all sequences are laid end to end and cut into
- * equal chunks; one workgroup per (chunk, kv head) attends to its chunk.  A
+ * equal chunks; per kv head, a wave walks a run of consecutive chunks.  A
  * sequence that lies inside one chunk is written to `out` directly; one
  * that spans chunks leaves a (max, sum, weighted-value) partial per chunk in
  * `workspace`, and a second kernel merges them with a log-sum-exp rescale.
  * partition_tokens = 0 lets the library size the chunks from the actual
- * lengths (all chunks equal, enough of them to fill the GPU); otherwise each
- * chunk is exactly partition_tokens tokens (a positive multiple of 16) of the
- * laid-out blocks.  The workspace is caller-owned device memory of at least
+ * lengths (all chunks equal, one per wave, enough waves to fill the GPU);
+ * otherwise each chunk is exactly partition_tokens tokens (a positive
+ * multiple of 16) of the laid-out blocks and a wave may walk several.
+ * Results do not depend on the number of chunks a wave walks; they are
+ * bitwise reproducible for the same arguments.  The workspace is
+ * caller-owned device memory of at least
  * paged_attention_decode_workspace_size(...) bytes for the same arguments;
  * its contents need no initialisation and are scratch after the call.
  *
