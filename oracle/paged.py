@@ -164,6 +164,30 @@ def copy_blocks(k_caches, v_caches, block_mapping):
     return k_new, v_new
 
 
+def swap_blocks(src_k_caches, src_v_caches, dst_k_caches, dst_v_caches, block_mapping):
+    """Copy whole blocks from one cache pool into another, every layer, K and
+    V: pair (s, d) sets dst[d] = src[s].  This is the V0 engine's swap of a
+    request's KV blocks between GPU memory and CPU memory ([Anatomy] "抢占：
+    RECOMPUTE", the v0 SWAP mode and its --swap-space; [V0/V1] §2.1 "V0 引擎
+    循环", blocks_to_swap_in / blocks_to_swap_out next to blocks_to_copy), and
+    of today's KV offloading to CPU memory ([Overview] "KV 缓存管理与前缀缓存",
+    --kv-offloading-size).  Which pool lives where does not change the bytes.
+
+    Precondition (checked): destinations are distinct.  Returns new lists of
+    destination caches.
+    """
+    pairs = [(int(s), int(d)) for s, d in np.asarray(block_mapping).reshape(-1, 2)]
+    dsts = [d for _, d in pairs]
+    assert len(set(dsts)) == len(dsts), "swap destinations must be distinct"
+    k_new = [np.array(c, copy=True) for c in dst_k_caches]
+    v_new = [np.array(c, copy=True) for c in dst_v_caches]
+    for src, dst in pairs:
+        for layer in range(len(k_new)):
+            k_new[layer][dst] = src_k_caches[layer][src]
+            v_new[layer][dst] = src_v_caches[layer][src]
+    return k_new, v_new
+
+
 # --------------------------------------------------------------------------
 # Attention
 # --------------------------------------------------------------------------

@@ -134,6 +134,45 @@ def pin_copy_blocks():
         raise AssertionError(f"precondition not enforced for {bad}")
 
 
+def pin_swap_round_trip():
+    """Swap a sequence's blocks out to a second pool and back into other
+    blocks of the first: through its repointed table the sequence's logical
+    K/V bytes and its decode output are unchanged, the second pool's other
+    blocks are untouched, and a swap inside one pool is copy_blocks
+    ([Anatomy] "抢占：RECOMPUTE", v0 SWAP; [V0/V1] §2.1)."""
+    rng = np.random.default_rng(21)
+    nb, hkv, d, length = 12, 2, 8, 50
+    kc = f32(rng.standard_normal((nb, hkv, B, d)))
+    vc = f32(rng.standard_normal((nb, hkv, B, d)))
+    table = np.array([[3, 9, 0, 6]], dtype=np.int32)
+    q = f32(rng.standard_normal((1, 4, d)))
+    before = P.decode_attention(q, F.F32, kc, vc, F.F32, table,
+                                np.array([length], np.int32), 0.37)
+    host_k = [np.full((5, hkv, B, d), 7.0, dtype=np.float32)]
+    host_v = [np.full((5, hkv, B, d), -7.0, dtype=np.float32)]
+    out_pairs = np.array([[3, 4], [9, 0], [0, 2], [6, 1]])       # device -> host
+    hk, hv = P.swap_blocks([kc], [vc], host_k, host_v, out_pairs)
+    assert np.all(hk[0][3] == 7.0) and np.all(hv[0][3] == -7.0)   # untouched
+    # the device blocks are reused by someone else, then the sequence comes
+    # back into different blocks
+    kc_clobbered = np.array(kc, copy=True); kc_clobbered[[3, 9, 0, 6]] = np.nan
+    vc_clobbered = np.array(vc, copy=True); vc_clobbered[[3, 9, 0, 6]] = np.nan
+    in_pairs = np.array([[4, 11], [0, 1], [2, 5], [1, 8]])        # host -> device
+    (k2,), (v2,) = P.swap_blocks(hk, hv, [kc_clobbered], [vc_clobbered], in_pairs)
+    table2 = np.array([[11, 1, 5, 8]], dtype=np.int32)
+    after = P.decode_attention(q, F.F32, k2, v2, F.F32, table2,
+                               np.array([length], np.int32), 0.37)
+    assert np.array_equal(before, after)
+    for j in range(4):
+        assert np.array_equal(k2[table2[0, j]], kc[table[0, j]])
+        assert np.array_equal(v2[table2[0, j]], vc[table[0, j]])
+    # inside one pool, with disjoint pairs, a swap is a block copy
+    pairs = np.array([[1, 7], [4, 2]])
+    ks, vs = P.swap_blocks([kc], [vc], [kc], [vc], pairs)
+    kcp, vcp = P.copy_blocks([kc], [vc], pairs)
+    assert np.array_equal(ks[0], kcp[0]) and np.array_equal(vs[0], vcp[0])
+
+
 # ------------------------------------------------------- softmax closed forms
 
 def pin_hand_example():
@@ -532,7 +571,7 @@ def pin_budget_example():
 
 
 ALL_PINS = [
-    pin_table1, pin_fig2_slots, pin_fig2_write_canary, pin_copy_blocks,
+    pin_table1, pin_fig2_slots, pin_fig2_write_canary, pin_copy_blocks, pin_swap_round_trip,
     pin_hand_example, pin_single_token, pin_zero_query_mean, pin_constant_values,
     pin_gqa_mapping, pin_bruteforce_gather, pin_torch_sdpa, pin_permutation,
     pin_prefix_sharing, pin_split_lse, pin_prefill_vs_decode, pin_fig3_replay,

@@ -101,6 +101,16 @@ def _copy_only_keys(k_caches, v_caches, block_mapping):
     return k_new, v_new
 
 
+def _swap_source_index_from_destination(src_k, src_v, dst_k, dst_v, block_mapping):
+    k_new = [np.array(c, copy=True) for c in dst_k]
+    v_new = [np.array(c, copy=True) for c in dst_v]
+    for src, dst in np.asarray(block_mapping).reshape(-1, 2):
+        for layer in range(len(k_new)):
+            k_new[layer][dst] = src_k[layer][dst % len(src_k[layer])]
+            v_new[layer][dst] = src_v[layer][dst % len(src_v[layer])]
+    return k_new, v_new
+
+
 def _write_ignoring_skip(key, value, k_cache, v_cache, slots, src, dst, ks=1.0, vs=1.0):
     k_out = np.array(k_cache, copy=True)
     v_out = np.array(v_cache, copy=True)
@@ -124,6 +134,7 @@ MUTANTS = [
     ("e4m3_encode", F, _encode_ties_away),
     ("e4m3_encode", F, _encode_no_saturation),
     ("copy_blocks", P, _copy_only_keys),
+    ("swap_blocks", P, _swap_source_index_from_destination),
     ("reshape_and_cache", P, _write_ignoring_skip),
 ]
 
