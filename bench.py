@@ -1,7 +1,7 @@
 """Benchmark of the paged-attention hot path on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
-                    [--no-mixed] [--no-longctx] [--no-mha]
+                    [--no-mixed] [--no-longctx] [--no-mha] [--no-swap]
     python bench.py --copy-calibration     (a plain 1 GiB device copy, for
                                             the HBM byte counters' scale)
 
@@ -15,8 +15,9 @@ steps so that the 256 MB last-level cache cannot serve a re-read.
 Prints one JSON line (rank 0): whole-step throughput in algorithmic KV GB/s,
 KV tokens/s, the decode call's roofline fraction, the oracle's CPU rate on a
 bounded sample, the mixed unified step with chunked prefill (MFMA
-utilisation of the prefill call), the fp8 long-context decode and the
-32-layer MHA decode step.  The roofline's "traffic" is the HBM bytes per
+utilisation of the prefill call), the fp8 long-context decode, the
+32-layer MHA decode step and a device <-> host block swap of one long
+sequence.  The roofline's "traffic" is the HBM bytes per
 decode call that rocprofv3's FETCH_SIZE and WRITE_SIZE counters measured
 (profiles/decode_llama3_8b_64seq_traffic.md), used only while the decode
 sources are the ones those counters were taken on.
@@ -220,6 +221,60 @@ def bench_mixed(args, pk, C):
             "decode_gbs": round(decode_bytes(s) / (ms_decode * 1e-3) / 1e9, 1)}
 
 
+PCIE5_X16_GBS = 64.0   # host link of one MI355X, per direction
+
+
+def swap_workload(num_layers=32, hkv=32, d=128, seq_blocks=512, pool_blocks=600):
+    """One 8,192-token sequence of the Llama-2-7B-shaped 32-layer cache
+    (512 blocks of 128 KiB per layer and K/V, seeded scattered placement in
+    a 600-block device pool) with a pinned host pool for it and a second
+    device pool to bring it back into (a seeded scattered set of blocks)."""
+    from synth import rng as R
+    rs = R.structure_rng(3, 7)
+    dev_ids = rs.permutation(pool_blocks)[:seq_blocks]
+    back_ids = rs.permutation(pool_blocks)[:seq_blocks]
+    shape = (pool_blocks, hkv, 16, d)
+    dev_k = [R.normal(shape, R.BF16, 3, 200 + l, "cuda") for l in range(num_layers)]
+    dev_v = [R.normal(shape, R.BF16, 3, 300 + l, "cuda") for l in range(num_layers)]
+    host_k = [torch.empty((seq_blocks, hkv, 16, d), dtype=torch.bfloat16, pin_memory=True)
+              for _ in range(num_layers)]
+    host_v = [torch.empty_like(t, pin_memory=True) for t in host_k]
+    back_k = [torch.zeros(shape, dtype=torch.bfloat16, device="cuda") for _ in range(num_layers)]
+    back_v = [torch.zeros_like(t) for t in back_k]
+    slots = np.arange(seq_blocks)
+    out_pairs = torch.as_tensor(np.stack([dev_ids, slots], 1).astype(np.int64), device="cuda")
+    in_pairs = torch.as_tensor(np.stack([slots, back_ids], 1).astype(np.int64), device="cuda")
+    return {"dev_k": dev_k, "dev_v": dev_v, "host_k": host_k, "host_v": host_v,
+            "back_k": back_k, "back_v": back_v, "out_pairs": out_pairs, "in_pairs": in_pairs,
+            "bytes": 2 * num_layers * seq_blocks * hkv * 16 * d * 2}
+
+
+def bench_swap(args, pk):
+    """Swap one sequence out to pinned host memory and back in (one
+    swap_blocks call each way), GB/s against the host link's peak."""
+    w = swap_workload()
+    stream = torch.cuda.current_stream()
+    out = lambda i: pk.swap_blocks(w["dev_k"], w["dev_v"], w["host_k"], w["host_v"],
+                                   w["out_pairs"])
+    back = lambda i: pk.swap_blocks(w["host_k"], w["host_v"], w["back_k"], w["back_v"],
+                                    w["in_pairs"])
+    out(0)
+    back(0)
+    iters = 3
+    ms_out = time_region(out, iters, stream)
+    ms_in = time_region(back, iters, stream)
+    gb = w["bytes"] / 1e9
+    return {"workload": "swap one 8,192-token sequence of the Llama-2-7B-shaped 32-layer "
+                        "cache (512 blocks x 128 KiB per layer and K/V = 4 GiB) to pinned "
+                        "host memory and back into scattered device blocks",
+            "bytes_each_way": w["bytes"],
+            "out_ms": round(ms_out, 3), "out_gbs": round(gb / (ms_out * 1e-3), 1),
+            "in_ms": round(ms_in, 3), "in_gbs": round(gb / (ms_in * 1e-3), 1),
+            "link_peak_gbs": PCIE5_X16_GBS,
+            "out_frac": round(gb / (ms_out * 1e-3) / PCIE5_X16_GBS, 3),
+            "in_frac": round(gb / (ms_in * 1e-3) / PCIE5_X16_GBS, 3)}
+
+
 def bench_extra_decode(args, pk, C, which):
     """Optional legs: the fp8 long-context decode (64/8 heads, 6 x 131,072
     tokens, 512-token partitions) or the 32-layer MHA decode step (32 x 8,192
@@ -267,6 +322,8 @@ def main():
                     help="skip the fp8 long-context decode (1.6 GB of KV)")
     ap.add_argument("--no-mha", action="store_true",
                     help="skip the 32-layer MHA decode step (128 GiB of KV)")
+    ap.add_argument("--no-swap", action="store_true",
+                    help="skip the device <-> host block swap of one long sequence")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter scale)")
     args = ap.parse_args()
@@ -331,6 +388,8 @@ def main():
         line["longctx_decode"] = bench_extra_decode(args, pk, C, "longctx")
     if not args.no_mha:
         line["mha_decode"] = bench_extra_decode(args, pk, C, "mha")
+    if not args.no_swap:
+        line["swap_blocks"] = bench_swap(args, pk)
     if cpu is not None:
         line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)

@@ -149,6 +149,40 @@ pkv_status copy_blocks(void* const* k_caches, void* const* v_caches,
                        int64_t block_bytes, void* stream);
 
 /*
+ * swap_blocks -- copy whole blocks from one cache pool into another, every
+ * layer, K and V; one pool is device memory and the other host memory (the
+ * other way round to swap back), or both are device memory.
+ *
+ * The v0 engine could preempt a request by swapping its KV blocks out to CPU
+ * memory and back in later ("vLLM 引擎解剖", section "抢占：RECOMPUTE", the v0
+ * SWAP mode); the swaps travelled with each step as blocks_to_swap_out /
+ * blocks_to_swap_in next to blocks_to_copy ("v1/v0 区别", §2.1 "V0 引擎循环").
+ * Today's engine offloads KV blocks to CPU memory
+ * ("01. vLLM：从分页 KV 起家的通用推理引擎", section "KV 缓存管理与前缀缓存",
+ * --kv-offloading-size).
+ *
+ *   src_k_caches, src_v_caches  HOST arrays of num_layers pointers to the
+ *   dst_k_caches, dst_v_caches  source and destination pools, each
+ *                               [num_*_blocks][num_kv_heads][16][head_dim];
+ *                               device memory, or pinned host memory from
+ *                               hipHostMalloc (it is read and written through
+ *                               its device mapping)
+ *   block_mapping  int64 [num_pairs][2] = (src block, dst block), device or
+ *                  pinned host memory
+ *   block_bytes    bytes of one block of one layer's K (or V) pool; a
+ *                  positive multiple of 16
+ * For each pair and layer: dst_K[dst] = src_K[src], dst_V[dst] = src_V[src],
+ * as one kernel launch on `stream`.  A pair with an id outside its pool is
+ * skipped.  Precondition: destinations are distinct; if the two pools are
+ * the same memory, no destination is also a source.
+ */
+pkv_status swap_blocks(void* const* src_k_caches, void* const* src_v_caches,
+                       void* const* dst_k_caches, void* const* dst_v_caches,
+                       int32_t num_layers, const int64_t* block_mapping,
+                       int32_t num_pairs, int32_t num_src_blocks,
+                       int32_t num_dst_blocks, int64_t block_bytes, void* stream);
+
+/*
  * paged_attention_decode -- one query token per sequence attends to its whole
  * paged KV history; decode streams the entire cache once per step and is
  * bound by memory bandwidth ("vLLM 引擎解剖", section "预填充、解码与三个时延指标").

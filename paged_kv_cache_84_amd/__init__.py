@@ -25,4 +25,5 @@ from ._binding import (  # noqa: F401
     paged_attention_decode,
     paged_attention_prefill_chunk,
     reshape_and_cache,
+    swap_blocks,
 )

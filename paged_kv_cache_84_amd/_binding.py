@@ -39,6 +39,7 @@ _SIGNATURES = {
     "reshape_and_cache": (_I32, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
                                  _I32, _F, _F, _P]),
     "copy_blocks": (_I32, [_P, _P, _I32, _P, _I32, _I32, _I64, _P]),
+    "swap_blocks": (_I32, [_P, _P, _P, _P, _I32, _P, _I32, _I32, _I32, _I64, _P]),
     "paged_attention_decode_workspace_size": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32]),
     "paged_attention_decode_num_chunks": (_I32, [_I32, _I32, _I32, _I32, _I32]),
     "paged_attention_decode": (_I32, [_P, _P, _P, _P, _I32, _P, _I32, _P, _I32, _I32,
@@ -157,6 +158,46 @@ def copy_blocks(k_caches, v_caches, block_mapping):
                                pairs.shape[0], shape[0], block_bytes,
                                _stream(k_caches[0]))
     _check("copy_blocks", st)
+
+
+def _dev_or_pinned(t, what):
+    """Device tensor, or pinned host tensor (reachable through its device
+    mapping); contiguous."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what} must be a torch.Tensor")
+    if not (t.is_cuda or t.is_pinned()):
+        raise ValueError(f"{what} must be on the GPU or in pinned host memory")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    return t.data_ptr()
+
+
+def swap_blocks(src_k_caches, src_v_caches, dst_k_caches, dst_v_caches, block_mapping,
+                stream_device=None):
+    """dst[d] = src[s] for every (s, d) = block_mapping[i], every layer, K and
+    V; pools on the GPU or in pinned host memory (see the header)."""
+    n = len(src_k_caches)
+    assert n > 0 and len(src_v_caches) == n and len(dst_k_caches) == n and len(dst_v_caches) == n
+    s_shape, d_shape = src_k_caches[0].shape, dst_k_caches[0].shape
+    assert s_shape[1:] == d_shape[1:], "source and destination blocks differ in shape"
+    dtype = src_k_caches[0].dtype
+    for c in list(src_k_caches) + list(src_v_caches):
+        assert c.shape == s_shape and c.dtype == dtype
+        _dev_or_pinned(c, "source cache")
+    for c in list(dst_k_caches) + list(dst_v_caches):
+        assert c.shape == d_shape and c.dtype == dtype
+        _dev_or_pinned(c, "destination cache")
+    block_bytes = src_k_caches[0][0].numel() * src_k_caches[0].element_size()
+    arr = lambda ts: (ctypes.c_void_p * n)(*[c.data_ptr() for c in ts])
+    if block_mapping.dtype != torch.int64:
+        raise TypeError("block_mapping must be int64")
+    pairs = block_mapping.reshape(-1, 2)
+    dev = torch.device("cuda", torch.cuda.current_device()) if stream_device is None else stream_device
+    st = library().swap_blocks(arr(src_k_caches), arr(src_v_caches), arr(dst_k_caches),
+                               arr(dst_v_caches), n, _dev_or_pinned(block_mapping, "block_mapping"),
+                               pairs.shape[0], s_shape[0], d_shape[0], block_bytes,
+                               torch.cuda.current_stream(dev).cuda_stream)
+    _check("swap_blocks", st)
 
 
 def decode_num_chunks(num_seqs, num_q_heads, num_kv_heads, max_context_len,

@@ -144,6 +144,35 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(
   for (int64_t i = threadIdx.x; i < n; i += blockDim.x) d[i] = s[i];
 }
 
+// grid: (pair, layer in this launch, K or V).  Whole blocks between two
+// pools, either of which may be pinned host memory mapped into the device's
+// address space (the loads or the stores then cross the host link, so each
+// thread keeps four 16-byte loads in flight).
+__global__ __launch_bounds__(256) void swap_blocks_kernel(
+    LayerPtrs src, LayerPtrs dst, const int64_t* __restrict__ mapping,
+    int32_t num_src_blocks, int32_t num_dst_blocks, int64_t block_bytes) {
+  const int pair = blockIdx.x;
+  const int layer = blockIdx.y;
+  const int64_t s_blk = mapping[2 * pair];
+  const int64_t d_blk = mapping[2 * pair + 1];
+  if (s_blk < 0 || d_blk < 0 || s_blk >= num_src_blocks || d_blk >= num_dst_blocks) return;
+  const char* sb = static_cast<const char*>(blockIdx.z == 0 ? src.k[layer] : src.v[layer]);
+  char* db = static_cast<char*>(blockIdx.z == 0 ? dst.k[layer] : dst.v[layer]);
+  const u32x4* s = reinterpret_cast<const u32x4*>(sb + s_blk * block_bytes);
+  u32x4* d = reinterpret_cast<u32x4*>(db + d_blk * block_bytes);
+  const int64_t n = block_bytes / 16;
+  const int64_t stride = blockDim.x;
+  int64_t i = threadIdx.x;
+  for (; i + 3 * stride < n; i += 4 * stride) {
+    const u32x4 a = s[i], b = s[i + stride], c = s[i + 2 * stride], e = s[i + 3 * stride];
+    d[i] = a;
+    d[i + stride] = b;
+    d[i + 2 * stride] = c;
+    d[i + 3 * stride] = e;
+  }
+  for (; i < n; i += stride) d[i] = s[i];
+}
+
 }  // namespace pkv
 
 // ===================================================================== ABI
@@ -248,6 +277,44 @@ extern "C" pkv_status copy_blocks(void* const* k_caches, void* const* v_caches,
     hipLaunchKernelGGL(copy_blocks_kernel, dim3(num_pairs, n, 2), dim3(256), 0,
                        as_stream(stream), ptrs, block_mapping, num_blocks,
                        block_bytes);
+    const pkv_status st = launch_status();
+    if (st != PKV_OK) return st;
+  }
+  return PKV_OK;
+}
+
+extern "C" pkv_status swap_blocks(void* const* src_k_caches, void* const* src_v_caches,
+                                  void* const* dst_k_caches, void* const* dst_v_caches,
+                                  int32_t num_layers, const int64_t* block_mapping,
+                                  int32_t num_pairs, int32_t num_src_blocks,
+                                  int32_t num_dst_blocks, int64_t block_bytes, void* stream) {
+  if (num_layers < 0 || num_pairs < 0 || num_src_blocks < 0 || num_dst_blocks < 0 ||
+      block_bytes <= 0 || block_bytes % 16 != 0)
+    return PKV_ERR_SHAPE;
+  if (num_layers == 0 || num_pairs == 0) return PKV_OK;
+  if (!src_k_caches || !src_v_caches || !dst_k_caches || !dst_v_caches || !block_mapping)
+    return PKV_ERR_NULL;
+  if (!aligned(block_mapping, 8)) return PKV_ERR_ALIGN;
+  for (int l = 0; l < num_layers; ++l) {
+    if (!src_k_caches[l] || !src_v_caches[l] || !dst_k_caches[l] || !dst_v_caches[l])
+      return PKV_ERR_NULL;
+    if (!aligned(src_k_caches[l], 16) || !aligned(src_v_caches[l], 16) ||
+        !aligned(dst_k_caches[l], 16) || !aligned(dst_v_caches[l], 16))
+      return PKV_ERR_ALIGN;
+  }
+  for (int first = 0; first < num_layers; first += kMaxLayersPerLaunch) {
+    const int n = num_layers - first < kMaxLayersPerLaunch ? num_layers - first
+                                                           : kMaxLayersPerLaunch;
+    LayerPtrs src = {}, dst = {};
+    for (int i = 0; i < n; ++i) {
+      src.k[i] = src_k_caches[first + i];
+      src.v[i] = src_v_caches[first + i];
+      dst.k[i] = dst_k_caches[first + i];
+      dst.v[i] = dst_v_caches[first + i];
+    }
+    hipLaunchKernelGGL(swap_blocks_kernel, dim3(num_pairs, n, 2), dim3(256), 0,
+                       as_stream(stream), src, dst, block_mapping, num_src_blocks,
+                       num_dst_blocks, block_bytes);
     const pkv_status st = launch_status();
     if (st != PKV_OK) return st;
   }

@@ -96,6 +96,22 @@ def test_copy_blocks_errors(lib):
     assert f(nul, arr, 1, 0x10000, 2, 10, 4096, None) == NULL
 
 
+def test_swap_blocks_errors(lib):
+    f = lib.swap_blocks
+    arr = (ctypes.c_void_p * 1)(0x10000)
+    assert f(arr, arr, arr, arr, 1, 0x10000, 0, 10, 10, 4096, None) == OK
+    assert f(arr, arr, arr, arr, 0, 0x10000, 2, 10, 10, 4096, None) == OK
+    assert f(arr, arr, arr, arr, 1, 0x10000, 2, 10, 10, 4095, None) == SHAPE
+    assert f(arr, arr, arr, arr, 1, 0x10000, 2, -1, 10, 4096, None) == SHAPE
+    assert f(arr, arr, None, arr, 1, 0x10000, 2, 10, 10, 4096, None) == NULL
+    assert f(arr, arr, arr, arr, 1, None, 2, 10, 10, 4096, None) == NULL
+    assert f(arr, arr, arr, arr, 1, 0x10004, 2, 10, 10, 4096, None) == ALIGN
+    bad = (ctypes.c_void_p * 1)(0x10008)
+    assert f(arr, arr, bad, arr, 1, 0x10000, 2, 10, 10, 4096, None) == ALIGN
+    nul = (ctypes.c_void_p * 1)(None)
+    assert f(arr, nul, arr, arr, 1, 0x10000, 2, 10, 10, 4096, None) == NULL
+
+
 def _decode(lib, **k):
     p = 0x100000
     a = dict(out=p, q=p, kc=p, vc=p, nb=100, bt=p, maxb=64, lens=p, s=4, maxlen=1000,
