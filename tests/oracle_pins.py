@@ -465,6 +465,29 @@ def pin_recompute():
                           _contiguous_kv(kc2, seqs2["X"].table, 40, 0))
 
 
+def pin_spec_verify():
+    """Verifying k draft tokens in one pass: a chunk of 1 + k query rows at
+    positions c .. c + k, each attending causally, gives exactly the outputs
+    of k + 1 separate decodes with context lengths c + 1 .. c + k + 1 over the
+    same cache ("01. vLLM：从分页 KV 起家的通用推理引擎", section "调度器：统一的
+    token 预算" and section "投机解码": drafts are verified by the target model
+    in one step; V1 EngineCore architecture page, section "统一 token 调度":
+    speculative candidates advance a request's progress by several tokens)."""
+    rng = np.random.default_rng(31)
+    c, k, d, hq, hkv = 37, 4, 8, 4, 2
+    q, kc, vc, tables = _random_case(rng, d, hq, hkv, [c + k + 1], 12)
+    rows = f32(rng.standard_normal((k + 1, hq, d)))
+    chunk = P.prefill_attention(rows, F.F32, kc, vc, F.F32, tables,
+                                np.array([0, k + 1], np.int32), np.array([c], np.int32), 0.3)
+    singles = P.decode_attention(rows, F.F32, kc, vc, F.F32,
+                                 np.repeat(tables, k + 1, axis=0),
+                                 np.arange(c + 1, c + k + 2, dtype=np.int32), 0.3)
+    assert np.array_equal(chunk, singles)
+    # and row i does not see the drafts after it
+    assert not np.allclose(singles[0], P.decode_attention(
+        rows[:1], F.F32, kc, vc, F.F32, tables, np.array([c + k + 1], np.int32), 0.3)[0])
+
+
 def pin_poison():
     """NaN in unused slots of the last block and in free blocks never reaches
     an output."""
@@ -575,7 +598,7 @@ ALL_PINS = [
     pin_hand_example, pin_single_token, pin_zero_query_mean, pin_constant_values,
     pin_gqa_mapping, pin_bruteforce_gather, pin_torch_sdpa, pin_permutation,
     pin_prefix_sharing, pin_split_lse, pin_prefill_vs_decode, pin_fig3_replay,
-    pin_recompute, pin_poison, pin_fp8_codec, pin_fp8_vs_torch, pin_bf16_decode,
+    pin_recompute, pin_spec_verify, pin_poison, pin_fp8_codec, pin_fp8_vs_torch, pin_bf16_decode,
     pin_budget_example,
 ]
 
