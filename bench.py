@@ -207,6 +207,11 @@ def bench_mixed(args, pk, C):
     ms_step = time_region(lambda i: ds.run(), iters, stream)
     ms_prefill = time_region(lambda i: ds.prefill(0), iters, stream)
     ms_decode = time_region(lambda i: ds.decode(0), iters, stream)
+    # the same step with one unified attention launch for all requests
+    for _ in range(2):
+        ds.run_varlen()
+    ms_step_varlen = time_region(lambda i: ds.run_varlen(), iters, stream)
+    ms_varlen = time_region(lambda i: ds.varlen(0), iters, stream)
     flops, pairs = prefill_flops(s)
     tflops = flops / (ms_prefill * 1e-3) / 1e12
     return {"workload": "mixed unified step: 64 x 100-token chunks on a 125-block "
@@ -218,7 +223,10 @@ def bench_mixed(args, pk, C):
             "prefill_mfma_frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
             "prefill_pairs": pairs,
             "decode_ms": round(ms_decode, 4),
-            "decode_gbs": round(decode_bytes(s) / (ms_decode * 1e-3) / 1e9, 1)}
+            "decode_gbs": round(decode_bytes(s) / (ms_decode * 1e-3) / 1e9, 1),
+            "unified": {"attention_ms": round(ms_varlen, 4),
+                        "two_launch_attention_ms": round(ms_prefill + ms_decode, 4),
+                        "ms_per_step": round(ms_step_varlen, 4)}}
 
 
 PCIE5_X16_GBS = 64.0   # host link of one MI355X, per direction

@@ -285,6 +285,52 @@ pkv_status paged_attention_prefill_chunk(void* out, const void* query,
                                          float k_scale, float v_scale,
                                          void* stream);
 
+/*
+ * paged_attention_varlen -- the attention of one whole engine step in one
+ * launch: every request's query rows, whatever their number -- one for a
+ * decode, 1 + k to verify k speculative drafts, many for a prompt chunk.
+ *
+ * The unified scheduler has no prefill or decode phase: a request only has
+ * the tokens computed so far and the tokens to reach (input + generated +
+ * drafts), and a step advances each by some tokens
+ * ("01. vLLM：从分页 KV 起家的通用推理引擎", section "调度器：统一的 token 预算";
+ * V1 EngineCore architecture page, section "统一 token 调度"); drafts are
+ * verified by the target model in one step (section "投机解码").
+ *
+ * Semantics are those of paged_attention_prefill_chunk over all requests:
+ * row i of request r, at position p = num_computed_tokens[r] + i, attends to
+ * positions 0 .. p through block_tables[r].  A request with at most 16 query
+ * rows (tokens x group) is streamed by one wave per (request, kv head, run of
+ * 64 blocks); longer requests run as chunked-prefill tiles; both kinds share
+ * one kernel and run side by side.  A second, small kernel on the same stream
+ * merges the runs of requests longer than 64 blocks (log-sum-exp rule).
+ *
+ *   out, query, query_start_loc, num_computed_tokens, block_tables: as for
+ *                   paged_attention_prefill_chunk, over all num_reqs requests
+ *   max_seq_len     bound on num_computed_tokens[r] + (query rows of r)
+ *   workspace       device memory of at least
+ *                   paged_attention_varlen_workspace_size(...) bytes for the
+ *                   same num_reqs, num_kv_heads, head_dim, max_seq_len; it
+ *                   holds the per-run partial results (no initial contents
+ *                   needed).  Calls that share a workspace must not overlap
+ *                   in time.
+ * Supported: head_dim 128, (q, kv) = (BF16, BF16), group 1, 2, 4 or 8,
+ * softmax_scale > 0.  Accumulation is fp32; the output is bf16.
+ */
+size_t paged_attention_varlen_workspace_size(int32_t num_reqs, int32_t num_kv_heads,
+                                             int32_t head_dim, int32_t max_seq_len);
+
+pkv_status paged_attention_varlen(void* out, const void* query, const void* k_cache,
+                                  const void* v_cache, int32_t num_blocks,
+                                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t* query_start_loc,
+                                  const int32_t* num_computed_tokens, int32_t num_reqs,
+                                  int32_t num_q_tokens, int32_t max_seq_len,
+                                  int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, float softmax_scale, pkv_dtype q_dtype,
+                                  pkv_dtype kv_dtype, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -22,8 +22,10 @@ from ._binding import (  # noqa: F401
     kv_bytes_per_token,
     library,
     library_path,
+    varlen_workspace_size,
     paged_attention_decode,
     paged_attention_prefill_chunk,
+    paged_attention_varlen,
     reshape_and_cache,
     swap_blocks,
 )

@@ -45,6 +45,9 @@ _SIGNATURES = {
     "paged_attention_decode": (_I32, [_P, _P, _P, _P, _I32, _P, _I32, _P, _I32, _I32,
                                       _I32, _I32, _I32, _F, _I32, _I32, _F, _F, _I32,
                                       _P, _SZ, _P]),
+    "paged_attention_varlen_workspace_size": (_SZ, [_I32, _I32, _I32, _I32]),
+    "paged_attention_varlen": (_I32, [_P, _P, _P, _P, _I32, _P, _I32, _P, _P, _I32, _I32,
+                                      _I32, _I32, _I32, _I32, _F, _I32, _I32, _P, _SZ, _P]),
     "paged_attention_prefill_chunk": (_I32, [_P, _P, _P, _P, _I32, _P, _I32, _P, _P,
                                              _I32, _I32, _I32, _I32, _I32, _I32, _F,
                                              _I32, _I32, _F, _F, _P]),
@@ -258,4 +261,37 @@ def paged_attention_prefill_chunk(query, k_cache, v_cache, block_tables,
         _dtype_code(query, "query"), _dtype_code(k_cache, "k_cache"), float(k_scale),
         float(v_scale), _stream(query))
     _check("paged_attention_prefill_chunk", st)
+    return out
+
+
+def varlen_workspace_size(num_reqs, num_kv_heads, head_dim, max_seq_len):
+    return int(library().paged_attention_varlen_workspace_size(num_reqs, num_kv_heads,
+                                                               head_dim, max_seq_len))
+
+
+def paged_attention_varlen(query, k_cache, v_cache, block_tables, query_start_loc,
+                           num_computed_tokens, max_seq_len, softmax_scale, out=None,
+                           workspace=None):
+    """out [T][Hq][D] = causal attention of every request's rows, one launch
+    (see the header).  `workspace`: device bytes for the per-run partials,
+    any contents; allocated here when not given."""
+    t, hq, d = query.shape
+    hkv = k_cache.shape[1]
+    r = num_computed_tokens.shape[0]
+    if out is None:
+        out = torch.empty_like(query)
+    need = varlen_workspace_size(r, hkv, d, max_seq_len)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=query.device)
+    assert query_start_loc.shape[0] == r + 1 and block_tables.shape[0] >= r
+    st = library().paged_attention_varlen(
+        _dev(out, "out", query.dtype), _dev(query, "query"), _dev(k_cache, "k_cache"),
+        _dev(v_cache, "v_cache"), k_cache.shape[0],
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(query_start_loc, "query_start_loc", torch.int32),
+        _dev(num_computed_tokens, "num_computed_tokens", torch.int32), r, t,
+        int(max_seq_len), hq, hkv, d, float(softmax_scale), _dtype_code(query, "query"),
+        _dtype_code(k_cache, "k_cache"), _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(query))
+    _check("paged_attention_varlen", st)
     return out

@@ -54,6 +54,7 @@ class DeviceStep:
         self.slots = torch.empty(step.num_tokens, dtype=torch.int64, device=dev)
         self.out = [torch.empty_like(q) for q in self.q]
         self.partition_tokens = partition_tokens
+        self.varlen_ws = None
         if self.num_decode > 0:
             hq, hkv, d = step.num_q_heads, step.num_kv_heads, step.head_dim
             need = B.decode_workspace_size(self.num_decode, hq, hkv, d,
@@ -97,6 +98,31 @@ class DeviceStep:
             self.dec_tables, self.dec_lens, self.max_context_len, s.softmax_scale,
             s.k_scale, s.v_scale, self.partition_tokens, out=self.out[layer][t:],
             workspace=self.workspace)
+
+    def varlen(self, layer):
+        """Attention of every request of the step (chunks and decodes) in one
+        launch, written to the same output rows as prefill() + decode()."""
+        s = self.step
+        if self.varlen_ws is None:
+            qsl = s.query_start_loc
+            self.varlen_qsl = _i32(qsl, self.device)
+            self.varlen_max_seq = int(np.max(s.num_computed + np.diff(qsl)))
+            need = B.varlen_workspace_size(s.num_reqs, s.num_kv_heads, s.head_dim,
+                                           self.varlen_max_seq)
+            self.varlen_ws = torch.empty(max(need, 16), dtype=torch.uint8, device=self.device)
+        B.paged_attention_varlen(self.q[layer], self.k_caches[layer], self.v_caches[layer],
+                                 self.block_tables, self.varlen_qsl, self.num_computed,
+                                 self.varlen_max_seq, s.softmax_scale, out=self.out[layer],
+                                 workspace=self.varlen_ws)
+
+    def run_varlen(self):
+        """The whole step with the unified attention launch."""
+        self.copy()
+        self.slot_mapping()
+        for layer in range(len(self.k_caches)):
+            self.write(layer)
+            self.varlen(layer)
+        return self.out
 
     def run(self):
         """The whole step: copies, slots, then per layer write and attend."""

@@ -171,3 +171,39 @@ def test_prefill_errors(lib):
     assert call(a14=80) == UNSUP
     assert call(a16=F32) == UNSUP
     assert call(a4=0) == SHAPE
+
+
+def test_varlen_errors(lib):
+    f = lib.paged_attention_varlen
+    p = 0x100000
+    need = lib.paged_attention_varlen_workspace_size(3, 8, 128, 2000)
+    # 2 runs of 64 blocks per request: per (request, kv head, run) 16 columns of
+    # 128 fp32 values and 16 (max, sum) pairs
+    assert need == 3 * 8 * 2 * 16 * 128 * 4 + 3 * 8 * 2 * 16 * 2 * 4
+    assert lib.paged_attention_varlen_workspace_size(3, 8, 96, 2000) == 0
+    assert lib.paged_attention_varlen_workspace_size(1, 8, 128, 0) == 8 * 16 * 130 * 4
+    base = [p, p, p, p, 100, p, 125, p, p, 3, 50, 2000, 32, 8, 128, 0.088, BF16, BF16,
+            p, need, None]
+
+    def call(**k):
+        a = list(base)
+        for i, v in k.items():
+            a[int(i[1:])] = v
+        return f(*a)
+
+    assert call(a9=0) == OK
+    assert call(a10=0) == OK
+    assert call(a0=None) == NULL
+    assert call(a1=p + 4) == ALIGN
+    assert call(a12=30) == SHAPE                 # not a multiple of hkv
+    assert call(a12=72) == UNSUP                 # group 9
+    assert call(a14=96) == UNSUP
+    assert call(a17=FP8) == UNSUP
+    assert call(a15=0.0) == UNSUP
+    assert call(a15=-0.5) == UNSUP
+    assert call(a6=124) == SHAPE                 # 1,984 tokens < max_seq_len
+    assert call(a4=0) == SHAPE
+    assert call(a11=-1) == SHAPE
+    assert call(a18=None) == WS
+    assert call(a19=need - 1) == WS
+    assert call(a18=p + 8) == ALIGN
