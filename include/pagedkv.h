@@ -302,8 +302,10 @@ pkv_status paged_attention_prefill_chunk(void* out, const void* query,
  * positions 0 .. p through block_tables[r].  A request with at most 16 query
  * rows (tokens x group) is streamed by one wave per (request, kv head, run of
  * 64 blocks); longer requests run as chunked-prefill tiles; both kinds share
- * one kernel and run side by side.  A second, small kernel on the same stream
- * merges the runs of requests longer than 64 blocks (log-sum-exp rule).
+ * one kernel and run side by side, handed out through per-XCD work queues.
+ * Three kernels go onto the stream: a one-workgroup reset of the queue
+ * counters, the attention kernel, and a small merge of the runs of requests
+ * longer than 64 blocks (log-sum-exp rule).
  *
  *   out, query, query_start_loc, num_computed_tokens, block_tables: as for
  *                   paged_attention_prefill_chunk, over all num_reqs requests
@@ -311,9 +313,9 @@ pkv_status paged_attention_prefill_chunk(void* out, const void* query,
  *   workspace       device memory of at least
  *                   paged_attention_varlen_workspace_size(...) bytes for the
  *                   same num_reqs, num_kv_heads, head_dim, max_seq_len; it
- *                   holds the per-run partial results (no initial contents
- *                   needed).  Calls that share a workspace must not overlap
- *                   in time.
+ *                   holds the queue counters and the per-run partial results
+ *                   (no initial contents needed).  Calls that share a
+ *                   workspace must not overlap in time.
  * Supported: head_dim 128, (q, kv) = (BF16, BF16), group 1, 2, 4 or 8,
  * softmax_scale > 0.  Accumulation is fp32; the output is bf16.
  */

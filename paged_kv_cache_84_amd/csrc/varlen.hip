@@ -257,13 +257,20 @@ PKV_DEVICE void narrow_unit(char* vl, int r, int kvh, int run, int runs_per_req,
 
 }  // namespace vl
 
-// Grid: wide workgroups (prefill tiles) and narrow workgroups (4 waves, one
-// narrow unit each), alternating in runs of eight while both last, then the
-// rest.  Both kinds number only the work that exists (a scan over the
-// requests maps a workgroup to its piece), so the alternation pairs real
-// work of both kinds; the grid is an upper bound and surplus workgroups exit.  Workgroup b runs on XCD b % 8, so in runs of eight the wide tiles
-// keep their kv-head-per-XCD order (index i of a kind sits on XCD i % 8) and
-// both kinds spread over every XCD.
+// Work queues.  Workgroup b runs on XCD b % 8, and the hardware spreads the
+// workgroups of an XCD over its compute units in a fixed rotation, so a
+// static pattern of kinds in the grid (wide, narrow, wide, ...) would pin each
+// kind to a fixed subset of the compute units.  Instead each XCD has a
+// ticket counter: a workgroup draws the next ticket of its XCD and runs the
+// piece of work that ticket names, whatever compute unit it landed on.
+// Queue x holds the wide tiles and narrow workgroups whose index is x mod 8
+// (wide tiles are numbered kv head fastest, so with a multiple of eight kv
+// heads one XCD keeps the tiles of the same kv heads and its L2 their shared
+// prefix), alternating one wide, one narrow while both last, then the rest.
+// The grid gives every XCD as many workgroups as its queue holds at most;
+// surplus workgroups draw a ticket past the end and exit.
+constexpr int kQueues = 8;
+
 __global__ __launch_bounds__(256, 2) void varlen_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
     const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
@@ -271,19 +278,25 @@ __global__ __launch_bounds__(256, 2) void varlen_kernel(
     const int32_t* __restrict__ query_start_loc, const int32_t* __restrict__ num_computed,
     int32_t num_reqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t group,
     float scale_log2, int32_t wide_wgs, int32_t narrow_wgs, int32_t runs_per_req,
-    float* __restrict__ part_o, float2* __restrict__ part_ml) {
+    int32_t* __restrict__ tickets, float* __restrict__ part_o, float2* __restrict__ part_ml) {
   __shared__ pf::Stage stage0, stage1;
-  const int g = blockIdx.x / 8, x = blockIdx.x % 8;
-  const int wide_groups = (wide_wgs + 7) / 8, narrow_groups = (narrow_wgs + 7) / 8;
-  const int paired = min(wide_groups, narrow_groups);
+  __shared__ int ticket_lds;
+  const int x = blockIdx.x % kQueues;
+  if (threadIdx.x == 0)
+    ticket_lds = __hip_atomic_fetch_add(tickets + x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const int k = ticket_lds;
+  const int wide_x = (wide_wgs + kQueues - 1 - x) / kQueues;     // queue x's share of each kind
+  const int narrow_x = (narrow_wgs + kQueues - 1 - x) / kQueues;
+  const int paired = min(wide_x, narrow_x);
   bool wide;
   int idx;
-  if (g < 2 * paired) {
-    wide = (g & 1) == 0;
-    idx = (g >> 1) * 8 + x;
+  if (k < 2 * paired) {
+    wide = (k & 1) == 0;
+    idx = (k >> 1) * kQueues + x;
   } else {
-    wide = wide_groups > narrow_groups;
-    idx = (g - paired) * 8 + x;
+    wide = wide_x > narrow_x;
+    idx = (k - paired) * kQueues + x;
   }
   if (wide) {
     if (idx >= wide_wgs) return;
@@ -293,13 +306,14 @@ __global__ __launch_bounds__(256, 2) void varlen_kernel(
     return;
   }
   if (idx >= narrow_wgs) return;
-  // narrow: workgroup idx serves kv head idx % num_kv_heads (so a kv head
-  // stays on the XCDs that run its prefill tiles), its wave w item
-  // (idx / num_kv_heads) * 4 + w; the items are the (narrow request, run)
-  // pairs in request order -- only requests with work get items
+  // narrow: wave w of workgroup idx takes unit idx * 4 + w; a unit is (item,
+  // kv head) with the kv head fastest, so the waves of a workgroup usually
+  // share an item and take equally long; the items are the (narrow request,
+  // run) pairs in request order -- only requests with work get items
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);
-  const int kvh = idx % num_kv_heads;
-  const int64_t item = int64_t(idx / num_kv_heads) * 4 + wave;
+  const int64_t u = int64_t(idx) * 4 + wave;
+  const int kvh = int(u % num_kv_heads);
+  const int64_t item = u / num_kv_heads;
   int r = -1, run = 0;
   {
     const int lane = lane_id();
@@ -331,6 +345,11 @@ __global__ __launch_bounds__(256, 2) void varlen_kernel(
   vl::narrow_unit(lds, r, kvh, run, runs_per_req, out, query, k_cache, v_cache, num_blocks,
                   block_tables, max_blocks, query_start_loc, num_computed, num_q_heads,
                   num_kv_heads, group, scale_log2, vl::Workspace{part_o, part_ml});
+}
+
+// Clears the ticket counters before a launch.
+__global__ void varlen_reset_kernel(int32_t* __restrict__ tickets) {
+  if (threadIdx.x < kQueues) tickets[threadIdx.x] = 0;
 }
 
 // Merge of the narrow requests that span several runs: one workgroup per
@@ -381,7 +400,7 @@ static size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
 struct VarlenPlan {
   int32_t runs_per_req;
-  size_t o_bytes, ml_bytes;
+  size_t ticket_bytes, o_bytes, ml_bytes;
 };
 
 static bool varlen_plan(int32_t num_reqs, int32_t num_kv_heads, int32_t head_dim,
@@ -391,6 +410,7 @@ static bool varlen_plan(int32_t num_reqs, int32_t num_kv_heads, int32_t head_dim
   p.runs_per_req = std::max(1, vl::runs_of(nblk));
   const size_t units = size_t(num_reqs) * num_kv_heads;
   const size_t recs = units * p.runs_per_req;
+  p.ticket_bytes = 256;
   p.o_bytes = align256(recs * vl::kNarrowRows * head_dim * sizeof(float));
   p.ml_bytes = align256(recs * vl::kNarrowRows * 2 * sizeof(float));
   return true;
@@ -406,7 +426,7 @@ extern "C" size_t paged_attention_varlen_workspace_size(int32_t num_reqs,
                                                         int32_t max_seq_len) {
   VarlenPlan p;
   if (!varlen_plan(num_reqs, num_kv_heads, head_dim, max_seq_len, p)) return 0;
-  return p.o_bytes + p.ml_bytes;
+  return p.ticket_bytes + p.o_bytes + p.ml_bytes;
 }
 
 extern "C" pkv_status paged_attention_varlen(
@@ -437,24 +457,27 @@ extern "C" pkv_status paged_attention_varlen(
     return PKV_ERR_ALIGN;
   VarlenPlan p;
   if (!varlen_plan(num_reqs, num_kv_heads, head_dim, max_seq_len, p)) return PKV_ERR_SHAPE;
-  if (!workspace || workspace_bytes < p.o_bytes + p.ml_bytes)
+  if (!workspace || workspace_bytes < p.ticket_bytes + p.o_bytes + p.ml_bytes)
     return PKV_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return PKV_ERR_ALIGN;
   const int tokens_per_wg = pf::kRows / group;
   const int64_t wide = ((int64_t(num_q_tokens) + tokens_per_wg - 1) / tokens_per_wg + num_reqs) *
                        num_kv_heads;
-  const int64_t narrow = (int64_t(num_reqs) * p.runs_per_req + 3) / 4 * num_kv_heads;
-  const int64_t grid = ((wide + 7) / 8 + (narrow + 7) / 8) * 8;
+  const int64_t narrow = (int64_t(num_reqs) * p.runs_per_req * num_kv_heads + 3) / 4;
+  const int64_t grid = ((wide + kQueues - 1) / kQueues + (narrow + kQueues - 1) / kQueues) * kQueues;
   if (grid > 0x7fffffff || int64_t(num_reqs) * num_kv_heads > 0x7fffffff) return PKV_ERR_SHAPE;
-  float* part_o = reinterpret_cast<float*>(workspace);
-  float2* part_ml = reinterpret_cast<float2*>(static_cast<char*>(workspace) + p.o_bytes);
+  char* ws = static_cast<char*>(workspace);
+  int32_t* tickets = reinterpret_cast<int32_t*>(ws);
+  float* part_o = reinterpret_cast<float*>(ws + p.ticket_bytes);
+  float2* part_ml = reinterpret_cast<float2*>(ws + p.ticket_bytes + p.o_bytes);
+  hipLaunchKernelGGL(varlen_reset_kernel, dim3(1), dim3(64), 0, as_stream(stream), tickets);
   hipLaunchKernelGGL(varlen_kernel, dim3(uint32_t(grid)), dim3(256), 0, as_stream(stream),
                      static_cast<uint16_t*>(out), static_cast<const uint16_t*>(query),
                      static_cast<const uint16_t*>(k_cache),
                      static_cast<const uint16_t*>(v_cache), num_blocks, block_tables,
                      max_blocks_per_seq, query_start_loc, num_computed_tokens, num_reqs,
                      num_q_heads, num_kv_heads, group, softmax_scale * pf::kLog2e,
-                     int32_t(wide), int32_t(narrow), p.runs_per_req, part_o, part_ml);
+                     int32_t(wide), int32_t(narrow), p.runs_per_req, tickets, part_o, part_ml);
   if (p.runs_per_req > 1)
     hipLaunchKernelGGL(varlen_merge_kernel, dim3(uint32_t(num_reqs * num_kv_heads)), dim3(256),
                        0, as_stream(stream), static_cast<uint16_t*>(out), query_start_loc,
