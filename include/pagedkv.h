@@ -303,24 +303,26 @@ pkv_status paged_attention_prefill_chunk(void* out, const void* query,
  * rows (tokens x group) is streamed by one wave per (request, kv head, run of
  * 64 blocks); longer requests run as chunked-prefill tiles; both kinds share
  * one kernel and run side by side, handed out through per-XCD work queues.
- * Three kernels go onto the stream: a one-workgroup reset of the queue
- * counters, the attention kernel, and a small merge of the runs of requests
- * longer than 64 blocks (log-sum-exp rule).
+ * Three kernels go onto the stream: a one-workgroup plan (clears the queue
+ * counters, lists the tiles and runs), the attention kernel, and a small
+ * merge of the runs of requests longer than 64 blocks (log-sum-exp rule).
  *
  *   out, query, query_start_loc, num_computed_tokens, block_tables: as for
  *                   paged_attention_prefill_chunk, over all num_reqs requests
  *   max_seq_len     bound on num_computed_tokens[r] + (query rows of r)
  *   workspace       device memory of at least
  *                   paged_attention_varlen_workspace_size(...) bytes for the
- *                   same num_reqs, num_kv_heads, head_dim, max_seq_len; it
- *                   holds the queue counters and the per-run partial results
- *                   (no initial contents needed).  Calls that share a
- *                   workspace must not overlap in time.
+ *                   same num_reqs, num_q_tokens, num_kv_heads, head_dim,
+ *                   max_seq_len (0 if those are unsupported); it holds the
+ *                   plan and the per-run partial results (no initial
+ *                   contents needed).  Calls that share a workspace must not
+ *                   overlap in time.
  * Supported: head_dim 128, (q, kv) = (BF16, BF16), group 1, 2, 4 or 8,
  * softmax_scale > 0.  Accumulation is fp32; the output is bf16.
  */
-size_t paged_attention_varlen_workspace_size(int32_t num_reqs, int32_t num_kv_heads,
-                                             int32_t head_dim, int32_t max_seq_len);
+size_t paged_attention_varlen_workspace_size(int32_t num_reqs, int32_t num_q_tokens,
+                                             int32_t num_kv_heads, int32_t head_dim,
+                                             int32_t max_seq_len);
 
 pkv_status paged_attention_varlen(void* out, const void* query, const void* k_cache,
                                   const void* v_cache, int32_t num_blocks,

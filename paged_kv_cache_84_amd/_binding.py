@@ -45,7 +45,7 @@ _SIGNATURES = {
     "paged_attention_decode": (_I32, [_P, _P, _P, _P, _I32, _P, _I32, _P, _I32, _I32,
                                       _I32, _I32, _I32, _F, _I32, _I32, _F, _F, _I32,
                                       _P, _SZ, _P]),
-    "paged_attention_varlen_workspace_size": (_SZ, [_I32, _I32, _I32, _I32]),
+    "paged_attention_varlen_workspace_size": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
     "paged_attention_varlen": (_I32, [_P, _P, _P, _P, _I32, _P, _I32, _P, _P, _I32, _I32,
                                       _I32, _I32, _I32, _I32, _F, _I32, _I32, _P, _SZ, _P]),
     "paged_attention_prefill_chunk": (_I32, [_P, _P, _P, _P, _I32, _P, _I32, _P, _P,
@@ -264,9 +264,10 @@ def paged_attention_prefill_chunk(query, k_cache, v_cache, block_tables,
     return out
 
 
-def varlen_workspace_size(num_reqs, num_kv_heads, head_dim, max_seq_len):
-    return int(library().paged_attention_varlen_workspace_size(num_reqs, num_kv_heads,
-                                                               head_dim, max_seq_len))
+def varlen_workspace_size(num_reqs, num_q_tokens, num_kv_heads, head_dim, max_seq_len):
+    return int(library().paged_attention_varlen_workspace_size(num_reqs, num_q_tokens,
+                                                               num_kv_heads, head_dim,
+                                                               max_seq_len))
 
 
 def paged_attention_varlen(query, k_cache, v_cache, block_tables, query_start_loc,
@@ -280,7 +281,7 @@ def paged_attention_varlen(query, k_cache, v_cache, block_tables, query_start_lo
     r = num_computed_tokens.shape[0]
     if out is None:
         out = torch.empty_like(query)
-    need = varlen_workspace_size(r, hkv, d, max_seq_len)
+    need = varlen_workspace_size(r, t, hkv, d, max_seq_len)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=query.device)
     assert query_start_loc.shape[0] == r + 1 and block_tables.shape[0] >= r

@@ -109,52 +109,22 @@ struct Stage {
 }  // namespace pf
 
 
-// One workgroup (4 waves) of the chunked prefill: token tile `wg / num_kv_heads`
-// of the requests' tiles, kv head `wg % num_kv_heads`.  Requests with at most
-// `narrow_rows` query rows (tokens x group) get no tiles here (another path
-// serves them; 0 = every request).  stage0 and stage1 are the workgroup's two
+// One workgroup (4 waves) of the chunked prefill: token tile `tile_in_req` of
+// request `req`, kv head `kvh`.  stage0 and stage1 are the workgroup's two
 // LDS stages, passed as separate objects so the compiler can tell the stage
 // being read from the stage the copies are writing.
-PKV_DEVICE void prefill_tile(
-    pf::Stage& stage0, pf::Stage& stage1, int wg, int narrow_rows,
+PKV_DEVICE void prefill_tile_at(
+    pf::Stage& stage0, pf::Stage& stage1, int req, int tile_in_req, int kvh,
     uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
     const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
     int32_t num_blocks, const int32_t* __restrict__ block_tables, int32_t max_blocks,
     const int32_t* __restrict__ query_start_loc, const int32_t* __restrict__ num_computed,
-    int32_t num_reqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t group,
-    float scale_log2) {
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t group, float scale_log2) {
   using namespace pf;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int tokens_per_wg = kRows / group;
-
-  // ---- which (request, token tile, kv head) this workgroup owns
-  const int kvh = wg % num_kv_heads;
-  const int tile = wg / num_kv_heads;
-  int req = -1, tile_in_req = 0;
-  {
-    int before = 0;
-    for (int base = 0; base < num_reqs; base += kWave) {
-      const int r = base + lane;
-      const int n = r < num_reqs ? query_start_loc[r + 1] - query_start_loc[r] : 0;
-      const int tiles = (n > 0 && n * group > narrow_rows) ? (n + tokens_per_wg - 1) / tokens_per_wg : 0;
-      const int incl = wave_scan(tiles);
-      const uint64_t hit = __ballot(before + incl > tile);
-      if (hit) {
-        const int first = __builtin_ctzll(hit);
-        const int incl_first = __shfl(incl, first, kWave);
-        const int tiles_first = __shfl(tiles, first, kWave);
-        req = base + first;
-        tile_in_req = tile - (before + incl_first - tiles_first);
-        break;
-      }
-      before += __shfl(incl, kWave - 1, kWave);
-    }
-  }
-  req = __builtin_amdgcn_readfirstlane(req);
-  tile_in_req = __builtin_amdgcn_readfirstlane(tile_in_req);
-  if (req < 0) return;
   const int q_begin = load_scalar(query_start_loc, req);
   const int n_req = load_scalar(query_start_loc, req + 1) - q_begin;
   const int computed = load_scalar(num_computed, req);
@@ -405,6 +375,53 @@ PKV_DEVICE void prefill_tile(
       *reinterpret_cast<uint2*>(op + db * 16) = make_uint2(w0, w1);
     }
   }
+}
+
+// The same, with the piece found by a scan over the requests: token tile
+// `wg / num_kv_heads` of the requests' tiles, kv head `wg % num_kv_heads`.
+// Requests with at most `narrow_rows` query rows (tokens x group) get no
+// tiles (another path serves them; 0 = every request).
+PKV_DEVICE void prefill_tile(
+    pf::Stage& stage0, pf::Stage& stage1, int wg, int narrow_rows,
+    uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
+    const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
+    int32_t num_blocks, const int32_t* __restrict__ block_tables, int32_t max_blocks,
+    const int32_t* __restrict__ query_start_loc, const int32_t* __restrict__ num_computed,
+    int32_t num_reqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t group,
+    float scale_log2) {
+  using namespace pf;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int tokens_per_wg = kRows / group;
+
+  // ---- which (request, token tile, kv head) this workgroup owns
+  const int kvh = wg % num_kv_heads;
+  const int tile = wg / num_kv_heads;
+  int req = -1, tile_in_req = 0;
+  {
+    int before = 0;
+    for (int base = 0; base < num_reqs; base += kWave) {
+      const int r = base + lane;
+      const int n = r < num_reqs ? query_start_loc[r + 1] - query_start_loc[r] : 0;
+      const int tiles = (n > 0 && n * group > narrow_rows) ? (n + tokens_per_wg - 1) / tokens_per_wg : 0;
+      const int incl = wave_scan(tiles);
+      const uint64_t hit = __ballot(before + incl > tile);
+      if (hit) {
+        const int first = __builtin_ctzll(hit);
+        const int incl_first = __shfl(incl, first, kWave);
+        const int tiles_first = __shfl(tiles, first, kWave);
+        req = base + first;
+        tile_in_req = tile - (before + incl_first - tiles_first);
+        break;
+      }
+      before += __shfl(incl, kWave - 1, kWave);
+    }
+  }
+  req = __builtin_amdgcn_readfirstlane(req);
+  tile_in_req = __builtin_amdgcn_readfirstlane(tile_in_req);
+  if (req < 0) return;
+  prefill_tile_at(stage0, stage1, req, tile_in_req, kvh, out, query, k_cache, v_cache,
+                  num_blocks, block_tables, max_blocks, query_start_loc, num_computed,
+                  num_q_heads, num_kv_heads, group, scale_log2);
 }
 
 }  // namespace pkv

@@ -48,7 +48,7 @@ using pf::lds_i16x4_t;
 constexpr int kD = 128;
 constexpr int kNarrowRows = 16;          // query rows of a narrow request at most
 constexpr int kNarrowChunk = 64;         // blocks per narrow run
-constexpr int kDepth = 4;                // blocks in flight per narrow wave
+constexpr int kDepth = 3;                // blocks in flight per narrow wave
 constexpr int kVStride = kD * 2 + 32;    // LDS bytes per staged V row
 constexpr int kKSteps = kD / 32;
 constexpr int kMTiles = kD / 16;
@@ -261,95 +261,146 @@ PKV_DEVICE void narrow_unit(char* vl, int r, int kvh, int run, int runs_per_req,
 // workgroups of an XCD over its compute units in a fixed rotation, so a
 // static pattern of kinds in the grid (wide, narrow, wide, ...) would pin each
 // kind to a fixed subset of the compute units.  Instead each XCD has a
-// ticket counter: a workgroup draws the next ticket of its XCD and runs the
-// piece of work that ticket names, whatever compute unit it landed on.
-// Queue x holds the wide tiles and narrow workgroups whose index is x mod 8
-// (wide tiles are numbered kv head fastest, so with a multiple of eight kv
-// heads one XCD keeps the tiles of the same kv heads and its L2 their shared
-// prefix), alternating one wide, one narrow while both last, then the rest.
-// The grid gives every XCD as many workgroups as its queue holds at most;
-// surplus workgroups draw a ticket past the end and exit.
+// ticket counter, and the kernel is persistent: about two workgroups per
+// compute unit, each drawing the next ticket of its XCD's queue, running the
+// piece of work that ticket names, and drawing again until the queue is
+// empty.  Queue x holds the wide and narrow workgroup indices equal to x
+// mod 8 (wide tiles are numbered kv head fastest, so with a multiple of eight
+// kv heads one XCD keeps the tiles of the same kv heads and its L2 their
+// shared prefix), alternating one wide, one narrow while both last, then the
+// rest.  The counters sit 256 bytes apart, so that their atomics do not queue
+// on one memory channel.
+//
+// A one-workgroup plan kernel runs first: it clears the counters and lists
+// every wide tile as (request, tile of the request) and every narrow item as
+// (request, run), so that a workgroup finds its piece with one load.
 constexpr int kQueues = 8;
+constexpr int kPlanThreads = 256;
+constexpr int kTicketStride = 64;                    // int32 apart: 256 bytes
+constexpr int kWideCount = kQueues * kTicketStride;  // where the plan's totals sit
+constexpr int kNarrowCount = kWideCount + 1;
+
+struct Plan {
+  int32_t* tickets;        // counter of queue x at x * kTicketStride; then the totals
+  int2* wide_map;          // tile -> (request, tile of the request)
+  int2* narrow_map;        // item -> (request, run)
+  int32_t wide_cap, narrow_cap;
+};
+
+__global__ __launch_bounds__(kPlanThreads) void varlen_plan_kernel(
+    const int32_t* __restrict__ query_start_loc, const int32_t* __restrict__ num_computed,
+    int32_t num_reqs, int32_t group, int32_t max_blocks, int32_t runs_per_req, Plan plan) {
+  __shared__ int sw[kPlanThreads], sn[kPlanThreads];
+  __shared__ int carry[2];
+  const int tid = threadIdx.x;
+  const int tokens_per_wg = pf::kRows / group;
+  if (tid < kQueues) plan.tickets[tid * kTicketStride] = 0;
+  if (tid < 2) carry[tid] = 0;
+  __syncthreads();
+  for (int base = 0; base < num_reqs; base += kPlanThreads) {
+    const int r = base + tid;
+    int wt = 0, ni = 0;
+    if (r < num_reqs) {
+      const int n = query_start_loc[r + 1] - query_start_loc[r];
+      const int c = num_computed[r];
+      if (n > 0 && n * group > vl::kNarrowRows)
+        wt = (n + tokens_per_wg - 1) / tokens_per_wg;
+      else if (n > 0 && c >= 0)
+        ni = min(vl::runs_of(min((c + n + kBlock - 1) / kBlock, max_blocks)), runs_per_req);
+    }
+    sw[tid] = wt;
+    sn[tid] = ni;
+    __syncthreads();
+    for (int o = 1; o < kPlanThreads; o <<= 1) {     // inclusive scans of both counts
+      const int aw = tid >= o ? sw[tid - o] : 0, an = tid >= o ? sn[tid - o] : 0;
+      __syncthreads();
+      sw[tid] += aw;
+      sn[tid] += an;
+      __syncthreads();
+    }
+    const int w0 = carry[0] + sw[tid] - wt, n0 = carry[1] + sn[tid] - ni;
+    for (int k = 0; k < wt && w0 + k < plan.wide_cap; ++k) plan.wide_map[w0 + k] = make_int2(r, k);
+    for (int k = 0; k < ni && n0 + k < plan.narrow_cap; ++k)
+      plan.narrow_map[n0 + k] = make_int2(r, k);
+    __syncthreads();
+    if (tid == 0) {
+      carry[0] += sw[kPlanThreads - 1];
+      carry[1] += sn[kPlanThreads - 1];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    plan.tickets[kWideCount] = min(carry[0], plan.wide_cap);
+    plan.tickets[kNarrowCount] = min(carry[1], plan.narrow_cap);
+  }
+}
 
 __global__ __launch_bounds__(256, 2) void varlen_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
     const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
     int32_t num_blocks, const int32_t* __restrict__ block_tables, int32_t max_blocks,
     const int32_t* __restrict__ query_start_loc, const int32_t* __restrict__ num_computed,
-    int32_t num_reqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t group,
-    float scale_log2, int32_t wide_wgs, int32_t narrow_wgs, int32_t runs_per_req,
-    int32_t* __restrict__ tickets, float* __restrict__ part_o, float2* __restrict__ part_ml) {
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t group, float scale_log2,
+    int32_t wide_wgs, int32_t narrow_wgs, int32_t runs_per_req, Plan plan,
+    float* __restrict__ part_o, float2* __restrict__ part_ml) {
   __shared__ pf::Stage stage0, stage1;
-  __shared__ int ticket_lds;
+  // the ticket is passed through the stages' first word (a separate LDS
+  // variable would take the workgroup past 64 KiB of LDS)
+  int* const ticket_lds = reinterpret_cast<int*>(&stage0);
   const int x = blockIdx.x % kQueues;
-  if (threadIdx.x == 0)
-    ticket_lds = __hip_atomic_fetch_add(tickets + x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  const int k = ticket_lds;
   const int wide_x = (wide_wgs + kQueues - 1 - x) / kQueues;     // queue x's share of each kind
   const int narrow_x = (narrow_wgs + kQueues - 1 - x) / kQueues;
   const int paired = min(wide_x, narrow_x);
-  bool wide;
-  int idx;
-  if (k < 2 * paired) {
-    wide = (k & 1) == 0;
-    idx = (k >> 1) * kQueues + x;
-  } else {
-    wide = wide_x > narrow_x;
-    idx = (k - paired) * kQueues + x;
-  }
-  if (wide) {
-    if (idx >= wide_wgs) return;
-    prefill_tile(stage0, stage1, idx, vl::kNarrowRows, out, query, k_cache, v_cache,
-                 num_blocks, block_tables, max_blocks, query_start_loc, num_computed,
-                 num_reqs, num_q_heads, num_kv_heads, group, scale_log2);
-    return;
-  }
-  if (idx >= narrow_wgs) return;
-  // narrow: wave w of workgroup idx takes unit idx * 4 + w; a unit is (item,
-  // kv head) with the kv head fastest, so the waves of a workgroup usually
-  // share an item and take equally long; the items are the (narrow request,
-  // run) pairs in request order -- only requests with work get items
+  const int wide_tiles = load_scalar(plan.tickets, kWideCount);
+  const int narrow_items = load_scalar(plan.tickets, kNarrowCount);
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);
-  const int64_t u = int64_t(idx) * 4 + wave;
-  const int kvh = int(u % num_kv_heads);
-  const int64_t item = u / num_kv_heads;
-  int r = -1, run = 0;
-  {
-    const int lane = lane_id();
-    int before = 0;
-    for (int base = 0; base < num_reqs; base += kWave) {
-      const int q = base + lane;
-      int runs = 0;
-      if (q < num_reqs) {
-        const int n = query_start_loc[q + 1] - query_start_loc[q];
-        const int c = num_computed[q];
-        if (n > 0 && n * group <= vl::kNarrowRows && c >= 0)
-          runs = min(vl::runs_of(min((c + n + kBlock - 1) / kBlock, max_blocks)), runs_per_req);
-      }
-      const int incl = pf::wave_scan(runs);
-      const uint64_t hit = __ballot(before + incl > item);
-      if (hit) {
-        const int first = __builtin_ctzll(hit);
-        r = base + first;
-        run = int(item - (before + __shfl(incl, first, kWave) - __shfl(runs, first, kWave)));
-        break;
-      }
-      before += __shfl(incl, kWave - 1, kWave);
+  for (;;) {
+    if (threadIdx.x == 0)
+      *ticket_lds = __hip_atomic_fetch_add(plan.tickets + x * kTicketStride, 1,
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int k = *ticket_lds;
+    __syncthreads();     // every thread holds the ticket before the stages fill
+    if (k >= wide_x + narrow_x) break;
+    bool wide;
+    int idx;
+    if (k < 2 * paired) {
+      wide = (k & 1) == 0;
+      idx = (k >> 1) * kQueues + x;
+    } else {
+      wide = wide_x > narrow_x;
+      idx = (k - paired) * kQueues + x;
     }
+    if (wide) {
+      const int tile = idx / num_kv_heads;
+      if (tile < wide_tiles) {
+        const int2 piece = reinterpret_cast<const int2*>(plan.wide_map)[tile];
+        prefill_tile_at(stage0, stage1, __builtin_amdgcn_readfirstlane(piece.x),
+                        __builtin_amdgcn_readfirstlane(piece.y), idx % num_kv_heads, out,
+                        query, k_cache, v_cache, num_blocks, block_tables, max_blocks,
+                        query_start_loc, num_computed, num_q_heads, num_kv_heads, group,
+                        scale_log2);
+      }
+    } else {
+      // narrow: wave w of workgroup idx takes unit idx * 4 + w; a unit is
+      // (item, kv head) with the kv head fastest, so the waves of a workgroup
+      // usually share an item and take equally long
+      const int64_t u = int64_t(idx) * 4 + wave;
+      const int kvh = int(u % num_kv_heads);
+      const int64_t item = u / num_kv_heads;
+      if (item < narrow_items) {
+        const int2 piece = plan.narrow_map[item];
+        const int r = __builtin_amdgcn_readfirstlane(piece.x);
+        const int run = __builtin_amdgcn_readfirstlane(piece.y);
+        char* lds = reinterpret_cast<char*>(&stage1) + wave * (kBlock * vl::kVStride);
+        vl::narrow_unit(lds, r, kvh, run, runs_per_req, out, query, k_cache, v_cache,
+                        num_blocks, block_tables, max_blocks, query_start_loc, num_computed,
+                        num_q_heads, num_kv_heads, group, scale_log2,
+                        vl::Workspace{part_o, part_ml});
+      }
+    }
+    __syncthreads();     // the stages are free before the next ticket
   }
-  r = __builtin_amdgcn_readfirstlane(r);
-  run = __builtin_amdgcn_readfirstlane(run);
-  if (r < 0) return;
-  char* lds = reinterpret_cast<char*>(&stage0) + wave * (kBlock * vl::kVStride);
-  vl::narrow_unit(lds, r, kvh, run, runs_per_req, out, query, k_cache, v_cache, num_blocks,
-                  block_tables, max_blocks, query_start_loc, num_computed, num_q_heads,
-                  num_kv_heads, group, scale_log2, vl::Workspace{part_o, part_ml});
-}
-
-// Clears the ticket counters before a launch.
-__global__ void varlen_reset_kernel(int32_t* __restrict__ tickets) {
-  if (threadIdx.x < kQueues) tickets[threadIdx.x] = 0;
 }
 
 // Merge of the narrow requests that span several runs: one workgroup per
@@ -400,17 +451,26 @@ static size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
 struct VarlenPlan {
   int32_t runs_per_req;
-  size_t ticket_bytes, o_bytes, ml_bytes;
+  int64_t wide_cap, narrow_cap;     // wide tiles (for groups up to 8), narrow items
+  size_t ticket_bytes, wide_bytes, narrow_bytes, o_bytes, ml_bytes;
+  size_t total() const { return ticket_bytes + wide_bytes + narrow_bytes + o_bytes + ml_bytes; }
 };
 
-static bool varlen_plan(int32_t num_reqs, int32_t num_kv_heads, int32_t head_dim,
-                        int32_t max_seq_len, VarlenPlan& p) {
-  if (num_reqs < 0 || num_kv_heads <= 0 || head_dim != vl::kD || max_seq_len < 0) return false;
+static bool varlen_plan(int32_t num_reqs, int32_t num_q_tokens, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t max_seq_len, VarlenPlan& p) {
+  if (num_reqs < 0 || num_q_tokens < 0 || num_kv_heads <= 0 || head_dim != vl::kD ||
+      max_seq_len < 0)
+    return false;
   const int nblk = (max_seq_len + kBlock - 1) / kBlock;
   p.runs_per_req = std::max(1, vl::runs_of(nblk));
-  const size_t units = size_t(num_reqs) * num_kv_heads;
-  const size_t recs = units * p.runs_per_req;
-  p.ticket_bytes = 256;
+  // a tile holds at least 16 tokens (128 rows, group at most 8); each
+  // request's last tile may be partial
+  p.wide_cap = (int64_t(num_q_tokens) + 15) / 16 + num_reqs;
+  p.narrow_cap = int64_t(num_reqs) * p.runs_per_req;
+  const size_t recs = size_t(p.narrow_cap) * num_kv_heads;
+  p.ticket_bytes = align256((kNarrowCount + 1) * sizeof(int32_t));
+  p.wide_bytes = align256(size_t(p.wide_cap) * sizeof(int2));
+  p.narrow_bytes = align256(size_t(p.narrow_cap) * sizeof(int2));
   p.o_bytes = align256(recs * vl::kNarrowRows * head_dim * sizeof(float));
   p.ml_bytes = align256(recs * vl::kNarrowRows * 2 * sizeof(float));
   return true;
@@ -420,13 +480,12 @@ static bool varlen_plan(int32_t num_reqs, int32_t num_kv_heads, int32_t head_dim
 
 using namespace pkv;
 
-extern "C" size_t paged_attention_varlen_workspace_size(int32_t num_reqs,
-                                                        int32_t num_kv_heads,
-                                                        int32_t head_dim,
+extern "C" size_t paged_attention_varlen_workspace_size(int32_t num_reqs, int32_t num_q_tokens,
+                                                        int32_t num_kv_heads, int32_t head_dim,
                                                         int32_t max_seq_len) {
   VarlenPlan p;
-  if (!varlen_plan(num_reqs, num_kv_heads, head_dim, max_seq_len, p)) return 0;
-  return p.ticket_bytes + p.o_bytes + p.ml_bytes;
+  if (!varlen_plan(num_reqs, num_q_tokens, num_kv_heads, head_dim, max_seq_len, p)) return 0;
+  return p.total();
 }
 
 extern "C" pkv_status paged_attention_varlen(
@@ -456,28 +515,47 @@ extern "C" pkv_status paged_attention_varlen(
       !aligned(num_computed_tokens, 4))
     return PKV_ERR_ALIGN;
   VarlenPlan p;
-  if (!varlen_plan(num_reqs, num_kv_heads, head_dim, max_seq_len, p)) return PKV_ERR_SHAPE;
-  if (!workspace || workspace_bytes < p.ticket_bytes + p.o_bytes + p.ml_bytes)
-    return PKV_ERR_WORKSPACE;
+  if (!varlen_plan(num_reqs, num_q_tokens, num_kv_heads, head_dim, max_seq_len, p))
+    return PKV_ERR_SHAPE;
+  if (!workspace || workspace_bytes < p.total()) return PKV_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return PKV_ERR_ALIGN;
   const int tokens_per_wg = pf::kRows / group;
   const int64_t wide = ((int64_t(num_q_tokens) + tokens_per_wg - 1) / tokens_per_wg + num_reqs) *
                        num_kv_heads;
   const int64_t narrow = (int64_t(num_reqs) * p.runs_per_req * num_kv_heads + 3) / 4;
-  const int64_t grid = ((wide + kQueues - 1) / kQueues + (narrow + kQueues - 1) / kQueues) * kQueues;
+  // persistent: two workgroups per compute unit (the occupancy the LDS and
+  // registers allow), never more than the longest queue needs
+  int device = 0, cus = 0;
+  if (hipGetDevice(&device) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
+      cus <= 0)
+    return PKV_ERR_LAUNCH;
+  const int64_t per_queue = std::min<int64_t>(
+      (wide + kQueues - 1) / kQueues + (narrow + kQueues - 1) / kQueues,
+      (2 * int64_t(cus) + kQueues - 1) / kQueues);
+  const int64_t grid = per_queue * kQueues;
   if (grid > 0x7fffffff || int64_t(num_reqs) * num_kv_heads > 0x7fffffff) return PKV_ERR_SHAPE;
+  if (p.wide_cap > 0x7fffffff || p.narrow_cap > 0x7fffffff) return PKV_ERR_SHAPE;
   char* ws = static_cast<char*>(workspace);
-  int32_t* tickets = reinterpret_cast<int32_t*>(ws);
-  float* part_o = reinterpret_cast<float*>(ws + p.ticket_bytes);
-  float2* part_ml = reinterpret_cast<float2*>(ws + p.ticket_bytes + p.o_bytes);
-  hipLaunchKernelGGL(varlen_reset_kernel, dim3(1), dim3(64), 0, as_stream(stream), tickets);
+  Plan plan;
+  plan.tickets = reinterpret_cast<int32_t*>(ws);
+  plan.wide_map = reinterpret_cast<int2*>(ws + p.ticket_bytes);
+  plan.narrow_map = reinterpret_cast<int2*>(ws + p.ticket_bytes + p.wide_bytes);
+  plan.wide_cap = int32_t(p.wide_cap);
+  plan.narrow_cap = int32_t(p.narrow_cap);
+  char* parts = ws + p.ticket_bytes + p.wide_bytes + p.narrow_bytes;
+  float* part_o = reinterpret_cast<float*>(parts);
+  float2* part_ml = reinterpret_cast<float2*>(parts + p.o_bytes);
+  hipLaunchKernelGGL(varlen_plan_kernel, dim3(1), dim3(kPlanThreads), 0, as_stream(stream),
+                     query_start_loc, num_computed_tokens, num_reqs, group, max_blocks_per_seq,
+                     p.runs_per_req, plan);
   hipLaunchKernelGGL(varlen_kernel, dim3(uint32_t(grid)), dim3(256), 0, as_stream(stream),
                      static_cast<uint16_t*>(out), static_cast<const uint16_t*>(query),
                      static_cast<const uint16_t*>(k_cache),
                      static_cast<const uint16_t*>(v_cache), num_blocks, block_tables,
-                     max_blocks_per_seq, query_start_loc, num_computed_tokens, num_reqs,
-                     num_q_heads, num_kv_heads, group, softmax_scale * pf::kLog2e,
-                     int32_t(wide), int32_t(narrow), p.runs_per_req, tickets, part_o, part_ml);
+                     max_blocks_per_seq, query_start_loc, num_computed_tokens, num_q_heads,
+                     num_kv_heads, group, softmax_scale * pf::kLog2e, int32_t(wide),
+                     int32_t(narrow), p.runs_per_req, plan, part_o, part_ml);
   if (p.runs_per_req > 1)
     hipLaunchKernelGGL(varlen_merge_kernel, dim3(uint32_t(num_reqs * num_kv_heads)), dim3(256),
                        0, as_stream(stream), static_cast<uint16_t*>(out), query_start_loc,

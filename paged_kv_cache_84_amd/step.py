@@ -107,7 +107,7 @@ class DeviceStep:
             qsl = s.query_start_loc
             self.varlen_qsl = _i32(qsl, self.device)
             self.varlen_max_seq = int(np.max(s.num_computed + np.diff(qsl)))
-            need = B.varlen_workspace_size(s.num_reqs, s.num_kv_heads, s.head_dim,
+            need = B.varlen_workspace_size(s.num_reqs, int(qsl[-1]), s.num_kv_heads, s.head_dim,
                                            self.varlen_max_seq)
             self.varlen_ws = torch.empty(max(need, 16), dtype=torch.uint8, device=self.device)
         B.paged_attention_varlen(self.q[layer], self.k_caches[layer], self.v_caches[layer],

@@ -81,7 +81,7 @@ def test_varlen_repeated_calls_with_a_reused_workspace_are_bitwise_identical():
     announce("varlen repeat")
     q, kc, vc, tables, qsl, comp, mx = schedule_case([3000, 5000, 70, 8000], [1, 4, 1, 2],
                                                      32, 8, seed=3)
-    need = pk.varlen_workspace_size(4, 8, 128, mx)
+    need = pk.varlen_workspace_size(4, int(qsl[-1]), 8, 128, mx)
     ws = torch.full((need,), 0x7F, dtype=torch.uint8, device=DEV)
     first = run_varlen(q, kc, vc, tables, qsl, comp, mx, ws).clone()
     for _ in range(3):
