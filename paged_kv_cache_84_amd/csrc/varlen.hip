@@ -276,12 +276,16 @@ PKV_DEVICE void narrow_unit(char* vl, int r, int kvh, int run, int runs_per_req,
 // (request, run), so that a workgroup finds its piece with one load.
 constexpr int kQueues = 8;
 constexpr int kPlanThreads = 256;
-constexpr int kTicketStride = 64;                    // int32 apart: 256 bytes
-constexpr int kWideCount = kQueues * kTicketStride;  // where the plan's totals sit
+constexpr int kTicketStride = 64;                        // int32 apart: 256 bytes
+constexpr int kWideCount = 2 * kQueues * kTicketStride;  // where the plan's totals sit
 constexpr int kNarrowCount = kWideCount + 1;
+constexpr int kCuSlots = kQueues * 8 * 2 * 16;           // XCD x engine x array x unit
+constexpr int kHwIdReg = 4 | (31 << 11);                 // HW_ID, bits 0..31
 
 struct Plan {
-  int32_t* tickets;        // counter of queue x at x * kTicketStride; then the totals
+  int32_t* tickets;        // counters: wide queue x at x * kTicketStride, narrow queue x
+                           // at (8 + x) * kTicketStride; then the totals
+  int32_t* cu_slots;       // workgroups arrived per compute unit
   int2* wide_map;          // tile -> (request, tile of the request)
   int2* narrow_map;        // item -> (request, run)
   int32_t wide_cap, narrow_cap;
@@ -294,7 +298,8 @@ __global__ __launch_bounds__(kPlanThreads) void varlen_plan_kernel(
   __shared__ int carry[2];
   const int tid = threadIdx.x;
   const int tokens_per_wg = pf::kRows / group;
-  if (tid < kQueues) plan.tickets[tid * kTicketStride] = 0;
+  if (tid < 2 * kQueues) plan.tickets[tid * kTicketStride] = 0;
+  for (int i = tid; i < kCuSlots; i += kPlanThreads) plan.cu_slots[i] = 0;
   if (tid < 2) carry[tid] = 0;
   __syncthreads();
   for (int base = 0; base < num_reqs; base += kPlanThreads) {
@@ -344,36 +349,55 @@ __global__ __launch_bounds__(256, 2) void varlen_kernel(
     int32_t wide_wgs, int32_t narrow_wgs, int32_t runs_per_req, Plan plan,
     float* __restrict__ part_o, float2* __restrict__ part_ml) {
   __shared__ pf::Stage stage0, stage1;
-  // the ticket is passed through the stages' first word (a separate LDS
+  // tickets are passed through the stages' first word (a separate LDS
   // variable would take the workgroup past 64 KiB of LDS)
   int* const ticket_lds = reinterpret_cast<int*>(&stage0);
   const int x = blockIdx.x % kQueues;
   const int wide_x = (wide_wgs + kQueues - 1 - x) / kQueues;     // queue x's share of each kind
   const int narrow_x = (narrow_wgs + kQueues - 1 - x) / kQueues;
-  const int paired = min(wide_x, narrow_x);
   const int wide_tiles = load_scalar(plan.tickets, kWideCount);
   const int narrow_items = load_scalar(plan.tickets, kNarrowCount);
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);
-  for (;;) {
+  // The first workgroup to arrive on a compute unit prefers wide work, the
+  // second narrow work, so that each compute unit runs one of each while
+  // both queues last: the matrix-core-bound tiles and the memory-bound
+  // streams then share every SIMD.  A compute unit is named by its XCD and
+  // its place in it (shader engine, array, unit fields of the wave's
+  // hardware id).
+  if (threadIdx.x == 0) {
+    const uint32_t hw = __builtin_amdgcn_s_getreg(kHwIdReg);
+    const int key = ((x * 8 + int((hw >> 13) & 7)) * 2 + int((hw >> 12) & 1)) * 16 +
+                    int((hw >> 8) & 15);
+    *ticket_lds = __hip_atomic_fetch_add(plan.cu_slots + key, 1, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  const bool prefer_wide = (*ticket_lds & 1) == 0;
+  __syncthreads();
+  bool wide_open = true, narrow_open = true;
+  while (wide_open || narrow_open) {
+    // the preferred queue while it lasts, then the other one
+    const bool wide = wide_open && (prefer_wide || !narrow_open);
     if (threadIdx.x == 0)
-      *ticket_lds = __hip_atomic_fetch_add(plan.tickets + x * kTicketStride, 1,
-                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      *ticket_lds = __hip_atomic_fetch_add(
+          plan.tickets + (wide ? x : kQueues + x) * kTicketStride, 1, __ATOMIC_RELAXED,
+          __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     const int k = *ticket_lds;
     __syncthreads();     // every thread holds the ticket before the stages fill
-    if (k >= wide_x + narrow_x) break;
-    bool wide;
-    int idx;
-    if (k < 2 * paired) {
-      wide = (k & 1) == 0;
-      idx = (k >> 1) * kQueues + x;
-    } else {
-      wide = wide_x > narrow_x;
-      idx = (k - paired) * kQueues + x;
+    const int idx = k * kQueues + x;
+    // indices only grow along a queue: the first one past the work closes it
+    if (wide && (k >= wide_x || idx / num_kv_heads >= wide_tiles)) {
+      wide_open = false;
+      continue;
+    }
+    if (!wide && (k >= narrow_x || int64_t(idx) * 4 / num_kv_heads >= narrow_items)) {
+      narrow_open = false;
+      continue;
     }
     if (wide) {
       const int tile = idx / num_kv_heads;
-      if (tile < wide_tiles) {
+      {
         const int2 piece = reinterpret_cast<const int2*>(plan.wide_map)[tile];
         prefill_tile_at(stage0, stage1, __builtin_amdgcn_readfirstlane(piece.x),
                         __builtin_amdgcn_readfirstlane(piece.y), idx % num_kv_heads, out,
@@ -468,7 +492,7 @@ static bool varlen_plan(int32_t num_reqs, int32_t num_q_tokens, int32_t num_kv_h
   p.wide_cap = (int64_t(num_q_tokens) + 15) / 16 + num_reqs;
   p.narrow_cap = int64_t(num_reqs) * p.runs_per_req;
   const size_t recs = size_t(p.narrow_cap) * num_kv_heads;
-  p.ticket_bytes = align256((kNarrowCount + 1) * sizeof(int32_t));
+  p.ticket_bytes = align256((kNarrowCount + 1) * sizeof(int32_t)) + kCuSlots * sizeof(int32_t);
   p.wide_bytes = align256(size_t(p.wide_cap) * sizeof(int2));
   p.narrow_bytes = align256(size_t(p.narrow_cap) * sizeof(int2));
   p.o_bytes = align256(recs * vl::kNarrowRows * head_dim * sizeof(float));
@@ -539,6 +563,7 @@ extern "C" pkv_status paged_attention_varlen(
   char* ws = static_cast<char*>(workspace);
   Plan plan;
   plan.tickets = reinterpret_cast<int32_t*>(ws);
+  plan.cu_slots = reinterpret_cast<int32_t*>(ws + align256((kNarrowCount + 1) * sizeof(int32_t)));
   plan.wide_map = reinterpret_cast<int2*>(ws + p.ticket_bytes);
   plan.narrow_map = reinterpret_cast<int2*>(ws + p.ticket_bytes + p.wide_bytes);
   plan.wide_cap = int32_t(p.wide_cap);

@@ -181,16 +181,16 @@ def test_varlen_errors(lib):
     def a256(n):
         return (n + 255) // 256 * 256
 
-    # the queue counters (256 bytes apart) and totals; the tile list (50 tokens in tiles of at
+    # the queue counters (256 bytes apart), totals and per-CU arrivals; the tile list (50 tokens in tiles of at
     # least 16, plus one partial tile per request) and the run list (2 runs of
     # 64 blocks per request), 8 bytes an entry; then per (request, kv head,
     # run) 16 columns of 128 fp32 values and 16 (max, sum) pairs
-    assert need == (2304 + a256((4 + 3) * 8) + a256(3 * 2 * 8) + 3 * 8 * 2 * 16 * 128 * 4
+    assert need == (12544 + a256((4 + 3) * 8) + a256(3 * 2 * 8) + 3 * 8 * 2 * 16 * 128 * 4
                     + 3 * 8 * 2 * 16 * 2 * 4)
     assert lib.paged_attention_varlen_workspace_size(3, 50, 8, 96, 2000) == 0
     assert lib.paged_attention_varlen_workspace_size(3, -1, 8, 128, 2000) == 0
     assert lib.paged_attention_varlen_workspace_size(1, 1, 8, 128, 0) == (
-        2304 + 256 + 256 + 8 * 16 * 130 * 4)
+        12544 + 256 + 256 + 8 * 16 * 130 * 4)
     base = [p, p, p, p, 100, p, 125, p, p, 3, 50, 2000, 32, 8, 128, 0.088, BF16, BF16,
             p, need, None]
 
