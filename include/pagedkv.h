@@ -295,7 +295,8 @@ pkv_status paged_attention_prefill_chunk(void* out, const void* query,
  * drafts), and a step advances each by some tokens
  * ("01. vLLM：从分页 KV 起家的通用推理引擎", section "调度器：统一的 token 预算";
  * V1 EngineCore architecture page, section "统一 token 调度"); drafts are
- * verified by the target model in one step (section "投机解码").
+ * verified by the target model in one step (the "01. vLLM" page, section
+ * "投机解码").
  *
  * Semantics are those of paged_attention_prefill_chunk over all requests:
  * row i of request r, at position p = num_computed_tokens[r] + i, attends to

@@ -7,27 +7,25 @@
 // speculative drafts), and a step advances every request by some tokens
 // ("01. vLLM：从分页 KV 起家的通用推理引擎", section "调度器：统一的 token 预算";
 // V1 EngineCore architecture page, section "统一 token 调度").  Drafts are
-// verified by the target model in one step (same page, section "投机解码"):
-// the 1 + k verified rows attend causally, like a short chunk.  The work
-// still differs in cost (same EngineCore section): a chunk of many rows is a
-// dense contraction, a request of a few rows streams its whole history.
+// verified by the target model in one step (the "01. vLLM" page, section
+// "投机解码"): the 1 + k verified rows attend causally, like a short chunk.
+// The rows of one step still differ in cost: a chunk of many rows is a dense
+// contraction, a request of a few rows streams its whole history.
 //
-// So the launch holds two kinds of workgroups, interleaved in the grid so
-// that both run at once -- the matrix cores on the chunks while the memory
-// system streams the short requests' histories:
+// So the launch holds two kinds of work, run side by side -- the matrix
+// cores on the chunks while the memory system streams the short requests'
+// histories:
 //   wide   requests with more than 16 query rows (tokens x group): the
-//          chunked-prefill tile of prefill_tile.h;
+//          chunked-prefill tile of prefill_tile.h, one workgroup per (tile,
+//          kv head);
 //   narrow requests with at most 16 rows: one wave per (request, kv head,
 //          run of kNarrowChunk blocks) holds the request's rows as the 16
 //          columns of MFMA tiles and streams the run's blocks (as the decode
 //          kernel does), with the causal limit of each row.  A request with
-//          several runs leaves one partial per run in the workspace; the
-//          run that finishes last (an atomic count per (request, kv head))
-//          merges them with the log-sum-exp rule and writes the output.
-//
-// The last-arriver merge needs no waiting: every run stores its partial,
-// fences, and counts; only the run that brings the count to the number of
-// runs reads the partials (after a fence) and resets the count to zero.
+//          several runs leaves one partial per run in the workspace, and a
+//          small merge kernel combines them with the log-sum-exp rule.
+// How workgroups find their work (a plan kernel, per-XCD queues, persistent
+// workgroups paired per compute unit) is described above varlen_kernel.
 
 #include <math.h>
 
@@ -260,16 +258,16 @@ PKV_DEVICE void narrow_unit(char* vl, int r, int kvh, int run, int runs_per_req,
 // Work queues.  Workgroup b runs on XCD b % 8, and the hardware spreads the
 // workgroups of an XCD over its compute units in a fixed rotation, so a
 // static pattern of kinds in the grid (wide, narrow, wide, ...) would pin each
-// kind to a fixed subset of the compute units.  Instead each XCD has a
-// ticket counter, and the kernel is persistent: about two workgroups per
-// compute unit, each drawing the next ticket of its XCD's queue, running the
-// piece of work that ticket names, and drawing again until the queue is
-// empty.  Queue x holds the wide and narrow workgroup indices equal to x
-// mod 8 (wide tiles are numbered kv head fastest, so with a multiple of eight
-// kv heads one XCD keeps the tiles of the same kv heads and its L2 their
-// shared prefix), alternating one wide, one narrow while both last, then the
-// rest.  The counters sit 256 bytes apart, so that their atomics do not queue
-// on one memory channel.
+// kind to a fixed subset of the compute units.  Instead each XCD has two
+// ticket counters, one per kind, and the kernel is persistent: about two
+// workgroups per compute unit, each drawing the next ticket of a queue of
+// its XCD, running the piece of work that ticket names, and drawing again
+// until both queues are empty.  The wide queue of XCD x holds the wide
+// workgroup indices equal to x mod 8 (tiles numbered kv head fastest, so
+// with a multiple of eight kv heads an XCD keeps the tiles of the same kv
+// heads and its L2 their shared prefix); the narrow queue likewise.  The
+// counters sit 256 bytes apart, so that their atomics do not queue on one
+// memory channel.
 //
 // A one-workgroup plan kernel runs first: it clears the counters and lists
 // every wide tile as (request, tile of the request) and every narrow item as
