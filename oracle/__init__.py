@@ -18,6 +18,11 @@ What it computes, and where the pages define it:
   ("vLLM 引擎解剖", sections "KV 缓存需要多少内存？" (Table 1),
   "PagedAttention：为 KV 缓存分页" (Fig. 2), "V1：统一调度预填充与解码" (Fig. 3)).
 
+* ``blocks``    -- the host block manager: pool, reference counts, LRU free
+  queue, prefix-hash chain and copy-on-write ("01. vLLM", section "KV 缓存管理
+  与前缀缓存"; "vLLM 引擎解剖", sections "PagedAttention：为 KV 缓存分页" and
+  "自动前缀缓存" (Fig. 4); "v1/v0 区别", §4 "KV Cache 管理").
+
 Everything is written for a reader to check by eye: explicit loops over
 logical blocks and query rows, float64 arithmetic, no tiling, no fusion.
 
@@ -29,6 +34,6 @@ value of attention on the large random configurations: the pages print no
 attention values.
 """
 
-from . import formats, paged  # noqa: F401
+from . import blocks, formats, paged  # noqa: F401
 
-__all__ = ["formats", "paged"]
+__all__ = ["blocks", "formats", "paged"]
