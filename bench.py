@@ -1,7 +1,7 @@
 """Benchmark of the paged-attention hot path on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
-                    [--no-mixed] [--no-longctx] [--no-mha] [--no-swap]
+                    [--no-mixed] [--no-longctx] [--no-mha] [--no-swap] [--no-blocks]
     python bench.py --copy-calibration     (a plain 1 GiB device copy, for
                                             the HBM byte counters' scale)
 
@@ -16,8 +16,9 @@ Prints one JSON line (rank 0): whole-step throughput in algorithmic KV GB/s,
 KV tokens/s, the decode call's roofline fraction, the oracle's CPU rate on a
 bounded sample, the mixed unified step with chunked prefill (MFMA
 utilisation of the prefill call), the fp8 long-context decode, the
-32-layer MHA decode step and a device <-> host block swap of one long
-sequence.  The roofline's "traffic" is the HBM bytes per
+32-layer MHA decode step, a device <-> host block swap of one long
+sequence, and the host block manager's operations per second on a serving
+trace (with the oracle's rate on a bounded sample beside it).  The roofline's "traffic" is the HBM bytes per
 decode call that rocprofv3's FETCH_SIZE and WRITE_SIZE counters measured
 (profiles/decode_llama3_8b_64seq_traffic.md), used only while the decode
 sources are the ones those counters were taken on.
@@ -283,6 +284,70 @@ def bench_swap(args, pk):
             "in_frac": round(gb / (ms_in * 1e-3) / PCIE5_X16_GBS, 3)}
 
 
+def _serve(m, trace, batched):
+    """One pass of a serving trace through a block manager (library: batched
+    calls per engine step; oracle: one call per request)."""
+    for st in trace:
+        for rid, prompt in st["adds"]:
+            m.allocate(rid, len(prompt) - m.add_request(rid, prompt))
+        ids, toks = st["decode_ids"], st["decode_tokens"]
+        if batched:
+            m.append_tokens_batch(ids, toks)
+            if m.allocate_batch(ids, np.ones(ids.size, np.int32)).any():
+                raise RuntimeError("block pool too small for the trace")
+        else:
+            for rid, t in zip(ids.tolist(), toks.tolist()):
+                m.append_tokens(rid, [t])
+                m.allocate(rid, 1)
+        for rid in st["frees"]:
+            m.free_request(rid)
+
+
+def bench_block_manager(args, oracle_budget_s=5.0):
+    """Host block manager on a serving trace: 2,000 engine steps, up to 256
+    live requests, prompts = one of 8 shared 2,000-token system prompts + 64..511
+    unique tokens, 32..255 generated tokens each; pool of 32,768 blocks."""
+    from paged_kv_cache_84_amd import blocks as PB
+    from synth.serving import serving_trace, trace_ops
+    trace = serving_trace()
+    ops = trace_ops(trace)
+    adds = sum(len(st["adds"]) for st in trace)
+    m = PB.BlockManager(32768)
+    t0 = time.perf_counter()
+    cached = 0
+    for st in trace:     # the same pass as _serve, counting prefix hits
+        for rid, prompt in st["adds"]:
+            c = m.add_request(rid, prompt)
+            cached += c
+            m.allocate(rid, len(prompt) - c)
+        ids = st["decode_ids"]
+        m.append_tokens_batch(ids, st["decode_tokens"])
+        if m.allocate_batch(ids, np.ones(ids.size, np.int32)).any():
+            raise RuntimeError("block pool too small for the trace")
+        for rid in st["frees"]:
+            m.free_request(rid)
+    lib_s = time.perf_counter() - t0
+    prompt_tokens = sum(len(p) for st in trace for _, p in st["adds"])
+    out = {"workload": " ".join(bench_block_manager.__doc__.split(":", 1)[1].split()),
+           "ops": ops, "requests": adds, "seconds": round(lib_s, 4),
+           "ops_per_s": round(ops / lib_s, 1),
+           "prefix_hit_tokens_frac": round(cached / prompt_tokens, 4)}
+    if not args.no_cpu_baseline:
+        from oracle import blocks as OB
+        om = OB.BlockManager(32768)
+        done_ops, t0 = 0, time.perf_counter()
+        for i, st in enumerate(trace):
+            _serve(om, [st], batched=False)
+            done_ops += 2 * len(st["adds"]) + st["decode_ids"].size + len(st["frees"])
+            if time.perf_counter() - t0 > oracle_budget_s:
+                break
+        osec = time.perf_counter() - t0
+        out["oracle"] = {"ops_per_s": round(done_ops / osec, 1), "steps": i + 1,
+                         "ops": done_ops, "cores": 1, "kind": "oracle",
+                         "sample": f"the first {i + 1} engine steps of the same trace"}
+    return out
+
+
 def bench_extra_decode(args, pk, C, which):
     """Optional legs: the fp8 long-context decode (64/8 heads, 6 x 131,072
     tokens, 512-token partitions) or the 32-layer MHA decode step (32 x 8,192
@@ -332,6 +397,8 @@ def main():
                     help="skip the 32-layer MHA decode step (128 GiB of KV)")
     ap.add_argument("--no-swap", action="store_true",
                     help="skip the device <-> host block swap of one long sequence")
+    ap.add_argument("--no-blocks", action="store_true",
+                    help="skip the host block manager on a serving trace")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter scale)")
     args = ap.parse_args()
@@ -398,6 +465,8 @@ def main():
         line["mha_decode"] = bench_extra_decode(args, pk, C, "mha")
     if not args.no_swap:
         line["swap_blocks"] = bench_swap(args, pk)
+    if not args.no_blocks:
+        line["block_manager"] = bench_block_manager(args)
     if cpu is not None:
         line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)

@@ -51,7 +51,9 @@ enum {
   PKV_ERR_SHAPE = 3,       /* inconsistent or negative sizes                */
   PKV_ERR_UNSUPPORTED = 4, /* head_dim / dtype / group size not built       */
   PKV_ERR_WORKSPACE = 5,   /* decode workspace missing or too small         */
-  PKV_ERR_LAUNCH = 6       /* the HIP runtime rejected a kernel launch      */
+  PKV_ERR_LAUNCH = 6,      /* the HIP runtime rejected a kernel launch      */
+  PKV_ERR_NO_BLOCKS = 7,   /* block manager: too few free blocks            */
+  PKV_ERR_REQUEST = 8      /* block manager: unknown or duplicate request   */
 };
 
 typedef int32_t pkv_dtype;

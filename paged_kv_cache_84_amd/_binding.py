@@ -51,6 +51,25 @@ _SIGNATURES = {
     "paged_attention_prefill_chunk": (_I32, [_P, _P, _P, _P, _I32, _P, _I32, _P, _P,
                                              _I32, _I32, _I32, _I32, _I32, _I32, _F,
                                              _I32, _I32, _F, _F, _P]),
+    # host block manager (include/pagedkv_blocks.h)
+    "pkv_bm_create": (_I32, [_I32, _P, _I32, _P]),
+    "pkv_bm_destroy": (None, [_P]),
+    "pkv_bm_add_request": (_I32, [_P, _I64, _P, _I32, _P, _I32, _P, _I32, _P]),
+    "pkv_bm_append_tokens": (_I32, [_P, _I64, _P, _I32]),
+    "pkv_bm_allocate": (_I32, [_P, _I64, _I32]),
+    "pkv_bm_append_tokens_batch": (_I32, [_P, _P, _P, _I32]),
+    "pkv_bm_allocate_batch": (_I32, [_P, _P, _P, _I32, _P]),
+    "pkv_bm_fork": (_I32, [_P, _I64, _I64]),
+    "pkv_bm_free_request": (_I32, [_P, _I64]),
+    "pkv_bm_num_free": (_I32, [_P]),
+    "pkv_bm_num_tokens": (_I32, [_P, _I64]),
+    "pkv_bm_ref_count": (_I32, [_P, _I32]),
+    "pkv_bm_table": (_I32, [_P, _I64, _P, _I32]),
+    "pkv_bm_free_queue": (_I32, [_P, _P, _I32]),
+    "pkv_bm_take_copies": (_I32, [_P, _P, _I32]),
+    "pkv_bm_export_tables": (_I32, [_P, _P, _I32, _P, _I32, _I32]),
+    "pkv_block_hash": (None, [_P, _P, _P, _I32, _P, _I32, _P]),
+    "pkv_sha256": (None, [_P, _SZ, _P]),
 }
 EXPORTED = tuple(_SIGNATURES)
 

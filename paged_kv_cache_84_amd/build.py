@@ -52,13 +52,29 @@ def _compile(src, extra, build_dir=BUILD):
     return obj, err.strip()
 
 
+def _compile_host(src, build_dir=BUILD):
+    """Host-only C++ (the block manager): the system C++ compiler."""
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+    cxx = shutil.which("g++") or shutil.which("c++")
+    if cxx is None:
+        raise RuntimeError("no host C++ compiler found")
+    cmd = [cxx, "-O3", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-c", src, "-o", obj]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"{cxx} failed for {src}:\n{res.stderr}")
+    return obj, res.stderr.strip()
+
+
 def build(verbose=False, extra_flags=(), lib=LIB, build_dir=BUILD):
     """Compile and link; `extra_flags` (e.g. -D tuning macros) and the output
     paths can be overridden to build variants side by side."""
     os.makedirs(build_dir, exist_ok=True)
     sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(sources))) as pool:
-        results = list(pool.map(lambda s: _compile(s, extra_flags, build_dir), sources))
+    host_sources = sorted(glob.glob(os.path.join(CSRC, "*.cpp")))
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(sources) + len(host_sources))) as pool:
+        jobs = [pool.submit(_compile, src, extra_flags, build_dir) for src in sources]
+        jobs += [pool.submit(_compile_host, src, build_dir) for src in host_sources]
+        results = [j.result() for j in jobs]
     for obj, err in results:
         if err and verbose:
             print(err, file=sys.stderr)

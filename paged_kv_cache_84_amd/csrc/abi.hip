@@ -13,6 +13,8 @@ extern "C" const char* pkv_status_string(pkv_status status) {
     case PKV_ERR_UNSUPPORTED: return "unsupported head_dim, dtype or group size";
     case PKV_ERR_WORKSPACE: return "decode workspace missing or too small";
     case PKV_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
+    case PKV_ERR_NO_BLOCKS: return "too few free blocks";
+    case PKV_ERR_REQUEST: return "unknown or duplicate request";
     default: return "unknown status";
   }
 }
