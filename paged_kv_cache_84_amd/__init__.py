@@ -10,7 +10,7 @@ The library is loaded on first use; if it is missing or does not load, every
 call raises ``LibraryNotBuilt`` -- there is no fallback implementation.
 """
 
-from . import step  # noqa: F401
+from . import blocks, step  # noqa: F401
 from ._binding import (  # noqa: F401
     BLOCK_SIZE,
     LibraryNotBuilt,
