@@ -13,6 +13,15 @@ The encodings below are the standard ones:
   mantissa bits; exponent field 0 is subnormal; S.1111.111 is NaN; there is no
   infinity; the largest finite magnitude is 448 (code 0x7E).
 
+* int4 per token-head (the pages only name "int4_per_token_head" among the
+  lower-bit --kv-cache-dtype choices, "01. vLLM", section "KV 缓存管理与前缀
+  缓存"; everything else is a reading): every (token, kv head) row of D
+  values has one binary32 scale s = max|x| / 7 and D signed 4-bit codes
+  q = round-half-even(x / s) in [-8, 7] (both divisions in binary32; s = 0
+  and q = 0 for a zero row); a code is stored offset by 8 (u = q + 8, a
+  nibble), element 2i in the low nibble and element 2i+1 in the high nibble
+  of byte i.  The value is (u - 8) * s.
+
 Storage is always handled as raw integers (uint16 for bf16, uint8 for fp8) or
 float32, exactly as the cache holds it; values are produced in float64.
 """
@@ -20,6 +29,7 @@ float32, exactly as the cache holds it; values are produced in float64.
 import numpy as np
 
 F32, BF16, FP8_E4M3 = "f32", "bf16", "fp8_e4m3"
+INT4_PTH = "int4_per_token_head"
 
 BYTES_PER_ELEM = {F32: 4, BF16: 2, FP8_E4M3: 1}
 
@@ -142,3 +152,33 @@ def quantise_to_e4m3(x_f32, scale):
     x = np.asarray(x_f32, dtype=np.float32)
     y = x / np.float32(scale)
     return e4m3_encode(y.astype(np.float32))
+
+
+def int4_quantize_row(x_f32):
+    """One (token, kv head) row of binary32 values -> (packed codes uint8
+    [D/2], binary32 scale), as described in the module docstring."""
+    x = np.asarray(x_f32, dtype=np.float32)
+    assert x.ndim == 1 and x.size % 2 == 0 and np.all(np.isfinite(x))
+    amax = np.float32(np.max(np.abs(x)))
+    s = np.float32(amax / np.float32(7.0))
+    if s == 0:
+        q = np.zeros(x.size, dtype=np.int64)
+    else:
+        q = np.clip(np.rint(x / s), -8, 7).astype(np.int64)
+    u = (q + 8).astype(np.uint8)
+    return (u[0::2] | (u[1::2] << np.uint8(4))).astype(np.uint8), s
+
+
+def int4_unpack_codes(packed):
+    """Packed bytes -> signed codes q in [-8, 7] (int64), element order."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    u = np.empty(packed.shape[:-1] + (2 * packed.shape[-1],), dtype=np.int64)
+    u[..., 0::2] = packed & 0x0F
+    u[..., 1::2] = packed >> 4
+    return u - 8
+
+
+def int4_rows_to_f64(packed_rows, scales):
+    """Rows of packed codes [n][D/2] with their scales [n] -> float64 [n][D]."""
+    q = int4_unpack_codes(packed_rows).astype(np.float64)
+    return q * np.asarray(scales, dtype=np.float32).astype(np.float64)[..., None]

@@ -32,6 +32,8 @@ from .formats import (
     BF16,
     F32,
     FP8_E4M3,
+    int4_quantize_row,
+    int4_rows_to_f64,
     quantise_to_e4m3,
     storage_to_f64,
 )
@@ -375,3 +377,71 @@ def split_attention_row(q, keys, values, softmax_scale, partition_len):
                                       values[start:start + partition_len],
                                       softmax_scale))
     return combine_partitions(states)
+
+
+# --- int4 per token-head caches (encoding: oracle/formats.py) -------------
+# A cache holds packed codes [num_blocks][num_kv_heads][16][D/2] (uint8) and
+# a parallel scale array [num_blocks][num_kv_heads][16] (binary32).
+
+
+def reshape_and_cache_int4(key, value, k_cache, v_cache, k_scales, v_scales, slots,
+                           src_dtype):
+    """reshape_and_cache into int4 caches: each token's K and V row of each
+    kv head is quantised with its own scale.  Returns the four new arrays."""
+    outs = [np.array(a, copy=True) for a in (k_cache, v_cache, k_scales, v_scales)]
+    kc, vc, ksc, vsc = outs
+    for t in range(len(slots)):
+        slot = int(slots[t])
+        if slot < 0:
+            continue
+        block, offset = divmod(slot, BLOCK_SIZE)
+        for h in range(kc.shape[1]):
+            for src, cache, scales in ((key, kc, ksc), (value, vc, vsc)):
+                x = storage_to_f64(src[t, h], src_dtype).astype(np.float32)   # exact
+                cache[block, h, offset], scales[block, h, offset] = int4_quantize_row(x)
+    return kc, vc, ksc, vsc
+
+
+def gather_kv_int4(cache, scales, block_table_row, length, kv_head):
+    """Rows 0..length-1 of one sequence and kv head from an int4 cache, float64."""
+    rows = []
+    for j in range(blocks_needed(length)):
+        block = int(block_table_row[j])
+        n = min(BLOCK_SIZE, length - j * BLOCK_SIZE)
+        rows.append(int4_rows_to_f64(cache[block, kv_head][:n], scales[block, kv_head][:n]))
+    if not rows:
+        return np.zeros((0, 2 * cache.shape[-1]), dtype=np.float64)
+    return np.concatenate(rows, axis=0)
+
+
+def decode_attention_int4(q, q_dtype, k_cache, v_cache, k_scales, v_scales, block_tables,
+                          context_lens, softmax_scale):
+    """decode_attention over int4 caches (float64 [S][Hq][D])."""
+    num_seqs, num_q_heads, head_dim = q.shape
+    num_kv_heads = k_cache.shape[1]
+    group = num_q_heads // num_kv_heads
+    scale = _as_f32_param(softmax_scale)
+    out = np.zeros((num_seqs, num_q_heads, head_dim), dtype=np.float64)
+    for s in range(num_seqs):
+        length = int(context_lens[s])
+        if length == 0:
+            continue
+        for kvh in range(num_kv_heads):
+            keys = gather_kv_int4(k_cache, k_scales, block_tables[s], length, kvh)
+            values = gather_kv_int4(v_cache, v_scales, block_tables[s], length, kvh)
+            for h in range(kvh * group, (kvh + 1) * group):
+                out[s, h] = attention_row(storage_to_f64(q[s, h], q_dtype), keys, values, scale)
+    return out
+
+
+def decode_attention_int4_one(q, q_dtype, k_cache, v_cache, k_scales, v_scales,
+                              block_tables, context_lens, softmax_scale, seq, head):
+    """One (sequence, q head) element of decode_attention_int4."""
+    kvh = head // (q.shape[1] // k_cache.shape[1])
+    length = int(context_lens[seq])
+    if length == 0:
+        return np.zeros(q.shape[-1])
+    keys = gather_kv_int4(k_cache, k_scales, block_tables[seq], length, kvh)
+    values = gather_kv_int4(v_cache, v_scales, block_tables[seq], length, kvh)
+    return attention_row(storage_to_f64(q[seq, head], q_dtype), keys, values,
+                         _as_f32_param(softmax_scale))
