@@ -60,7 +60,9 @@ typedef int32_t pkv_dtype;
 enum {
   PKV_F32 = 0,      /* IEEE binary32                                          */
   PKV_BF16 = 1,     /* bfloat16 (upper half of a binary32)                    */
-  PKV_FP8_E4M3 = 2  /* OCP fp8 E4M3 ("fn": no inf, max 448), cache dtype only */
+  PKV_FP8_E4M3 = 2, /* OCP fp8 E4M3 ("fn": no inf, max 448), cache dtype only */
+  PKV_INT4 = 3      /* int4 per token-head codes (see reshape_and_cache_int4),
+                       cache dtype only, with separate per-row scale arrays    */
 };
 
 #define PKV_BLOCK_SIZE 16
@@ -286,6 +288,52 @@ pkv_status paged_attention_prefill_chunk(void* out, const void* query,
                                          pkv_dtype q_dtype, pkv_dtype kv_dtype,
                                          float k_scale, float v_scale,
                                          void* stream);
+
+/*
+ * int4 per token-head KV cache (PKV_INT4).  The pages list
+ * "int4_per_token_head" among the lower-bit --kv-cache-dtype formats ("01.
+ * vLLM：从分页 KV 起家的通用推理引擎", section "KV 缓存管理与前缀缓存", the
+ * --kv-cache-dtype row) and fix nothing else; the encoding here: every
+ * (token, kv head) row of head_dim values x has one binary32 scale
+ * s = max|x| / 7 and codes q = round-half-even(x / s) in [-8, 7] (both
+ * divisions in binary32; a zero row has s = 0, q = 0), stored as nibbles
+ * u = q + 8, element 2i in the low nibble of byte i.  Its value is
+ * (u - 8) * s.  Layouts:
+ *   k_cache, v_cache   uint8 [num_blocks][num_kv_heads][16][head_dim / 2]
+ *   k_scales, v_scales float [num_blocks][num_kv_heads][16]
+ * A quarter of bf16's bytes per element, plus 4 bytes per row.
+ *
+ * reshape_and_cache_int4 -- reshape_and_cache into int4 caches: each
+ * scheduled token's K and V rows are quantised as above (from bf16 or fp32
+ * sources, finite values) and written with their scales at the slot; a
+ * negative slot skips the token.  head_dim even and at most 128.
+ */
+pkv_status reshape_and_cache_int4(const void* key, const void* value, void* k_cache,
+                                  void* v_cache, float* k_scales, float* v_scales,
+                                  const int64_t* slot_mapping, int32_t num_tokens,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                                  pkv_dtype src_dtype, void* stream);
+
+/*
+ * paged_attention_decode_int4 -- paged_attention_decode over int4 caches:
+ * the result is attention over the rows' values (u - 8) * s.  The kernel
+ * never widens a row with its scale: a code enters the products as the bf16
+ * 128 + u, the key's scale multiplies its score and the value's scale its
+ * weight, and the constant offset is taken out of both sums afterwards.
+ * Same work split, workspace (paged_attention_decode_workspace_size) and
+ * merge as paged_attention_decode.  Supported: bf16 queries, head_dim 128,
+ * group <= 8.  Scale arrays 16-byte aligned.
+ */
+pkv_status paged_attention_decode_int4(void* out, const void* query, const void* k_cache,
+                                       const void* v_cache, const float* k_scales,
+                                       const float* v_scales, int32_t num_blocks,
+                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                       const int32_t* context_lens, int32_t num_seqs,
+                                       int32_t max_context_len, int32_t num_q_heads,
+                                       int32_t num_kv_heads, int32_t head_dim,
+                                       float softmax_scale, pkv_dtype q_dtype,
+                                       int32_t partition_tokens, void* workspace,
+                                       size_t workspace_bytes, void* stream);
 
 /*
  * paged_attention_varlen -- the attention of one whole engine step in one

@@ -24,8 +24,10 @@ from ._binding import (  # noqa: F401
     library_path,
     varlen_workspace_size,
     paged_attention_decode,
+    paged_attention_decode_int4,
     paged_attention_prefill_chunk,
     paged_attention_varlen,
     reshape_and_cache,
+    reshape_and_cache_int4,
     swap_blocks,
 )

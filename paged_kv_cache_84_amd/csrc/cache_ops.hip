@@ -120,6 +120,51 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
   }
 }
 
+// ------------------------------------------------- int4 per token-head write
+// One wave per (token, K|V, kv head) row: lane L quantises elements 2L and
+// 2L + 1.  s = max|x| / 7 (a wave-wide max, then a binary32 division),
+// q = round half to even of x / s, stored as the nibbles q + 8, element 2L in
+// the low nibble of byte L; a zero row gets s = 0 and q = 0.
+
+PKV_DEVICE float src_to_f32(uint16_t bits) { return bf16_to_f32(bits); }
+PKV_DEVICE float src_to_f32(float v) { return v; }
+
+template <typename Src>
+__global__ __launch_bounds__(256) void reshape_and_cache_int4_kernel(
+    const typename Src::storage* __restrict__ key,
+    const typename Src::storage* __restrict__ value, uint8_t* __restrict__ k_cache,
+    uint8_t* __restrict__ v_cache, float* __restrict__ k_scales, float* __restrict__ v_scales,
+    const int64_t* __restrict__ slots, int32_t num_kv_heads, int32_t head_dim,
+    int32_t num_blocks) {
+  const int t = blockIdx.x;
+  const int64_t slot = slots[t];
+  if (slot < 0 || slot >= int64_t(num_blocks) * kBlock) return;
+  const int64_t block = slot / kBlock;
+  const int offset = int(slot % kBlock);
+  const int lane = lane_id();
+  const int wave = int(threadIdx.x) / kWave;
+  const bool on = 2 * lane < head_dim;
+  for (int row = wave; row < 2 * num_kv_heads; row += int(blockDim.x) / kWave) {
+    const bool is_v = row >= num_kv_heads;
+    const int h = is_v ? row - num_kv_heads : row;
+    const typename Src::storage* src = (is_v ? value : key) + (int64_t(t) * num_kv_heads + h) * head_dim;
+    const float x0 = on ? src_to_f32(src[2 * lane]) : 0.f;
+    const float x1 = on ? src_to_f32(src[2 * lane + 1]) : 0.f;
+    float amax = fmaxf(fabsf(x0), fabsf(x1));
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, shfl_xor(amax, o));
+    const float s = amax / 7.0f;
+    int q0 = 0, q1 = 0;
+    if (s > 0.f) {
+      q0 = min(7, max(-8, int(rintf(x0 / s))));
+      q1 = min(7, max(-8, int(rintf(x1 / s))));
+    }
+    const int64_t r = (block * num_kv_heads + h) * kBlock + offset;
+    if (on) (is_v ? v_cache : k_cache)[r * (head_dim / 2) + lane] = uint8_t((q0 + 8) | ((q1 + 8) << 4));
+    if (lane == 0) (is_v ? v_scales : k_scales)[r] = s;
+  }
+}
+
 // ------------------------------------------------------------ block copies
 
 constexpr int kMaxLayersPerLaunch = 64;
@@ -249,6 +294,38 @@ extern "C" pkv_status reshape_and_cache(const void* key, const void* value,
                                   num_tokens, num_kv_heads, head_dim, num_blocks,
                                   k_scale, v_scale, stream);
   return PKV_ERR_UNSUPPORTED;
+}
+
+extern "C" pkv_status reshape_and_cache_int4(const void* key, const void* value,
+                                             void* k_cache, void* v_cache, float* k_scales,
+                                             float* v_scales, const int64_t* slot_mapping,
+                                             int32_t num_tokens, int32_t num_kv_heads,
+                                             int32_t head_dim, int32_t num_blocks,
+                                             pkv_dtype src_dtype, void* stream) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || num_blocks < 0)
+    return PKV_ERR_SHAPE;
+  if (head_dim % 2 != 0 || head_dim > 2 * kWave) return PKV_ERR_UNSUPPORTED;
+  if (src_dtype != PKV_BF16 && src_dtype != PKV_F32) return PKV_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PKV_OK;
+  if (!key || !value || !k_cache || !v_cache || !k_scales || !v_scales || !slot_mapping)
+    return PKV_ERR_NULL;
+  if (!aligned(key, 16) || !aligned(value, 16) || !aligned(k_cache, 16) ||
+      !aligned(v_cache, 16) || !aligned(k_scales, 4) || !aligned(v_scales, 4) ||
+      !aligned(slot_mapping, 8))
+    return PKV_ERR_ALIGN;
+  auto* kc = static_cast<uint8_t*>(k_cache);
+  auto* vc = static_cast<uint8_t*>(v_cache);
+  if (src_dtype == PKV_BF16)
+    hipLaunchKernelGGL(reshape_and_cache_int4_kernel<BF16>, dim3(num_tokens), dim3(256), 0,
+                       as_stream(stream), static_cast<const uint16_t*>(key),
+                       static_cast<const uint16_t*>(value), kc, vc, k_scales, v_scales,
+                       slot_mapping, num_kv_heads, head_dim, num_blocks);
+  else
+    hipLaunchKernelGGL(reshape_and_cache_int4_kernel<F32>, dim3(num_tokens), dim3(256), 0,
+                       as_stream(stream), static_cast<const float*>(key),
+                       static_cast<const float*>(value), kc, vc, k_scales, v_scales,
+                       slot_mapping, num_kv_heads, head_dim, num_blocks);
+  return launch_status();
 }
 
 extern "C" pkv_status copy_blocks(void* const* k_caches, void* const* v_caches,

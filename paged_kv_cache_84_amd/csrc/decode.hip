@@ -815,6 +815,50 @@ pkv_status launch_prefill_rows(const PrefillArgs& a) {
 
 using namespace pkv;
 
+namespace pkv {
+
+// The matrix-core decode: the chunk kernel, then the merge of split
+// sequences.  Fixed partitions are walked several to a wave, so that a short
+// partition does not cost a wave start (and the wave's loads run on across
+// the partitions' boundaries).  A bf16 block keeps one wave per SIMD busy; an
+// fp8 or int4 block carries a half or a quarter of the bytes for the same
+// products, so those caches get PKV_FP8_WAVES_PER_SIMD waves per SIMD.
+#ifndef PKV_FP8_WAVES_PER_SIMD
+#define PKV_FP8_WAVES_PER_SIMD 3
+#endif
+static pkv_status mfma_decode(void* out, const void* query, const void* k_cache,
+                              const void* v_cache, const float* k_scales,
+                              const float* v_scales, int32_t num_blocks,
+                              const int32_t* block_tables, int32_t max_blocks_per_seq,
+                              const int32_t* context_lens, int32_t num_seqs,
+                              int32_t max_context_len, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, float scale_log2,
+                              pkv_dtype kv_dtype, float v_scale, const DecodePlan& lay,
+                              void* workspace, void* stream) {
+  const int64_t target = int64_t(PKV_DECODE_TARGET_WAVES) *
+                         (kv_dtype == PKV_BF16 ? 1 : PKV_FP8_WAVES_PER_SIMD);
+  const int64_t per_wave =
+      lay.fixed_chunk > 0
+          ? std::max<int64_t>(1, (int64_t(lay.num_chunks) * num_kv_heads + target - 1) / target)
+          : 1;
+  DecodeMfmaArgs a{out, query, k_cache, v_cache, num_blocks, block_tables,
+                   max_blocks_per_seq, context_lens, num_seqs, max_context_len,
+                   num_q_heads, num_kv_heads, head_dim, kv_dtype, scale_log2, v_scale,
+                   lay.num_chunks, lay.fixed_chunk, int32_t(per_wave),
+                   static_cast<float*>(workspace),
+                   reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.out_bytes),
+                   stream, k_scales, v_scales};
+  if (launch_decode_mfma(a) != PKV_OK) return PKV_ERR_LAUNCH;
+  hipStream_t st = as_stream(stream);
+  return head_dim == 64
+             ? launch_merge<BF16, 64>(out, context_lens, num_seqs, max_context_len,
+                                      num_q_heads, v_scale, lay, workspace, st)
+             : launch_merge<BF16, 128>(out, context_lens, num_seqs, max_context_len,
+                                       num_q_heads, v_scale, lay, workspace, st);
+}
+
+}  // namespace pkv
+
 extern "C" int32_t paged_attention_decode_num_chunks(int32_t num_seqs,
                                                      int32_t num_q_heads,
                                                      int32_t num_kv_heads,
@@ -882,36 +926,11 @@ extern "C" pkv_status paged_attention_decode(
   if (!aligned(workspace, 16)) return PKV_ERR_ALIGN;
 
 #if PKV_DECODE_USE_MFMA
-  if (decode_mfma_supported(q_dtype, kv_dtype, head_dim, group)) {
-    // Fixed partitions are walked several to a wave, so that a short
-    // partition does not cost a wave start (and the wave's loads run on
-    // across the partitions' boundaries).  A bf16 block keeps one wave per
-    // SIMD busy; an fp8 block carries half the bytes for the same products,
-    // so fp8 caches get PKV_FP8_WAVES_PER_SIMD waves per SIMD.
-#ifndef PKV_FP8_WAVES_PER_SIMD
-#define PKV_FP8_WAVES_PER_SIMD 3
-#endif
-    const int64_t target = int64_t(PKV_DECODE_TARGET_WAVES) *
-                           (kv_dtype == PKV_FP8_E4M3 ? PKV_FP8_WAVES_PER_SIMD : 1);
-    const int64_t per_wave =
-        lay.fixed_chunk > 0
-            ? std::max<int64_t>(1, (int64_t(lay.num_chunks) * num_kv_heads + target - 1) / target)
-            : 1;
-    DecodeMfmaArgs a{out, query, k_cache, v_cache, num_blocks, block_tables,
-                     max_blocks_per_seq, context_lens, num_seqs, max_context_len,
-                     num_q_heads, num_kv_heads, head_dim, kv_dtype,
-                     softmax_scale * k_scale * kLog2e, v_scale, lay.num_chunks,
-                     lay.fixed_chunk, int32_t(per_wave), static_cast<float*>(workspace),
-                     reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.out_bytes),
-                     stream};
-    if (launch_decode_mfma(a) != PKV_OK) return PKV_ERR_LAUNCH;
-    hipStream_t st = as_stream(stream);
-    return head_dim == 64
-               ? launch_merge<BF16, 64>(out, context_lens, num_seqs, max_context_len,
-                                        num_q_heads, v_scale, lay, workspace, st)
-               : launch_merge<BF16, 128>(out, context_lens, num_seqs, max_context_len,
-                                         num_q_heads, v_scale, lay, workspace, st);
-  }
+  if (decode_mfma_supported(q_dtype, kv_dtype, head_dim, group))
+    return mfma_decode(out, query, k_cache, v_cache, nullptr, nullptr, num_blocks, block_tables,
+                       max_blocks_per_seq, context_lens, num_seqs, max_context_len,
+                       num_q_heads, num_kv_heads, head_dim, softmax_scale * k_scale * kLog2e,
+                       kv_dtype, v_scale, lay, workspace, stream);
 #endif
   // fp32 q with head_dim 128 keeps at most two heads per wave (registers)
   const int max_gw = (f32 && head_dim == 128) ? 2 : PKV_DECODE_MAX_HEADS_PER_WAVE;
@@ -933,4 +952,41 @@ extern "C" pkv_status paged_attention_decode(
   return head_dim == 64 ? dispatch_gw<BF16, FP8, 64>(PKV_DECODE_ARGS)
                         : dispatch_gw<BF16, FP8, 128>(PKV_DECODE_ARGS);
 #undef PKV_DECODE_ARGS
+}
+
+extern "C" pkv_status paged_attention_decode_int4(
+    void* out, const void* query, const void* k_cache, const void* v_cache,
+    const float* k_scales, const float* v_scales, int32_t num_blocks,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+    int32_t num_seqs, int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, float softmax_scale, pkv_dtype q_dtype, int32_t partition_tokens,
+    void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_seqs < 0 || num_blocks < 0 || max_blocks_per_seq < 0 || max_context_len < 0 ||
+      num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0)
+    return PKV_ERR_SHAPE;
+  if (num_q_heads % num_kv_heads != 0) return PKV_ERR_SHAPE;
+  if (int64_t(max_blocks_per_seq) * kBlock < max_context_len) return PKV_ERR_SHAPE;
+  const int group = num_q_heads / num_kv_heads;
+  if (group > 8 || head_dim != 128 || q_dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+  if (partition_tokens < 0 || partition_tokens % kBlock != 0) return PKV_ERR_SHAPE;
+  if (num_seqs == 0) return PKV_OK;
+  if (num_blocks == 0) return PKV_ERR_SHAPE;
+  if (!out || !query || !k_cache || !v_cache || !k_scales || !v_scales || !block_tables ||
+      !context_lens)
+    return PKV_ERR_NULL;
+  if (!aligned(out, 16) || !aligned(query, 16) || !aligned(k_cache, 16) ||
+      !aligned(v_cache, 16) || !aligned(k_scales, 16) || !aligned(v_scales, 16) ||
+      !aligned(block_tables, 4) || !aligned(context_lens, 4))
+    return PKV_ERR_ALIGN;
+  DecodePlan lay;
+  if (!make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                 partition_tokens, lay) ||
+      int64_t(num_seqs) * num_q_heads > 0x7fffffff)
+    return PKV_ERR_SHAPE;
+  if (!workspace || workspace_bytes < lay.out_bytes + lay.ml_bytes) return PKV_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return PKV_ERR_ALIGN;
+  return mfma_decode(out, query, k_cache, v_cache, k_scales, v_scales, num_blocks,
+                     block_tables, max_blocks_per_seq, context_lens, num_seqs, max_context_len,
+                     num_q_heads, num_kv_heads, head_dim, softmax_scale * kLog2e, PKV_INT4,
+                     1.0f, lay, workspace, stream);
 }

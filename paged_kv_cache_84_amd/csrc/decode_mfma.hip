@@ -62,16 +62,52 @@ PKV_DEVICE uint32_t pack_bf16_rne(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// int4 per token-head cache: two codes u = q + 8 per byte (element 2i in the
+// low nibble), the binary32 scale of each (block, kv head, slot) row in a
+// separate array.  `bytes` is 0 so that byte-based formulas cannot be used
+// for it by mistake.
+struct INT4 {
+  using storage = uint8_t;
+  static constexpr int bytes = 0;
+};
+template <typename KVT>
+constexpr bool kInt4 = std::is_same<KVT, INT4>::value;
+template <typename KVT>
+constexpr int kElemBits = kInt4<KVT> ? 4 : 8 * KVT::bytes;
+
+// 136 in bf16: an int4 element enters the products as 128 + u = 136 + q (a
+// bf16 with the nibble in its low mantissa bits), and 136 * (sum of the
+// other operand) is subtracted afterwards.
+constexpr uint32_t kBf16x2_136 = 0x43084308u;
+constexpr float kInt4Offset = 136.0f;
+
+// Eight nibbles (elements 0..7 of a little-endian dword) -> four dwords of
+// bf16 pairs 128 + u: dword e holds elements 2e (low half) and 2e + 1.
+PKV_DEVICE u32x4 int4x8_to_bf16_offset(uint32_t w) {
+  const uint32_t lo = w & 0x0F0F0F0Fu;           // elements 0, 2, 4, 6 (bytes 0..3)
+  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;    // elements 1, 3, 5, 7
+  u32x4 o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    // v_perm: selector byte e picks lo's byte e, 4 + e picks hi's byte e,
+    // 0x0C gives a zero byte
+    const uint32_t sel = 0x0C000C00u | (uint32_t(4 + e) << 16) | uint32_t(e);
+    o[e] = __builtin_amdgcn_perm(hi, lo, sel) | 0x43004300u;
+  }
+  return o;
+}
+
 template <typename KVT, int D>
 struct MGeom {
   static constexpr int kKSteps = D / 32;               // QK products per block
   static constexpr int kMTiles = D / 16;               // 16-dim slices of V
-  static constexpr int kRowBytes = D * KVT::bytes;     // one cache row
+  static constexpr int kRowBytes = D * kElemBits<KVT> / 8;   // one cache row
   static constexpr int kTileBytes = kBlock * kRowBytes;
   static constexpr int kVLoads = kTileBytes / (kWave * 16);  // 16-byte V pieces per lane
-  static constexpr int kKLoads = KVT::bytes == 2 ? kKSteps : kKSteps / 2;
+  static constexpr int kKLoads = kInt4<KVT> ? kKSteps / 4 : KVT::bytes == 2 ? kKSteps : kKSteps / 2;
   static constexpr int kVStride = D * 2 + 32;          // LDS bytes per staged bf16 V row
   static_assert(kKSteps >= 2 && kVLoads >= 1, "unsupported head size");
+  static_assert(!kInt4<KVT> || D == 128, "int4 caches: head_dim 128");
 };
 
 // First dim of the 8 consecutive dims that lane group j feeds to QK product ks
@@ -79,17 +115,26 @@ struct MGeom {
 // each lane's 16-byte load cover two products).
 template <typename KVT>
 PKV_DEVICE int qk_dim(int j, int ks) {
-  return KVT::bytes == 2 ? 8 * j + 32 * ks : 16 * j + 64 * (ks / 2) + 8 * (ks % 2);
+  if constexpr (kInt4<KVT>) return 32 * j + 8 * ks;   // one 16-byte load = 32 dims
+  else return KVT::bytes == 2 ? 8 * j + 32 * ks : 16 * j + 64 * (ks / 2) + 8 * (ks % 2);
 }
 
 template <typename KVT, int D>
 struct KRegs {
   u32x4 v[MGeom<KVT, D>::kKLoads];
+  u32x4 sc;       // int4: the scales of this lane's four keys
 };
 template <typename KVT, int D>
 struct VRegs {
   u32x4 v[MGeom<KVT, D>::kVLoads];
+  u32x4 sc;       // int4: the scales of this lane's four keys
 };
+
+// int4: the scales of keys 4 (lane/16) .. + 3 of one (block, kv head) row
+// set of a scale array (16 floats per (block, kv head)).
+PKV_DEVICE u32x4 load_scales(const float* row16, int lane) {
+  return buffer_load16(tile_resource(row16, kBlock * 4), uint32_t((lane / 16) * 16));
+}
 
 template <typename KVT, int D>
 PKV_DEVICE void load_k(KRegs<KVT, D>& r, const typename KVT::storage* tile, int lane) {
@@ -111,7 +156,9 @@ PKV_DEVICE void load_v(VRegs<KVT, D>& r, const typename KVT::storage* tile, int 
 // The A operand of QK product ks from the K registers.
 template <typename KVT, int D>
 PKV_DEVICE u32x4 k_operand(const KRegs<KVT, D>& r, int ks) {
-  if constexpr (KVT::bytes == 2) {
+  if constexpr (kInt4<KVT>) {
+    return int4x8_to_bf16_offset(r.v[0][ks]);
+  } else if constexpr (KVT::bytes == 2) {
     return r.v[ks];
   } else {
     const u32x4 x = r.v[ks / 2];
@@ -128,6 +175,16 @@ PKV_DEVICE u32x4 k_operand(const KRegs<KVT, D>& r, int ks) {
 template <typename KVT, int D>
 PKV_DEVICE void stage_v(VRegs<KVT, D>& r, char* vl, int lane, int rows) {
   using M = MGeom<KVT, D>;
+  if constexpr (kInt4<KVT>) {
+    // lane L holds dims 32 (L%4) .. + 31 of key L/4; every code is a finite
+    // bf16 (128 + u), and rows past `rows` get zero weight, so nothing is
+    // cleared here
+    char* dst = vl + (lane / 4) * M::kVStride + (lane % 4) * 64;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      *reinterpret_cast<u32x4*>(dst + 16 * w) = int4x8_to_bf16_offset(r.v[0][w]);
+    return;
+  }
   if (rows < kBlock) {
 #pragma unroll
     for (int i = 0; i < M::kVLoads; ++i)
@@ -137,7 +194,7 @@ PKV_DEVICE void stage_v(VRegs<KVT, D>& r, char* vl, int lane, int rows) {
   for (int i = 0; i < M::kVLoads; ++i) {
     const int o = lane * 16 + i * 1024;         // byte offset in the cache tile
     const int row = o / M::kRowBytes;
-    const int col = (o % M::kRowBytes) / KVT::bytes;
+    const int col = (o % M::kRowBytes) / (kInt4<KVT> ? 1 : KVT::bytes);
     char* dst = vl + row * M::kVStride + col * 2;
     if constexpr (KVT::bytes == 2) {
       *reinterpret_cast<u32x4*>(dst) = r.v[i];
@@ -182,7 +239,8 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
     const int32_t* __restrict__ context_lens, int32_t num_seqs, int32_t max_len,
     int32_t num_q_heads, int32_t num_kv_heads, int32_t group, float scale_log2,
     float v_scale, int32_t num_chunks, int32_t fixed_chunk, int32_t chunks_per_wave,
-    float* __restrict__ rec_out, float* __restrict__ rec_ml) {
+    float* __restrict__ rec_out, float* __restrict__ rec_ml,
+    const float* __restrict__ k_scales, const float* __restrict__ v_scales) {
   using M = MGeom<KVT, D>;
   __shared__ __align__(16) char vl[kBlock * M::kVStride];
   const int kvh = blockIdx.x % num_kv_heads;
@@ -201,12 +259,16 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
   if (b0 >= sc.total) return;
   const int b1 = min(b0 + chunks_per_wave * c, sc.total);
 
-  const int64_t head_stride = int64_t(kBlock) * D;
+  const int64_t head_stride = int64_t(kBlock) * M::kRowBytes /
+                              int64_t(sizeof(typename KVT::storage));
   const int64_t block_stride = int64_t(num_kv_heads) * head_stride;
   auto tile = [&](const typename KVT::storage* base, int32_t b) {
     return base + int64_t(b) * block_stride + int64_t(kvh) * head_stride;
   };
   auto valid = [&](int32_t b) { return b >= 0 && b < num_blocks; };
+  auto scale_row = [&](const float* base, int32_t b) {
+    return base + (int64_t(b) * num_kv_heads + kvh) * kBlock;
+  };
   auto table_id = [&](const SeqCursor& q, int x) -> int32_t {
     const int i = x - q.before;
     return i < max_blocks ? load_scalar(block_tables, int64_t(q.s) * max_blocks + i) : -1;
@@ -236,6 +298,16 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
   SeqCursor lc = cc, ic = cc;
   u32x4 qb[M::kKSteps], qn[M::kKSteps];
   load_q(cc.s, qb);
+  // int4: 136 * (sum of the column's query), the offset's share of S^T
+  auto offset_share = [&]() {
+    f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < M::kKSteps; ++ks)
+      c = mfma_k32(u32x4{kBf16x2_136, kBf16x2_136, kBf16x2_136, kBf16x2_136}, qb[ks], c);
+    return c[0];
+  };
+  float kcorr = 0.f;
+  if constexpr (kInt4<KVT>) kcorr = offset_share();
   int32_t id_cur = table_id(cc, b0);
   int32_t id_next = -1;
   if (b0 + 1 < b1) {
@@ -248,8 +320,10 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
   // V before K, the order of the loop's own loads, so that each wait inside
   // the loop covers exactly the pieces it needs
   load_v<KVT, D>(vr, tile(v_cache, b_any), lane);
+  if constexpr (kInt4<KVT>) vr.sc = load_scales(scale_row(v_scales, b_any), lane);
   __builtin_amdgcn_sched_barrier(0);
   load_k<KVT, D>(kr, tile(k_cache, b_any), lane);
+  if constexpr (kInt4<KVT>) kr.sc = load_scales(scale_row(k_scales, b_any), lane);
   __builtin_amdgcn_sched_barrier(0);
 
   f32x4_t acc[M::kMTiles];
@@ -258,6 +332,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
   // running max starts finite: a fully masked block then gives weights
   // 2^-inf = 0 instead of 2^(-inf + inf)
   float m = kNoMax, l = 0.f;
+  float lp = 0.f;                     // int4: sum of the weights the products used
   int seg_start = b0;
   int chunk = b0 / c;                 // chunk of the current segment
   int chunk_end = b0 + c;             // its end
@@ -269,8 +344,10 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
     const bool more = x + 1 < b1;
     const int32_t bn = (more && valid(id_next)) ? id_next : b_any;
     stage_v<KVT, D>(vr, vl, lane, rows);
+    const u32x4 vsc = vr.sc;          // int4: this block's V scales (before the reload)
     __builtin_amdgcn_sched_barrier(0);
     load_v<KVT, D>(vr, tile(v_cache, bn), lane);
+    if constexpr (kInt4<KVT>) vr.sc = load_scales(scale_row(v_scales, bn), lane);
     __builtin_amdgcn_sched_barrier(0);
     // Q of a sequence entered by the next block
     const bool new_seq = more && x + 1 >= lc.before + lc.n;
@@ -289,13 +366,19 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
     f32x4_t st = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < M::kKSteps; ++ks) st = mfma_k32(k_operand<KVT, D>(kr, ks), qb[ks], st);
+    const u32x4 ksc = kr.sc;          // int4: this block's K scales (before the reload)
     load_k<KVT, D>(kr, tile(k_cache, bn), lane);
+    if constexpr (kInt4<KVT>) kr.sc = load_scales(scale_row(k_scales, bn), lane);
     // online softmax over this lane's 4 keys of its head
     float sv[4];
     bool raise = false;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float t = st[r] * scale_log2;
+      float t;
+      if constexpr (kInt4<KVT>)
+        t = (st[r] - kcorr) * __uint_as_float(ksc[r]) * scale_log2;
+      else
+        t = st[r] * scale_log2;
       sv[r] = 4 * j + r < rows ? t : -INFINITY;
       raise |= sv[r] > m + kRaiseM;
     }
@@ -307,6 +390,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
       const float alpha = fast_exp2(m - mn);
       m = mn;
       l *= alpha;
+      if constexpr (kInt4<KVT>) lp *= alpha;
 #pragma unroll
       for (int mt = 0; mt < M::kMTiles; ++mt) acc[mt] *= alpha;
     }
@@ -314,6 +398,12 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
 #pragma unroll
     for (int r = 0; r < 4; ++r) p[r] = fast_exp2(sv[r] - m);
     l += (p[0] + p[1]) + (p[2] + p[3]);
+    // int4: the V scale of each key joins its weight (masked keys keep
+    // weight 0 whatever their scale slot holds)
+    if constexpr (kInt4<KVT>) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p[r] = 4 * j + r < rows ? p[r] * __uint_as_float(vsc[r]) : 0.f;
+    }
     // P^T = hi + lo, both bf16
     uint32_t hi[2], lo[2];
 #pragma unroll
@@ -322,6 +412,9 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
       hi[w] = (b & 0xffff0000u) | (a >> 16);
       lo[w] = pack_bf16_rne(p[2 * w] - __uint_as_float(a & 0xffff0000u),
                             p[2 * w + 1] - __uint_as_float(b & 0xffff0000u));
+      if constexpr (kInt4<KVT>)   // the weights exactly as the products see them
+        lp += (__uint_as_float(a & 0xffff0000u) + __uint_as_float(lo[w] << 16)) +
+              (__uint_as_float(b & 0xffff0000u) + __uint_as_float(lo[w] & 0xffff0000u));
     }
     const i16x4_t phi = __builtin_bit_cast(i16x4_t, uint2{hi[0], hi[1]});
     const i16x4_t plo = __builtin_bit_cast(i16x4_t, uint2{lo[0], lo[1]});
@@ -341,6 +434,13 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
       // sum of weights of each head over the four lane groups
       float lt = l + shfl_xor(l, 16);
       lt += shfl_xor(lt, 32);
+      if constexpr (kInt4<KVT>) {
+        // remove the offset: O = sum p (136 + q) - 136 sum p
+        float lpt = lp + shfl_xor(lp, 16);
+        lpt += shfl_xor(lpt, 32);
+#pragma unroll
+        for (int mt = 0; mt < M::kMTiles; ++mt) acc[mt] -= kInt4Offset * lpt;
+      }
       if (head_ok) {
         if (seg_start == cc.before && x + 1 == seq_end) {
           const float f = v_scale / lt;
@@ -366,6 +466,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
       for (int mt = 0; mt < M::kMTiles; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       m = kNoMax;
       l = 0.f;
+      lp = 0.f;
       seg_start = x + 1;
       if (x + 1 == chunk_end) {
         ++chunk;
@@ -375,6 +476,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
         cursor_to(cc, x + 1, sc, context_lens, max_len);
 #pragma unroll
         for (int ks = 0; ks < M::kKSteps; ++ks) qb[ks] = qn[ks];
+        if constexpr (kInt4<KVT>) kcorr = offset_share();
       }
     }
   }
@@ -391,16 +493,19 @@ static pkv_status launch_one(const DecodeMfmaArgs& a) {
                      a.block_tables, a.max_blocks, a.context_lens, a.num_seqs, a.max_len,
                      a.num_q_heads, a.num_kv_heads, a.num_q_heads / a.num_kv_heads,
                      a.scale_log2, a.v_scale, a.num_chunks, a.fixed_chunk,
-                     a.chunks_per_wave, a.rec_out, a.rec_ml);
+                     a.chunks_per_wave, a.rec_out, a.rec_ml, a.k_scales, a.v_scales);
   return launch_status();
 }
 
 bool decode_mfma_supported(pkv_dtype q_dtype, pkv_dtype kv_dtype, int head_dim, int group) {
+  if (kv_dtype == PKV_INT4)
+    return q_dtype == PKV_BF16 && head_dim == 128 && group >= 1 && group <= 16;
   return q_dtype == PKV_BF16 && (kv_dtype == PKV_BF16 || kv_dtype == PKV_FP8_E4M3) &&
          (head_dim == 64 || head_dim == 128) && group >= 1 && group <= 16;
 }
 
 pkv_status launch_decode_mfma(const DecodeMfmaArgs& a) {
+  if (a.kv_dtype == PKV_INT4) return launch_one<INT4, 128>(a);
   if (a.kv_dtype == PKV_BF16)
     return a.head_dim == 64 ? launch_one<BF16, 64>(a) : launch_one<BF16, 128>(a);
   return a.head_dim == 64 ? launch_one<FP8, 64>(a) : launch_one<FP8, 128>(a);

@@ -77,3 +77,18 @@ def storage_dtype_of(t):
     if t.dtype in (torch.uint8, torch.float8_e4m3fn):
         return FP8_E4M3
     raise ValueError(t.dtype)
+
+
+def int4_codes(shape, config_id, purpose, device="cpu"):
+    """Packed int4 codes: uniform random bytes (every byte is two valid
+    codes), uint8 ``shape`` (the last dim is head_dim / 2)."""
+    g = value_generator(config_id, purpose, device)
+    return torch.randint(0, 256, shape, generator=g, device=device, dtype=torch.int32).to(
+        torch.uint8)
+
+
+def int4_scales(shape, config_id, purpose, device="cpu", lo=0.05, hi=0.6):
+    """Per-row int4 scales: float32 uniform in [lo, hi) (max|x| / 7 of N(0, 1)
+    rows of 128 values lies near 0.4)."""
+    g = value_generator(config_id, purpose, device)
+    return lo + (hi - lo) * torch.rand(shape, generator=g, device=device, dtype=torch.float32)

@@ -218,3 +218,43 @@ def test_varlen_errors(lib):
     assert call(a18=None) == WS
     assert call(a19=need - 1) == WS
     assert call(a18=p + 8) == ALIGN
+
+
+def test_int4_errors(lib):
+    f = lib.reshape_and_cache_int4
+    p = 0x100000
+    base = [p, p, p, p, p, p, p, 4, 8, 128, 100, BF16, None]
+
+    def call(**k):
+        a = list(base)
+        for i, v in k.items():
+            a[int(i[1:])] = v
+        return f(*a)
+
+    assert call(a7=0) == OK
+    assert call(a4=None) == NULL
+    assert call(a0=p + 4) == ALIGN
+    assert call(a9=130) == UNSUP          # more than 128 elements per row
+    assert call(a9=63) == UNSUP           # odd
+    assert call(a11=FP8) == UNSUP
+    assert call(a8=0) == SHAPE
+    d = lib.paged_attention_decode_int4
+    need = lib.paged_attention_decode_workspace_size(4, 32, 8, 128, 1000, 0)
+    dbase = [p, p, p, p, p, p, 100, p, 63, p, 4, 1000, 32, 8, 128, 0.088, BF16, 0, p, need,
+             None]
+
+    def dcall(**k):
+        a = list(dbase)
+        for i, v in k.items():
+            a[int(i[1:])] = v
+        return d(*a)
+
+    assert dcall(a10=0) == OK
+    assert dcall(a4=None) == NULL
+    assert dcall(a5=p + 4) == ALIGN
+    assert dcall(a14=64) == UNSUP
+    assert dcall(a16=F32) == UNSUP
+    assert dcall(a12=72) == UNSUP         # group 9
+    assert dcall(a8=62) == SHAPE          # 992 tokens < max_context_len
+    assert dcall(a17=100) == SHAPE        # partition not a multiple of 16
+    assert dcall(a19=need - 1) == WS
