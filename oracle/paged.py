@@ -445,3 +445,55 @@ def decode_attention_int4_one(q, q_dtype, k_cache, v_cache, k_scales, v_scales,
     values = gather_kv_int4(v_cache, v_scales, block_tables[seq], length, kvh)
     return attention_row(storage_to_f64(q[seq, head], q_dtype), keys, values,
                          _as_f32_param(softmax_scale))
+
+
+# --- sliding-window decode --------------------------------------------------
+# For sliding-window layers only the most recent tokens are attended to, and
+# the blocks that fall out of the window can be released early ("01. vLLM",
+# section "KV 缓存管理与前缀缓存", the hybrid KV cache manager paragraph).
+# Reading: a query at position L-1 sees the `window` positions
+# max(0, L - window) .. L-1, its own included.
+
+
+def window_start(length, window):
+    """First position a decode query of a length-`length` sequence sees."""
+    return max(0, int(length) - int(window))
+
+
+def decode_attention_window(q, q_dtype, k_cache, v_cache, kv_dtype, block_tables,
+                            context_lens, softmax_scale, window, k_scale=1.0, v_scale=1.0):
+    """decode_attention restricted to each sequence's last `window` tokens."""
+    num_seqs, num_q_heads, head_dim = q.shape
+    num_kv_heads = k_cache.shape[1]
+    group = num_q_heads // num_kv_heads
+    scale = _as_f32_param(softmax_scale)
+    ks, vs = _as_f32_param(k_scale), _as_f32_param(v_scale)
+    out = np.zeros((num_seqs, num_q_heads, head_dim), dtype=np.float64)
+    for s in range(num_seqs):
+        length = int(context_lens[s])
+        if length == 0:
+            continue
+        first = window_start(length, window)
+        for kvh in range(num_kv_heads):
+            keys = gather_kv(k_cache, kv_dtype, ks, block_tables[s], length, kvh)[first:]
+            values = gather_kv(v_cache, kv_dtype, vs, block_tables[s], length, kvh)[first:]
+            for h in range(kvh * group, (kvh + 1) * group):
+                out[s, h] = attention_row(storage_to_f64(q[s, h], q_dtype), keys, values, scale)
+    return out
+
+
+def decode_attention_window_one(q, q_dtype, k_cache, v_cache, kv_dtype, block_tables,
+                                context_lens, softmax_scale, window, seq, head,
+                                k_scale=1.0, v_scale=1.0):
+    """One (sequence, q head) element of decode_attention_window."""
+    kvh = head // (q.shape[1] // k_cache.shape[1])
+    length = int(context_lens[seq])
+    if length == 0:
+        return np.zeros(q.shape[-1])
+    first = window_start(length, window)
+    keys = gather_kv(k_cache, kv_dtype, _as_f32_param(k_scale), block_tables[seq], length,
+                     kvh)[first:]
+    values = gather_kv(v_cache, kv_dtype, _as_f32_param(v_scale), block_tables[seq], length,
+                       kvh)[first:]
+    return attention_row(storage_to_f64(q[seq, head], q_dtype), keys, values,
+                         _as_f32_param(softmax_scale))
