@@ -290,6 +290,33 @@ pkv_status paged_attention_prefill_chunk(void* out, const void* query,
                                          void* stream);
 
 /*
+ * paged_attention_decode_sliding -- paged_attention_decode for sliding-window
+ * layers: the query of a sequence of length L attends to positions
+ * max(0, L - sliding_window) .. L-1 only (its own included; the pages note
+ * that such layers' blocks outside the window can be released early, "01.
+ * vLLM：从分页 KV 起家的通用推理引擎", section "KV 缓存管理与前缀缓存").
+ * Blocks before the window are not read: the work split counts only the
+ * window's blocks, so the cost follows min(L, window).  block_tables rows
+ * must still map every logical block index up to L-1 (entries before the
+ * window are never read and may be invalid).  sliding_window >= 1 (else
+ * PKV_ERR_SHAPE); bf16 queries with bf16 or fp8 caches (else
+ * PKV_ERR_UNSUPPORTED); other arguments, workspace and errors as
+ * paged_attention_decode.
+ */
+pkv_status paged_attention_decode_sliding(void* out, const void* query, const void* k_cache,
+                                          const void* v_cache, int32_t num_blocks,
+                                          const int32_t* block_tables,
+                                          int32_t max_blocks_per_seq,
+                                          const int32_t* context_lens, int32_t num_seqs,
+                                          int32_t max_context_len, int32_t num_q_heads,
+                                          int32_t num_kv_heads, int32_t head_dim,
+                                          float softmax_scale, pkv_dtype q_dtype,
+                                          pkv_dtype kv_dtype, float k_scale, float v_scale,
+                                          int32_t sliding_window, int32_t partition_tokens,
+                                          void* workspace, size_t workspace_bytes,
+                                          void* stream);
+
+/*
  * int4 per token-head KV cache (PKV_INT4).  The pages list
  * "int4_per_token_head" among the lower-bit --kv-cache-dtype formats ("01.
  * vLLM：从分页 KV 起家的通用推理引擎", section "KV 缓存管理与前缀缓存", the

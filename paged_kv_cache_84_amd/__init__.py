@@ -25,6 +25,7 @@ from ._binding import (  # noqa: F401
     varlen_workspace_size,
     paged_attention_decode,
     paged_attention_decode_int4,
+    paged_attention_decode_sliding,
     paged_attention_prefill_chunk,
     paged_attention_varlen,
     reshape_and_cache,

@@ -45,6 +45,9 @@ _SIGNATURES = {
     "paged_attention_decode": (_I32, [_P, _P, _P, _P, _I32, _P, _I32, _P, _I32, _I32,
                                       _I32, _I32, _I32, _F, _I32, _I32, _F, _F, _I32,
                                       _P, _SZ, _P]),
+    "paged_attention_decode_sliding": (_I32, [_P, _P, _P, _P, _I32, _P, _I32, _P, _I32, _I32,
+                                              _I32, _I32, _I32, _F, _I32, _I32, _F, _F, _I32,
+                                              _I32, _P, _SZ, _P]),
     "reshape_and_cache_int4": (_I32, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
                                       _I32, _P]),
     "paged_attention_decode_int4": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _P, _I32, _P, _I32,
@@ -262,6 +265,32 @@ def paged_attention_decode(query, k_cache, v_cache, block_tables, context_lens,
         int(partition_tokens), _dev(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), _stream(query))
     _check("paged_attention_decode", st)
+    return out
+
+
+def paged_attention_decode_sliding(query, k_cache, v_cache, block_tables, context_lens,
+                                   max_context_len, softmax_scale, sliding_window,
+                                   k_scale=1.0, v_scale=1.0, partition_tokens=0, out=None,
+                                   workspace=None):
+    """Decode over each sequence's last `sliding_window` tokens (see the header)."""
+    s, hq, d = query.shape
+    hkv = k_cache.shape[1]
+    if out is None:
+        out = torch.empty_like(query)
+    need = decode_workspace_size(s, hq, hkv, d, max_context_len, partition_tokens)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=query.device)
+    assert block_tables.shape[0] >= s and context_lens.shape[0] >= s
+    st = library().paged_attention_decode_sliding(
+        _dev(out, "out", query.dtype), _dev(query, "query"), _dev(k_cache, "k_cache"),
+        _dev(v_cache, "v_cache"), k_cache.shape[0],
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(context_lens, "context_lens", torch.int32), s, int(max_context_len), hq,
+        hkv, d, float(softmax_scale), _dtype_code(query, "query"),
+        _dtype_code(k_cache, "k_cache"), float(k_scale), float(v_scale), int(sliding_window),
+        int(partition_tokens), _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(query))
+    _check("paged_attention_decode_sliding", st)
     return out
 
 

@@ -581,7 +581,7 @@ __global__ __launch_bounds__(kWave * W) void decode_merge_kernel(
     typename QT::storage* __restrict__ out, const float* __restrict__ rec_out,
     const float* __restrict__ rec_ml, const int32_t* __restrict__ context_lens,
     int32_t num_seqs, int32_t max_len, int32_t num_q_heads, int32_t num_chunks,
-    int32_t fixed_chunk, float v_scale) {
+    int32_t fixed_chunk, float v_scale, int32_t window) {
   constexpr int kPer = D / kWave;
   __shared__ float wts[W][kWave];
   __shared__ float part[W][D + 1];
@@ -589,12 +589,12 @@ __global__ __launch_bounds__(kWave * W) void decode_merge_kernel(
   const int seq = blockIdx.y;
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
-  const BatchScan sc = scan_batch(context_lens, num_seqs, max_len);
+  const BatchScan sc = scan_batch(context_lens, num_seqs, max_len, window);
   const int owner = seq / sc.k;
   int before = __builtin_amdgcn_readlane(sc.first, owner);
   for (int t = owner * sc.k; t < seq; ++t)
-    before += blocks_of(seq_len(sc, context_lens, t, max_len));
-  const int n = blocks_of(seq_len(sc, context_lens, seq, max_len));
+    before += window_blocks(seq_len(sc, context_lens, t, max_len), window);
+  const int n = window_blocks(seq_len(sc, context_lens, seq, max_len), window);
   typename QT::storage* o = out + (int64_t(seq) * num_q_heads + h) * D;
   if (n == 0) {
     if (wave == 0) {
@@ -714,18 +714,18 @@ static bool make_plan(int32_t s, int32_t hq, int32_t hkv, int32_t d, int32_t max
 template <typename QT, int D>
 static pkv_status launch_merge(void* out, const int32_t* lens, int32_t s, int32_t max_len,
                                int32_t hq, float v_scale, const DecodePlan& plan, void* ws,
-                               hipStream_t st) {
+                               hipStream_t st, int32_t window = 0) {
   const float* rec_out = static_cast<const float*>(ws);
   const float* rec_ml =
       reinterpret_cast<const float*>(static_cast<const char*>(ws) + plan.out_bytes);
   if (plan.fixed_chunk > 0)
     hipLaunchKernelGGL((decode_merge_kernel<QT, D, 4>), dim3(hq, s), dim3(kWave * 4), 0, st,
                        static_cast<typename QT::storage*>(out), rec_out, rec_ml, lens, s,
-                       max_len, hq, plan.num_chunks, plan.fixed_chunk, v_scale);
+                       max_len, hq, plan.num_chunks, plan.fixed_chunk, v_scale, window);
   else
     hipLaunchKernelGGL((decode_merge_kernel<QT, D, 1>), dim3(hq, s), dim3(kWave), 0, st,
                        static_cast<typename QT::storage*>(out), rec_out, rec_ml, lens, s,
-                       max_len, hq, plan.num_chunks, plan.fixed_chunk, v_scale);
+                       max_len, hq, plan.num_chunks, plan.fixed_chunk, v_scale, window);
   return launch_status();
 }
 
@@ -834,7 +834,7 @@ static pkv_status mfma_decode(void* out, const void* query, const void* k_cache,
                               int32_t max_context_len, int32_t num_q_heads,
                               int32_t num_kv_heads, int32_t head_dim, float scale_log2,
                               pkv_dtype kv_dtype, float v_scale, const DecodePlan& lay,
-                              void* workspace, void* stream) {
+                              void* workspace, void* stream, int32_t window = 0) {
   const int64_t target = int64_t(PKV_DECODE_TARGET_WAVES) *
                          (kv_dtype == PKV_BF16 ? 1 : PKV_FP8_WAVES_PER_SIMD);
   const int64_t per_wave =
@@ -847,14 +847,14 @@ static pkv_status mfma_decode(void* out, const void* query, const void* k_cache,
                    lay.num_chunks, lay.fixed_chunk, int32_t(per_wave),
                    static_cast<float*>(workspace),
                    reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.out_bytes),
-                   stream, k_scales, v_scales};
+                   stream, k_scales, v_scales, window};
   if (launch_decode_mfma(a) != PKV_OK) return PKV_ERR_LAUNCH;
   hipStream_t st = as_stream(stream);
   return head_dim == 64
              ? launch_merge<BF16, 64>(out, context_lens, num_seqs, max_context_len,
-                                      num_q_heads, v_scale, lay, workspace, st)
+                                      num_q_heads, v_scale, lay, workspace, st, window)
              : launch_merge<BF16, 128>(out, context_lens, num_seqs, max_context_len,
-                                       num_q_heads, v_scale, lay, workspace, st);
+                                       num_q_heads, v_scale, lay, workspace, st, window);
 }
 
 }  // namespace pkv
@@ -885,14 +885,15 @@ extern "C" size_t paged_attention_decode_workspace_size(int32_t num_seqs,
   return p.out_bytes + p.ml_bytes;
 }
 
-extern "C" pkv_status paged_attention_decode(
+static pkv_status decode_impl(
     void* out, const void* query, const void* k_cache, const void* v_cache,
     int32_t num_blocks, const int32_t* block_tables, int32_t max_blocks_per_seq,
     const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
     float softmax_scale, pkv_dtype q_dtype, pkv_dtype kv_dtype, float k_scale,
     float v_scale, int32_t partition_tokens, void* workspace,
-    size_t workspace_bytes, void* stream) {
+    size_t workspace_bytes, void* stream, int32_t window) {
+  if (window < 0) return PKV_ERR_SHAPE;
   if (num_seqs < 0 || num_blocks < 0 || max_blocks_per_seq < 0 ||
       max_context_len < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
       head_dim <= 0)
@@ -930,8 +931,10 @@ extern "C" pkv_status paged_attention_decode(
     return mfma_decode(out, query, k_cache, v_cache, nullptr, nullptr, num_blocks, block_tables,
                        max_blocks_per_seq, context_lens, num_seqs, max_context_len,
                        num_q_heads, num_kv_heads, head_dim, softmax_scale * k_scale * kLog2e,
-                       kv_dtype, v_scale, lay, workspace, stream);
+                       kv_dtype, v_scale, lay, workspace, stream, window);
 #endif
+  // the sliding window is built into the matrix-core kernel only
+  if (window > 0) return PKV_ERR_UNSUPPORTED;
   // fp32 q with head_dim 128 keeps at most two heads per wave (registers)
   const int max_gw = (f32 && head_dim == 128) ? 2 : PKV_DECODE_MAX_HEADS_PER_WAVE;
   const int waves = (group + max_gw - 1) / max_gw;
@@ -952,6 +955,35 @@ extern "C" pkv_status paged_attention_decode(
   return head_dim == 64 ? dispatch_gw<BF16, FP8, 64>(PKV_DECODE_ARGS)
                         : dispatch_gw<BF16, FP8, 128>(PKV_DECODE_ARGS);
 #undef PKV_DECODE_ARGS
+}
+
+extern "C" pkv_status paged_attention_decode(
+    void* out, const void* query, const void* k_cache, const void* v_cache,
+    int32_t num_blocks, const int32_t* block_tables, int32_t max_blocks_per_seq,
+    const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    float softmax_scale, pkv_dtype q_dtype, pkv_dtype kv_dtype, float k_scale,
+    float v_scale, int32_t partition_tokens, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  return decode_impl(out, query, k_cache, v_cache, num_blocks, block_tables,
+                     max_blocks_per_seq, context_lens, num_seqs, max_context_len, num_q_heads,
+                     num_kv_heads, head_dim, softmax_scale, q_dtype, kv_dtype, k_scale, v_scale,
+                     partition_tokens, workspace, workspace_bytes, stream, 0);
+}
+
+extern "C" pkv_status paged_attention_decode_sliding(
+    void* out, const void* query, const void* k_cache, const void* v_cache,
+    int32_t num_blocks, const int32_t* block_tables, int32_t max_blocks_per_seq,
+    const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    float softmax_scale, pkv_dtype q_dtype, pkv_dtype kv_dtype, float k_scale,
+    float v_scale, int32_t sliding_window, int32_t partition_tokens, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  if (sliding_window <= 0) return PKV_ERR_SHAPE;
+  return decode_impl(out, query, k_cache, v_cache, num_blocks, block_tables,
+                     max_blocks_per_seq, context_lens, num_seqs, max_context_len, num_q_heads,
+                     num_kv_heads, head_dim, softmax_scale, q_dtype, kv_dtype, k_scale, v_scale,
+                     partition_tokens, workspace, workspace_bytes, stream, sliding_window);
 }
 
 extern "C" pkv_status paged_attention_decode_int4(

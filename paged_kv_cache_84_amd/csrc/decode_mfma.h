@@ -27,6 +27,7 @@ struct DecodeMfmaArgs {
   void* stream;
   const float* k_scales = nullptr;   // int4 caches: per (block, kv head, slot) scales
   const float* v_scales = nullptr;
+  int32_t window = 0;                // sliding window in tokens (0 = none)
 };
 
 // bf16 queries with a bf16 or fp8 E4M3 cache (head_dim 64 or 128) or an int4

@@ -216,17 +216,19 @@ PKV_DEVICE void stage_v(VRegs<KVT, D>& r, char* vl, int lane, int rows) {
 // [before, before + n) of the flattened batch.
 struct SeqCursor {
   int s, before, n, len;
+  int first;   // first block read (sliding window), 0 otherwise
 };
 
 // Move the cursor forward to the sequence holding block x (x below the
 // batch's block count, so the walk ends inside the batch).
 PKV_DEVICE void cursor_to(SeqCursor& c, int x, const BatchScan& sc, const int32_t* lens,
-                          int max_len) {
+                          int max_len, int window) {
   while (x >= c.before + c.n) {
     c.before += c.n;
     ++c.s;
     c.len = seq_len(sc, lens, c.s, max_len);
-    c.n = blocks_of(c.len);
+    c.n = window_blocks(c.len, window);
+    c.first = first_block(c.len, window);
   }
 }
 
@@ -240,7 +242,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
     int32_t num_q_heads, int32_t num_kv_heads, int32_t group, float scale_log2,
     float v_scale, int32_t num_chunks, int32_t fixed_chunk, int32_t chunks_per_wave,
     float* __restrict__ rec_out, float* __restrict__ rec_ml,
-    const float* __restrict__ k_scales, const float* __restrict__ v_scales) {
+    const float* __restrict__ k_scales, const float* __restrict__ v_scales, int32_t window) {
   using M = MGeom<KVT, D>;
   __shared__ __align__(16) char vl[kBlock * M::kVStride];
   const int kvh = blockIdx.x % num_kv_heads;
@@ -253,7 +255,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
 
   // This wave walks the blocks [b0, b1) of the flattened batch: chunks
   // wg * chunks_per_wave .. + chunks_per_wave - 1, each of c blocks.
-  const BatchScan sc = scan_batch(context_lens, num_seqs, max_len);
+  const BatchScan sc = scan_batch(context_lens, num_seqs, max_len, window);
   const int c = chunk_blocks(sc.total, num_chunks, fixed_chunk);
   const int b0 = wg * chunks_per_wave * c;
   if (b0 >= sc.total) return;
@@ -270,7 +272,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
     return base + (int64_t(b) * num_kv_heads + kvh) * kBlock;
   };
   auto table_id = [&](const SeqCursor& q, int x) -> int32_t {
-    const int i = x - q.before;
+    const int i = x - q.before + q.first;
     return i < max_blocks ? load_scalar(block_tables, int64_t(q.s) * max_blocks + i) : -1;
   };
   // Q^T of sequence s as B operands (zero columns past the group)
@@ -292,9 +294,10 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
   // the scalar cache).  Loads therefore cross sequence and chunk boundaries
   // without a pause; past b1 they re-read a block already read.
   SeqCursor cc;
-  locate(sc, context_lens, max_len, b0, cc.s, cc.before);
+  locate(sc, context_lens, max_len, b0, cc.s, cc.before, window);
   cc.len = seq_len(sc, context_lens, cc.s, max_len);
-  cc.n = blocks_of(cc.len);
+  cc.n = window_blocks(cc.len, window);
+  cc.first = first_block(cc.len, window);
   SeqCursor lc = cc, ic = cc;
   u32x4 qb[M::kKSteps], qn[M::kKSteps];
   load_q(cc.s, qb);
@@ -311,7 +314,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
   int32_t id_cur = table_id(cc, b0);
   int32_t id_next = -1;
   if (b0 + 1 < b1) {
-    cursor_to(ic, b0 + 1, sc, context_lens, max_len);
+    cursor_to(ic, b0 + 1, sc, context_lens, max_len, window);
     id_next = table_id(ic, b0 + 1);
   }
   const int32_t b_any = valid(id_cur) ? id_cur : 0;   // a block to re-read
@@ -338,8 +341,10 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
   int chunk_end = b0 + c;             // its end
 
   for (int x = b0; x < b1; ++x) {
-    const int i = x - cc.before;                       // block of sequence cc.s
+    const int i = x - cc.before + cc.first;            // block of sequence cc.s
     const int rows = valid(id_cur) ? min(kBlock, cc.len - i * kBlock) : 0;
+    // sliding window: keys before `first_key` (in this block) are out of sight
+    const int first_key = window > 0 ? cc.len - window - i * kBlock : 0;
     // the next block (possibly of the next sequence), or a re-read past b1
     const bool more = x + 1 < b1;
     const int32_t bn = (more && valid(id_next)) ? id_next : b_any;
@@ -352,14 +357,14 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
     // Q of a sequence entered by the next block
     const bool new_seq = more && x + 1 >= lc.before + lc.n;
     if (new_seq) {
-      cursor_to(lc, x + 1, sc, context_lens, max_len);
+      cursor_to(lc, x + 1, sc, context_lens, max_len, window);
       load_q(lc.s, qn);
     }
     // the id two blocks ahead, requested only once bn has been consumed:
     // waiting for one scalar load waits for all of them
     int32_t id_new = -1;
     if (x + 2 < b1) {
-      cursor_to(ic, x + 2, sc, context_lens, max_len);
+      cursor_to(ic, x + 2, sc, context_lens, max_len, window);
       id_new = table_id(ic, x + 2);
     }
     // S^T = K . Q^T
@@ -379,7 +384,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
         t = (st[r] - kcorr) * __uint_as_float(ksc[r]) * scale_log2;
       else
         t = st[r] * scale_log2;
-      sv[r] = 4 * j + r < rows ? t : -INFINITY;
+      sv[r] = (4 * j + r < rows && 4 * j + r >= first_key) ? t : -INFINITY;
       raise |= sv[r] > m + kRaiseM;
     }
     if (__builtin_expect(__ballot(raise) != 0, 0)) {
@@ -402,7 +407,8 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
     // weight 0 whatever their scale slot holds)
     if constexpr (kInt4<KVT>) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) p[r] = 4 * j + r < rows ? p[r] * __uint_as_float(vsc[r]) : 0.f;
+      for (int r = 0; r < 4; ++r)
+        p[r] = (4 * j + r < rows && 4 * j + r >= first_key) ? p[r] * __uint_as_float(vsc[r]) : 0.f;
     }
     // P^T = hi + lo, both bf16
     uint32_t hi[2], lo[2];
@@ -473,7 +479,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
         chunk_end += c;
       }
       if (x + 1 == seq_end && more) {
-        cursor_to(cc, x + 1, sc, context_lens, max_len);
+        cursor_to(cc, x + 1, sc, context_lens, max_len, window);
 #pragma unroll
         for (int ks = 0; ks < M::kKSteps; ++ks) qb[ks] = qn[ks];
         if constexpr (kInt4<KVT>) kcorr = offset_share();
@@ -493,7 +499,8 @@ static pkv_status launch_one(const DecodeMfmaArgs& a) {
                      a.block_tables, a.max_blocks, a.context_lens, a.num_seqs, a.max_len,
                      a.num_q_heads, a.num_kv_heads, a.num_q_heads / a.num_kv_heads,
                      a.scale_log2, a.v_scale, a.num_chunks, a.fixed_chunk,
-                     a.chunks_per_wave, a.rec_out, a.rec_ml, a.k_scales, a.v_scales);
+                     a.chunks_per_wave, a.rec_out, a.rec_ml, a.k_scales, a.v_scales,
+                     a.window);
   return launch_status();
 }
 

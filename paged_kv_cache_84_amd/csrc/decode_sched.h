@@ -18,6 +18,16 @@ namespace pkv {
 PKV_DEVICE int clamp_len(int len, int max_len) { return min(max(len, 0), max_len); }
 PKV_DEVICE int blocks_of(int len) { return (len + kBlock - 1) / kBlock; }
 
+// Sliding window (window > 0): a sequence of length len attends to its last
+// `window` positions only, so it reads its blocks from first_block on; the
+// split below counts those blocks (window 0 = the whole context).
+PKV_DEVICE int first_block(int len, int window) {
+  return window > 0 && len > window ? (len - window) / kBlock : 0;
+}
+PKV_DEVICE int window_blocks(int len, int window) {
+  return blocks_of(len) - first_block(len, window);
+}
+
 // Block counts of the batch: lane i owns the k = ceil(S / 64) consecutive
 // sequences [i k, i k + k).
 struct BatchScan {
@@ -28,7 +38,8 @@ struct BatchScan {
   int total;    // blocks of the batch
 };
 
-PKV_DEVICE BatchScan scan_batch(const int32_t* lens, int num_seqs, int max_len) {
+PKV_DEVICE BatchScan scan_batch(const int32_t* lens, int num_seqs, int max_len,
+                                int window = 0) {
   BatchScan b;
   const int lane = lane_id();
   b.k = (num_seqs + kWave - 1) / kWave;
@@ -43,7 +54,7 @@ PKV_DEVICE BatchScan scan_batch(const int32_t* lens, int num_seqs, int max_len) 
       l4[u] = (j + u < b.k && sq < num_seqs) ? clamp_len(lens[sq], max_len) : 0;
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) b.own += blocks_of(l4[u]);
+    for (int u = 0; u < 4; ++u) b.own += window_blocks(l4[u], window);
     if (j == 0) b.own_len = l4[0];
   }
   b.first = wave_exclusive_sum(b.own);
@@ -60,13 +71,13 @@ PKV_DEVICE int seq_len(const BatchScan& b, const int32_t* lens, int s, int max_l
 // The sequence holding block `blk` of the batch (blk < total) and the number
 // of blocks before it.
 PKV_DEVICE void locate(const BatchScan& b, const int32_t* lens, int max_len, int blk,
-                       int& s, int& before) {
+                       int& s, int& before, int window = 0) {
   const uint64_t m = __ballot(b.own > 0 && b.first <= blk && blk < b.first + b.own);
   const int owner = __builtin_amdgcn_readfirstlane(int(__builtin_ctzll(m)));
   s = owner * b.k;
   before = __builtin_amdgcn_readlane(b.first, owner);
   for (;;) {
-    const int n = blocks_of(seq_len(b, lens, s, max_len));
+    const int n = window_blocks(seq_len(b, lens, s, max_len), window);
     if (before + n > blk) break;
     before += n;
     ++s;

@@ -258,3 +258,24 @@ def test_int4_errors(lib):
     assert dcall(a8=62) == SHAPE          # 992 tokens < max_context_len
     assert dcall(a17=100) == SHAPE        # partition not a multiple of 16
     assert dcall(a19=need - 1) == WS
+
+
+def test_sliding_errors(lib):
+    f = lib.paged_attention_decode_sliding
+    p = 0x100000
+    need = lib.paged_attention_decode_workspace_size(4, 32, 8, 128, 1000, 0)
+    base = [p, p, p, p, 100, p, 63, p, 4, 1000, 32, 8, 128, 0.088, BF16, BF16, 1.0, 1.0, 256,
+            0, p, need, None]
+
+    def call(**k):
+        a = list(base)
+        for i, v in k.items():
+            a[int(i[1:])] = v
+        return f(*a)
+
+    assert call(a8=0) == OK
+    assert call(a18=0) == SHAPE           # window must be positive
+    assert call(a18=-5) == SHAPE
+    assert call(a14=F32, a15=F32) == UNSUP  # the window is built into the matrix-core path
+    assert call(a0=None) == NULL
+    assert call(a21=need - 1) == WS
