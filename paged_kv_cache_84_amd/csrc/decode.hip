@@ -685,8 +685,15 @@ struct DecodePlan {
   size_t out_bytes, ml_bytes;
 };
 
+// waves_per_simd: how many waves the library's own split aims for per SIMD
+// (a bf16 block keeps one wave busy; an int4 block carries a quarter of the
+// bytes for the same products, so int4 caches ask for four).
+#ifndef PKV_INT4_WAVES_PER_SIMD
+#define PKV_INT4_WAVES_PER_SIMD 4
+#endif
+constexpr int kInt4WavesPerSimd = PKV_INT4_WAVES_PER_SIMD;
 static bool make_plan(int32_t s, int32_t hq, int32_t hkv, int32_t d, int32_t max_len,
-                      int32_t partition_tokens, DecodePlan& p) {
+                      int32_t partition_tokens, DecodePlan& p, int waves_per_simd = 1) {
   if (s < 0 || hq <= 0 || hkv <= 0 || d <= 0 || max_len < 0 || hq % hkv != 0) return false;
   const int64_t bound = int64_t(s) * ((max_len + kBlock - 1) / kBlock);
   int64_t chunks;
@@ -698,7 +705,7 @@ static bool make_plan(int32_t s, int32_t hq, int32_t hkv, int32_t d, int32_t max
     // one chunk per wave slot and kv head (the matrix-core kernel runs a
     // whole query group in one wave; the vector kernel's second wave for
     // groups above four shares its chunk's tiles through the cache)
-    chunks = PKV_DECODE_TARGET_WAVES / int64_t(hkv);
+    chunks = int64_t(PKV_DECODE_TARGET_WAVES) * waves_per_simd / int64_t(hkv);
     chunks = std::min<int64_t>(chunks, (bound + kMinChunkBlocks - 1) / kMinChunkBlocks);
   }
   chunks = std::max<int64_t>(chunks, 1);
@@ -877,10 +884,11 @@ extern "C" size_t paged_attention_decode_workspace_size(int32_t num_seqs,
                                                         int32_t head_dim,
                                                         int32_t max_context_len,
                                                         int32_t partition_tokens) {
+  // large enough for every cache dtype's plan (int4 splits finer)
   DecodePlan p;
   if (partition_tokens < 0 || partition_tokens % kBlock != 0 ||
       !make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
-                 partition_tokens, p))
+                 partition_tokens, p, kInt4WavesPerSimd))
     return 0;
   return p.out_bytes + p.ml_bytes;
 }
@@ -1012,7 +1020,7 @@ extern "C" pkv_status paged_attention_decode_int4(
     return PKV_ERR_ALIGN;
   DecodePlan lay;
   if (!make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
-                 partition_tokens, lay) ||
+                 partition_tokens, lay, kInt4WavesPerSimd) ||
       int64_t(num_seqs) * num_q_heads > 0x7fffffff)
     return PKV_ERR_SHAPE;
   if (!workspace || workspace_bytes < lay.out_bytes + lay.ml_bytes) return PKV_ERR_WORKSPACE;
