@@ -1,7 +1,7 @@
 """Benchmark of the paged-attention hot path on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
-                    [--no-mixed] [--no-longctx] [--no-mha] [--no-swap] [--no-int4] [--no-blocks]
+                    [--no-mixed] [--no-longctx] [--no-mha] [--no-swap] [--no-window] [--no-int4] [--no-blocks]
     python bench.py --copy-calibration     (a plain 1 GiB device copy, for
                                             the HBM byte counters' scale)
 
@@ -16,7 +16,8 @@ Prints one JSON line (rank 0): whole-step throughput in algorithmic KV GB/s,
 KV tokens/s, the decode call's roofline fraction, the oracle's CPU rate on a
 bounded sample, the mixed unified step with chunked prefill (MFMA
 utilisation of the prefill call), the fp8 long-context decode, the
-32-layer MHA decode step, the 8B batch over an int4 per token-head cache,
+32-layer MHA decode step, the 8B batch with a sliding window and over an
+int4 per token-head cache,
 a device <-> host block swap of one long sequence, and the host block manager's operations per second on a serving
 trace (with the oracle's rate on a bounded sample beside it).  The roofline's "traffic" is the HBM bytes per
 decode call that rocprofv3's FETCH_SIZE and WRITE_SIZE counters measured
@@ -225,9 +226,22 @@ def bench_mixed(args, pk, C):
             "prefill_pairs": pairs,
             "decode_ms": round(ms_decode, 4),
             "decode_gbs": round(decode_bytes(s) / (ms_decode * 1e-3) / 1e9, 1),
-            "unified": {"attention_ms": round(ms_varlen, 4),
-                        "two_launch_attention_ms": round(ms_prefill + ms_decode, 4),
-                        "ms_per_step": round(ms_step_varlen, 4)}}
+            "unified": unified_roofline(ms_varlen, ms_prefill + ms_decode, ms_step_varlen,
+                                        flops, decode_bytes(s))}
+
+
+def unified_roofline(ms, ms_two, ms_step, flops, nbytes):
+    """The unified call does the chunks' products (matrix-core bound) and
+    streams the decodes' K/V (HBM bound) side by side: its floor is the
+    larger of the two ideal times."""
+    t_mfma = flops / (BF16_MFMA_PEAK_TFLOPS * 1e12) * 1e3
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9) * 1e3
+    bound = "hbm" if t_hbm >= t_mfma else "mfma"
+    return {"attention_ms": round(ms, 4), "two_launch_attention_ms": round(ms_two, 4),
+            "ms_per_step": round(ms_step, 4),
+            "roofline": {"bound": bound, "ideal_ms": round(max(t_mfma, t_hbm), 4),
+                         "ideal_mfma_ms": round(t_mfma, 4), "ideal_hbm_ms": round(t_hbm, 4),
+                         "frac": round(max(t_mfma, t_hbm) / ms, 4)}}
 
 
 PCIE5_X16_GBS = 64.0   # host link of one MI355X, per direction
@@ -384,6 +398,36 @@ def bench_extra_decode(args, pk, C, which):
             "algorithmic_bytes": nbytes}
 
 
+def bench_window(args, pk, ds, step, window=1024):
+    """The 8B decode batch with a 1,024-token sliding window on the decode
+    leg's device inputs: only the window's K/V are read (algorithmic bytes
+    count min(L, W) tokens per sequence)."""
+    lens = step.decode_context_lens
+    stream = torch.cuda.current_stream()
+    q = ds.q[0][ds.num_prefill_tokens:]
+    out = torch.empty_like(q)
+    ws = torch.empty(pk.decode_workspace_size(len(lens), step.num_q_heads, step.num_kv_heads,
+                                              step.head_dim, int(lens.max())),
+                     dtype=torch.uint8, device="cuda")
+
+    def run(i):
+        pk.paged_attention_decode_sliding(q, ds.k_caches[0], ds.v_caches[0], ds.dec_tables,
+                                          ds.dec_lens, int(lens.max()), step.softmax_scale,
+                                          window, out=out, workspace=ws)
+
+    for i in range(args.warmup):
+        run(i)
+    ms = time_region(run, args.steps, stream)
+    seen = np.minimum(lens.astype(np.int64), window)
+    nbytes = (int(seen.sum()) * 2 * step.num_kv_heads * step.head_dim * 2
+              + 2 * len(lens) * step.num_q_heads * step.head_dim * 2)
+    return {"workload": f"Llama-3.1-8B-shaped decode batch with a {window}-token sliding "
+                        "window (64 sequences, context 512..4096, 32/8 heads, d128, bf16)",
+            "window": window, "ms_per_call": round(ms, 4), "algorithmic_bytes": nbytes,
+            "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def bench_int4(args, pk, step, copies=3):
     """The 8B decode batch (64 sequences, 512..4096 tokens, 32 q / 8 kv heads)
     over an int4 per token-head cache: decode calls on resident inputs,
@@ -438,6 +482,8 @@ def main():
                     help="skip the 32-layer MHA decode step (128 GiB of KV)")
     ap.add_argument("--no-swap", action="store_true",
                     help="skip the device <-> host block swap of one long sequence")
+    ap.add_argument("--no-window", action="store_true",
+                    help="skip the sliding-window decode of the 8B batch")
     ap.add_argument("--no-int4", action="store_true",
                     help="skip the int4 per token-head decode of the 8B batch")
     ap.add_argument("--no-blocks", action="store_true",
@@ -506,6 +552,8 @@ def main():
         line["longctx_decode"] = bench_extra_decode(args, pk, C, "longctx")
     if not args.no_mha:
         line["mha_decode"] = bench_extra_decode(args, pk, C, "mha")
+    if not args.no_window:
+        line["window_decode"] = bench_window(args, pk, dss[0], step)
     if not args.no_int4:
         line["int4_decode"] = bench_int4(args, pk, step)
     if not args.no_swap:
