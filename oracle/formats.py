@@ -22,6 +22,17 @@ The encodings below are the standard ones:
   nibble), element 2i in the low nibble and element 2i+1 in the high nibble
   of byte i.  The value is (u - 8) * s.
 
+* nvfp4-style blocks (the pages name "nvfp4" among the lower-bit
+  --kv-cache-dtype choices, same row; everything else is a reading): FP4
+  E2M1 elements (1 sign, 2 exponent bits with bias 1, 1 mantissa bit;
+  magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), one E4M3 scale per 16 consecutive
+  elements of a (token, kv head) row, and a per-tensor binary32 scale g.
+  Block scale code = E4M3(fp32(fp32(max|x| / 6) / g)); element code =
+  E2M1(fp32(x / fp32(S * g))) with S the block scale's value (0 for a zero
+  block: all codes 0); E2M1 rounds to nearest with ties to the even
+  mantissa and saturates to +-6, keeping the sign (of zero too).  Codes are
+  packed two per byte, element 2i in the low nibble.  Value = e2m1 * S * g.
+
 Storage is always handled as raw integers (uint16 for bf16, uint8 for fp8) or
 float32, exactly as the cache holds it; values are produced in float64.
 """
@@ -30,6 +41,7 @@ import numpy as np
 
 F32, BF16, FP8_E4M3 = "f32", "bf16", "fp8_e4m3"
 INT4_PTH = "int4_per_token_head"
+NVFP4 = "nvfp4"
 
 BYTES_PER_ELEM = {F32: 4, BF16: 2, FP8_E4M3: 1}
 
@@ -182,3 +194,66 @@ def int4_rows_to_f64(packed_rows, scales):
     """Rows of packed codes [n][D/2] with their scales [n] -> float64 [n][D]."""
     q = int4_unpack_codes(packed_rows).astype(np.float64)
     return q * np.asarray(scales, dtype=np.float32).astype(np.float64)[..., None]
+
+
+E2M1_MAGNITUDES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+NVFP4_BLOCK = 16
+
+
+def e2m1_code_value(code):
+    """Real value of one E2M1 code (low 4 bits), written from its fields."""
+    code = int(code) & 0xF
+    sign = -1.0 if code & 8 else 1.0
+    e, m = (code >> 1) & 3, code & 1
+    if e == 0:
+        return sign * m * 0.5                    # subnormal: 0 or 0.5
+    return sign * (1.0 + m / 2.0) * 2.0 ** (e - 1)
+
+
+def e2m1_encode_scalar(y):
+    """Nearest E2M1 code of one binary32 value: ties to the even mantissa,
+    |y| > 6 saturates, the sign bit of y is kept."""
+    y = np.float32(y)
+    assert np.isfinite(y)
+    sign = int(np.array([y], dtype=np.float32).view(np.uint32)[0] >> 31)
+    mag = abs(float(y))
+    dist = np.abs(E2M1_MAGNITUDES - mag)
+    best = np.flatnonzero(dist == dist.min())
+    idx = int(best[0]) if len(best) == 1 else int([i for i in best if i % 2 == 0][0])
+    return idx | (sign << 3)
+
+
+def nvfp4_quantize_row(x_f32, g):
+    """One row (D a multiple of 16) -> (packed codes uint8 [D/2], block scale
+    codes uint8 [D/16]) under the per-tensor scale g."""
+    x = np.asarray(x_f32, dtype=np.float32)
+    g = np.float32(g)
+    assert x.ndim == 1 and x.size % NVFP4_BLOCK == 0 and np.all(np.isfinite(x)) and g > 0
+    codes = np.zeros(x.size, dtype=np.uint8)
+    scales = np.zeros(x.size // NVFP4_BLOCK, dtype=np.uint8)
+    for b in range(x.size // NVFP4_BLOCK):
+        blk = x[NVFP4_BLOCK * b:NVFP4_BLOCK * (b + 1)]
+        amax = np.float32(np.max(np.abs(blk)))
+        t = np.float32(np.float32(amax / np.float32(6.0)) / g)
+        sc = int(e4m3_encode_scalar(t))
+        scales[b] = sc
+        sval = np.float32(e4m3_code_value(sc))
+        if sval == 0:
+            continue
+        denom = np.float32(sval * g)
+        for i, v in enumerate(blk):
+            codes[NVFP4_BLOCK * b + i] = e2m1_encode_scalar(np.float32(v / denom))
+    return (codes[0::2] | (codes[1::2] << np.uint8(4))).astype(np.uint8), scales
+
+
+def nvfp4_rows_to_f64(packed_rows, scale_rows, g):
+    """Rows of packed codes [n][D/2] with block scale codes [n][D/16] ->
+    float64 [n][D] (times the per-tensor scale g)."""
+    packed = np.asarray(packed_rows, dtype=np.uint8)
+    c = np.empty(packed.shape[:-1] + (2 * packed.shape[-1],), dtype=np.int64)
+    c[..., 0::2] = packed & 0x0F
+    c[..., 1::2] = packed >> 4
+    vals = np.vectorize(e2m1_code_value, otypes=[np.float64])(c) if c.size else c.astype(float)
+    s = E4M3_TABLE[np.asarray(scale_rows, dtype=np.uint8)]
+    s = np.repeat(s, NVFP4_BLOCK, axis=-1)
+    return vals * s * float(np.float32(g))

@@ -34,6 +34,8 @@ from .formats import (
     FP8_E4M3,
     int4_quantize_row,
     int4_rows_to_f64,
+    nvfp4_quantize_row,
+    nvfp4_rows_to_f64,
     quantise_to_e4m3,
     storage_to_f64,
 )
@@ -497,3 +499,55 @@ def decode_attention_window_one(q, q_dtype, k_cache, v_cache, kv_dtype, block_ta
                        kvh)[first:]
     return attention_row(storage_to_f64(q[seq, head], q_dtype), keys, values,
                          _as_f32_param(softmax_scale))
+
+
+# --- nvfp4-style caches (encoding: oracle/formats.py) -----------------------
+# Codes [num_blocks][num_kv_heads][16][D/2] (uint8), block scale codes
+# [num_blocks][num_kv_heads][16][D/16] (E4M3 bytes), per-tensor k/v scales.
+
+
+def reshape_and_cache_nvfp4(key, value, k_cache, v_cache, k_bscales, v_bscales, slots,
+                            src_dtype, k_scale, v_scale):
+    """reshape_and_cache into nvfp4 caches; returns the four new arrays."""
+    kc, vc, ksc, vsc = [np.array(a, copy=True) for a in (k_cache, v_cache, k_bscales, v_bscales)]
+    for t in range(len(slots)):
+        slot = int(slots[t])
+        if slot < 0:
+            continue
+        block, offset = divmod(slot, BLOCK_SIZE)
+        for h in range(kc.shape[1]):
+            for src, cache, sc, g in ((key, kc, ksc, k_scale), (value, vc, vsc, v_scale)):
+                x = storage_to_f64(src[t, h], src_dtype).astype(np.float32)   # exact
+                cache[block, h, offset], sc[block, h, offset] = nvfp4_quantize_row(x, g)
+    return kc, vc, ksc, vsc
+
+
+def gather_kv_nvfp4(cache, bscales, g, block_table_row, length, kv_head):
+    rows = []
+    for j in range(blocks_needed(length)):
+        block = int(block_table_row[j])
+        n = min(BLOCK_SIZE, length - j * BLOCK_SIZE)
+        rows.append(nvfp4_rows_to_f64(cache[block, kv_head][:n], bscales[block, kv_head][:n], g))
+    if not rows:
+        return np.zeros((0, 2 * cache.shape[-1]), dtype=np.float64)
+    return np.concatenate(rows, axis=0)
+
+
+def decode_attention_nvfp4(q, q_dtype, k_cache, v_cache, k_bscales, v_bscales, block_tables,
+                           context_lens, softmax_scale, k_scale, v_scale):
+    """decode_attention over nvfp4 caches (float64 [S][Hq][D])."""
+    num_seqs, num_q_heads, head_dim = q.shape
+    num_kv_heads = k_cache.shape[1]
+    group = num_q_heads // num_kv_heads
+    scale = _as_f32_param(softmax_scale)
+    out = np.zeros((num_seqs, num_q_heads, head_dim), dtype=np.float64)
+    for s in range(num_seqs):
+        length = int(context_lens[s])
+        if length == 0:
+            continue
+        for kvh in range(num_kv_heads):
+            keys = gather_kv_nvfp4(k_cache, k_bscales, k_scale, block_tables[s], length, kvh)
+            values = gather_kv_nvfp4(v_cache, v_bscales, v_scale, block_tables[s], length, kvh)
+            for h in range(kvh * group, (kvh + 1) * group):
+                out[s, h] = attention_row(storage_to_f64(q[s, h], q_dtype), keys, values, scale)
+    return out
