@@ -61,8 +61,11 @@ enum {
   PKV_F32 = 0,      /* IEEE binary32                                          */
   PKV_BF16 = 1,     /* bfloat16 (upper half of a binary32)                    */
   PKV_FP8_E4M3 = 2, /* OCP fp8 E4M3 ("fn": no inf, max 448), cache dtype only */
-  PKV_INT4 = 3      /* int4 per token-head codes (see reshape_and_cache_int4),
+  PKV_INT4 = 3,     /* int4 per token-head codes (see reshape_and_cache_int4),
                        cache dtype only, with separate per-row scale arrays    */
+  PKV_NVFP4 = 4     /* FP4 E2M1 codes with an E4M3 scale per 16 elements and a
+                       per-tensor scale (see reshape_and_cache_nvfp4), cache
+                       dtype only, with separate block-scale arrays           */
 };
 
 #define PKV_BLOCK_SIZE 16
@@ -361,6 +364,57 @@ pkv_status paged_attention_decode_int4(void* out, const void* query, const void*
                                        float softmax_scale, pkv_dtype q_dtype,
                                        int32_t partition_tokens, void* workspace,
                                        size_t workspace_bytes, void* stream);
+
+/*
+ * nvfp4-style KV cache (PKV_NVFP4).  The pages list "nvfp4" among the
+ * lower-bit --kv-cache-dtype formats ("01. vLLM：从分页 KV 起家的通用推理引擎",
+ * section "KV 缓存管理与前缀缓存", the --kv-cache-dtype row) and fix nothing
+ * else; the encoding here: every 16 consecutive elements of a (token, kv
+ * head) row share one E4M3 block scale, and a per-tensor binary32 scale g
+ * (k_scale for K, v_scale for V) sits above all blocks.  For a block x:
+ *   scale code  c = E4M3(fp32(fp32(max|x| / 6) / g))   (round to nearest
+ *               even, saturating at 448)
+ *   element     e = E2M1(fp32(x / fp32(S * g)))         (S = value of c;
+ *               nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6 with ties to the even
+ *               mantissa, saturating at 6, sign kept; all codes 0 if S = 0)
+ * and its value is e * S * g.  E2M1 codes are packed two per byte, element
+ * 2i in the low nibble.  Layouts:
+ *   k_cache, v_cache     uint8 [num_blocks][num_kv_heads][16][head_dim / 2]
+ *   k_bscales, v_bscales uint8 [num_blocks][num_kv_heads][16][head_dim / 16]
+ * 4.5 bits per element.
+ *
+ * reshape_and_cache_nvfp4 -- reshape_and_cache into nvfp4 caches: each
+ * scheduled token's K and V rows (bf16 or fp32, finite) are encoded as
+ * above and written with their block scales at the slot; a negative slot
+ * skips the token.  head_dim a multiple of 16, at most 128; k_scale,
+ * v_scale > 0.
+ */
+pkv_status reshape_and_cache_nvfp4(const void* key, const void* value, void* k_cache,
+                                   void* v_cache, void* k_bscales, void* v_bscales,
+                                   const int64_t* slot_mapping, int32_t num_tokens,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                                   pkv_dtype src_dtype, float k_scale, float v_scale,
+                                   void* stream);
+
+/*
+ * paged_attention_decode_nvfp4 -- paged_attention_decode over nvfp4 caches:
+ * the result is attention over the values e * S * g.  Each 16-element piece
+ * is widened to bf16 exactly in registers (e * S has at most six significant
+ * bits); g of K multiplies the scores and g of V the output.  Same work
+ * split, workspace (paged_attention_decode_workspace_size) and merge as
+ * paged_attention_decode.  Supported: bf16 queries, head_dim 128,
+ * group <= 8; k_scale, v_scale > 0.
+ */
+pkv_status paged_attention_decode_nvfp4(void* out, const void* query, const void* k_cache,
+                                        const void* v_cache, const void* k_bscales,
+                                        const void* v_bscales, int32_t num_blocks,
+                                        const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                        const int32_t* context_lens, int32_t num_seqs,
+                                        int32_t max_context_len, int32_t num_q_heads,
+                                        int32_t num_kv_heads, int32_t head_dim,
+                                        float softmax_scale, pkv_dtype q_dtype, float k_scale,
+                                        float v_scale, int32_t partition_tokens,
+                                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * paged_attention_varlen -- the attention of one whole engine step in one

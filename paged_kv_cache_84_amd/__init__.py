@@ -25,10 +25,12 @@ from ._binding import (  # noqa: F401
     varlen_workspace_size,
     paged_attention_decode,
     paged_attention_decode_int4,
+    paged_attention_decode_nvfp4,
     paged_attention_decode_sliding,
     paged_attention_prefill_chunk,
     paged_attention_varlen,
     reshape_and_cache,
     reshape_and_cache_int4,
+    reshape_and_cache_nvfp4,
     swap_blocks,
 )

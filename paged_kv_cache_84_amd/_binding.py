@@ -8,7 +8,7 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 BLOCK_SIZE = 16
 
-PKV_F32, PKV_BF16, PKV_FP8_E4M3, PKV_INT4 = 0, 1, 2, 3
+PKV_F32, PKV_BF16, PKV_FP8_E4M3, PKV_INT4, PKV_NVFP4 = 0, 1, 2, 3, 4
 _STATUS = {0: "ok", 1: "null pointer", 2: "misaligned pointer", 3: "bad shape",
            4: "unsupported", 5: "workspace too small", 6: "launch failed"}
 
@@ -53,6 +53,11 @@ _SIGNATURES = {
     "paged_attention_decode_int4": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _P, _I32, _P, _I32,
                                            _I32, _I32, _I32, _I32, _F, _I32, _I32, _P, _SZ,
                                            _P]),
+    "reshape_and_cache_nvfp4": (_I32, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
+                                       _I32, _F, _F, _P]),
+    "paged_attention_decode_nvfp4": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _P, _I32, _P, _I32,
+                                            _I32, _I32, _I32, _I32, _F, _I32, _F, _F, _I32, _P,
+                                            _SZ, _P]),
     "paged_attention_varlen_workspace_size": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
     "paged_attention_varlen": (_I32, [_P, _P, _P, _P, _I32, _P, _I32, _P, _P, _I32, _I32,
                                       _I32, _I32, _I32, _I32, _F, _I32, _I32, _P, _SZ, _P]),
@@ -388,4 +393,46 @@ def paged_attention_decode_int4(query, k_cache, v_cache, k_scales, v_scales, blo
         int(partition_tokens), _dev(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), _stream(query))
     _check("paged_attention_decode_int4", st)
+    return out
+
+
+def reshape_and_cache_nvfp4(key, value, k_cache, v_cache, k_bscales, v_bscales, slot_mapping,
+                            k_scale, v_scale):
+    """Encode key/value [T][Hkv][D] (bf16 or fp32) into nvfp4 caches
+    [NB][Hkv][16][D/2] (uint8 E2M1 pairs) with block scales
+    [NB][Hkv][16][D/16] (uint8 E4M3) under the per-tensor scales."""
+    t, hkv, d = key.shape
+    assert value.shape == key.shape and key.dtype == value.dtype
+    assert k_cache.shape == v_cache.shape and k_cache.shape[1:] == (hkv, BLOCK_SIZE, d // 2)
+    assert k_bscales.shape == v_bscales.shape == k_cache.shape[:3] + (d // 16,)
+    st = library().reshape_and_cache_nvfp4(
+        _dev(key, "key"), _dev(value, "value"), _dev(k_cache, "k_cache", torch.uint8),
+        _dev(v_cache, "v_cache", torch.uint8), _dev(k_bscales, "k_bscales", torch.uint8),
+        _dev(v_bscales, "v_bscales", torch.uint8),
+        _dev(slot_mapping, "slot_mapping", torch.int64), t, hkv, d, k_cache.shape[0],
+        _dtype_code(key, "key"), float(k_scale), float(v_scale), _stream(key))
+    _check("reshape_and_cache_nvfp4", st)
+
+
+def paged_attention_decode_nvfp4(query, k_cache, v_cache, k_bscales, v_bscales, block_tables,
+                                 context_lens, max_context_len, softmax_scale, k_scale,
+                                 v_scale, partition_tokens=0, out=None, workspace=None):
+    """Decode over nvfp4 caches; same contract as paged_attention_decode."""
+    s, hq, d = query.shape
+    hkv = k_cache.shape[1]
+    if out is None:
+        out = torch.empty_like(query)
+    need = decode_workspace_size(s, hq, hkv, d, max_context_len, partition_tokens)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=query.device)
+    st = library().paged_attention_decode_nvfp4(
+        _dev(out, "out", query.dtype), _dev(query, "query"),
+        _dev(k_cache, "k_cache", torch.uint8), _dev(v_cache, "v_cache", torch.uint8),
+        _dev(k_bscales, "k_bscales", torch.uint8), _dev(v_bscales, "v_bscales", torch.uint8),
+        k_cache.shape[0], _dev(block_tables, "block_tables", torch.int32),
+        block_tables.shape[1], _dev(context_lens, "context_lens", torch.int32), s,
+        int(max_context_len), hq, hkv, d, float(softmax_scale), _dtype_code(query, "query"),
+        float(k_scale), float(v_scale), int(partition_tokens), _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(query))
+    _check("paged_attention_decode_nvfp4", st)
     return out

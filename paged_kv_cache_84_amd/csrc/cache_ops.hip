@@ -3,6 +3,8 @@
 // All three are bound by HBM traffic; they use 16-byte accesses and grids of
 // one workgroup per token / per copied block.
 
+#include <float.h>
+
 #include "abi_util.h"
 #include "common.h"
 
@@ -162,6 +164,71 @@ __global__ __launch_bounds__(256) void reshape_and_cache_int4_kernel(
     const int64_t r = (block * num_kv_heads + h) * kBlock + offset;
     if (on) (is_v ? v_cache : k_cache)[r * (head_dim / 2) + lane] = uint8_t((q0 + 8) | ((q1 + 8) << 4));
     if (lane == 0) (is_v ? v_scales : k_scales)[r] = s;
+  }
+}
+
+// ------------------------------------------------------ nvfp4-style write
+// One wave per (token, K|V, kv head) row: lane L encodes elements 2L and
+// 2L + 1; the eight lanes of a 16-element block share its scale.
+//   scale code  c = E4M3(fp32(fp32(max|x| / 6) / g))
+//   element     E2M1(fp32(x / fp32(S * g))), S the value of c (codes 0 if S = 0)
+// Element 2L goes to the low nibble of byte L; lane 8b writes block b's
+// scale byte.
+
+// binary32 -> E2M1 code: nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6, ties to the
+// even mantissa (so 0.25 -> 0, 0.75 -> 1, 1.25 -> 1, 1.75 -> 2, 2.5 -> 2,
+// 3.5 -> 4, 5 -> 4), above 6 saturates; the sign bit is kept (also of zero).
+// Each comparison adds one step of the magnitude code; `>` where the tie
+// stays below, `>=` where it goes up.
+PKV_DEVICE uint32_t f32_to_e2m1(float y) {
+  const float a = fabsf(y);
+  const uint32_t mag = uint32_t(a > 0.25f) + uint32_t(a >= 0.75f) + uint32_t(a > 1.25f) +
+                       uint32_t(a >= 1.75f) + uint32_t(a > 2.5f) + uint32_t(a >= 3.5f) +
+                       uint32_t(a > 5.0f);
+  return mag | ((__float_as_uint(y) >> 28) & 8u);
+}
+
+template <typename Src>
+__global__ __launch_bounds__(256) void reshape_and_cache_nvfp4_kernel(
+    const typename Src::storage* __restrict__ key,
+    const typename Src::storage* __restrict__ value, uint8_t* __restrict__ k_cache,
+    uint8_t* __restrict__ v_cache, uint8_t* __restrict__ k_bscales,
+    uint8_t* __restrict__ v_bscales, const int64_t* __restrict__ slots, int32_t num_kv_heads,
+    int32_t head_dim, int32_t num_blocks, float k_scale, float v_scale) {
+  const int t = blockIdx.x;
+  const int64_t slot = slots[t];
+  if (slot < 0 || slot >= int64_t(num_blocks) * kBlock) return;
+  const int64_t block = slot / kBlock;
+  const int offset = int(slot % kBlock);
+  const int lane = lane_id();
+  const int wave = int(threadIdx.x) / kWave;
+  const bool on = 2 * lane < head_dim;
+  for (int row = wave; row < 2 * num_kv_heads; row += int(blockDim.x) / kWave) {
+    const bool is_v = row >= num_kv_heads;
+    const int h = is_v ? row - num_kv_heads : row;
+    const typename Src::storage* src =
+        (is_v ? value : key) + (int64_t(t) * num_kv_heads + h) * head_dim;
+    const float x0 = on ? src_to_f32(src[2 * lane]) : 0.f;
+    const float x1 = on ? src_to_f32(src[2 * lane + 1]) : 0.f;
+    float amax = fmaxf(fabsf(x0), fabsf(x1));
+    amax = fmaxf(amax, shfl_xor(amax, 1));
+    amax = fmaxf(amax, shfl_xor(amax, 2));
+    amax = fmaxf(amax, shfl_xor(amax, 4));
+    const float g = is_v ? v_scale : k_scale;
+    const uint8_t sc = f32_to_e4m3((amax / 6.0f) / g);
+    float s, unused;
+    fp8x2_to_f32<false>(uint32_t(sc), s, unused);
+    uint32_t c0 = 0, c1 = 0;
+    if (s > 0.f) {
+      const float den = s * g;
+      c0 = f32_to_e2m1(x0 / den);
+      c1 = f32_to_e2m1(x1 / den);
+    }
+    const int64_t r = (block * num_kv_heads + h) * kBlock + offset;
+    if (on) {
+      (is_v ? v_cache : k_cache)[r * (head_dim / 2) + lane] = uint8_t(c0 | (c1 << 4));
+      if (lane % 8 == 0) (is_v ? v_bscales : k_bscales)[r * (head_dim / 16) + lane / 8] = sc;
+    }
   }
 }
 
@@ -325,6 +392,43 @@ extern "C" pkv_status reshape_and_cache_int4(const void* key, const void* value,
                        as_stream(stream), static_cast<const float*>(key),
                        static_cast<const float*>(value), kc, vc, k_scales, v_scales,
                        slot_mapping, num_kv_heads, head_dim, num_blocks);
+  return launch_status();
+}
+
+extern "C" pkv_status reshape_and_cache_nvfp4(const void* key, const void* value,
+                                              void* k_cache, void* v_cache, void* k_bscales,
+                                              void* v_bscales, const int64_t* slot_mapping,
+                                              int32_t num_tokens, int32_t num_kv_heads,
+                                              int32_t head_dim, int32_t num_blocks,
+                                              pkv_dtype src_dtype, float k_scale,
+                                              float v_scale, void* stream) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || num_blocks < 0)
+    return PKV_ERR_SHAPE;
+  if (!(k_scale > 0.f && v_scale > 0.f && k_scale <= FLT_MAX && v_scale <= FLT_MAX))
+    return PKV_ERR_SHAPE;
+  if (head_dim % 16 != 0 || head_dim > 2 * kWave) return PKV_ERR_UNSUPPORTED;
+  if (src_dtype != PKV_BF16 && src_dtype != PKV_F32) return PKV_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PKV_OK;
+  if (!key || !value || !k_cache || !v_cache || !k_bscales || !v_bscales || !slot_mapping)
+    return PKV_ERR_NULL;
+  if (!aligned(key, 16) || !aligned(value, 16) || !aligned(k_cache, 16) ||
+      !aligned(v_cache, 16) || !aligned(k_bscales, 16) || !aligned(v_bscales, 16) ||
+      !aligned(slot_mapping, 8))
+    return PKV_ERR_ALIGN;
+  auto* kc = static_cast<uint8_t*>(k_cache);
+  auto* vc = static_cast<uint8_t*>(v_cache);
+  auto* ks = static_cast<uint8_t*>(k_bscales);
+  auto* vs = static_cast<uint8_t*>(v_bscales);
+  if (src_dtype == PKV_BF16)
+    hipLaunchKernelGGL(reshape_and_cache_nvfp4_kernel<BF16>, dim3(num_tokens), dim3(256), 0,
+                       as_stream(stream), static_cast<const uint16_t*>(key),
+                       static_cast<const uint16_t*>(value), kc, vc, ks, vs, slot_mapping,
+                       num_kv_heads, head_dim, num_blocks, k_scale, v_scale);
+  else
+    hipLaunchKernelGGL(reshape_and_cache_nvfp4_kernel<F32>, dim3(num_tokens), dim3(256), 0,
+                       as_stream(stream), static_cast<const float*>(key),
+                       static_cast<const float*>(value), kc, vc, ks, vs, slot_mapping,
+                       num_kv_heads, head_dim, num_blocks, k_scale, v_scale);
   return launch_status();
 }
 

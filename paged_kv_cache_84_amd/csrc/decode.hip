@@ -692,6 +692,14 @@ struct DecodePlan {
 #define PKV_INT4_WAVES_PER_SIMD 4
 #endif
 constexpr int kInt4WavesPerSimd = PKV_INT4_WAVES_PER_SIMD;
+// nvfp4 blocks carry about as many bytes as int4 ones, with more vector work
+// per block (the block scales are applied before the products).
+#ifndef PKV_NVFP4_WAVES_PER_SIMD
+#define PKV_NVFP4_WAVES_PER_SIMD 4
+#endif
+constexpr int kNvfp4WavesPerSimd = PKV_NVFP4_WAVES_PER_SIMD;
+// paged_attention_decode_workspace_size sizes for the finest split
+static_assert(kNvfp4WavesPerSimd <= kInt4WavesPerSimd, "workspace sized by the int4 plan");
 static bool make_plan(int32_t s, int32_t hq, int32_t hkv, int32_t d, int32_t max_len,
                       int32_t partition_tokens, DecodePlan& p, int waves_per_simd = 1) {
   if (s < 0 || hq <= 0 || hkv <= 0 || d <= 0 || max_len < 0 || hq % hkv != 0) return false;
@@ -834,8 +842,8 @@ namespace pkv {
 #define PKV_FP8_WAVES_PER_SIMD 3
 #endif
 static pkv_status mfma_decode(void* out, const void* query, const void* k_cache,
-                              const void* v_cache, const float* k_scales,
-                              const float* v_scales, int32_t num_blocks,
+                              const void* v_cache, const void* k_scales,
+                              const void* v_scales, int32_t num_blocks,
                               const int32_t* block_tables, int32_t max_blocks_per_seq,
                               const int32_t* context_lens, int32_t num_seqs,
                               int32_t max_context_len, int32_t num_q_heads,
@@ -1029,4 +1037,42 @@ extern "C" pkv_status paged_attention_decode_int4(
                      block_tables, max_blocks_per_seq, context_lens, num_seqs, max_context_len,
                      num_q_heads, num_kv_heads, head_dim, softmax_scale * kLog2e, PKV_INT4,
                      1.0f, lay, workspace, stream);
+}
+
+extern "C" pkv_status paged_attention_decode_nvfp4(
+    void* out, const void* query, const void* k_cache, const void* v_cache,
+    const void* k_bscales, const void* v_bscales, int32_t num_blocks,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+    int32_t num_seqs, int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, float softmax_scale, pkv_dtype q_dtype, float k_scale, float v_scale,
+    int32_t partition_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_seqs < 0 || num_blocks < 0 || max_blocks_per_seq < 0 || max_context_len < 0 ||
+      num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0)
+    return PKV_ERR_SHAPE;
+  if (num_q_heads % num_kv_heads != 0) return PKV_ERR_SHAPE;
+  if (int64_t(max_blocks_per_seq) * kBlock < max_context_len) return PKV_ERR_SHAPE;
+  if (!(k_scale > 0.f && v_scale > 0.f)) return PKV_ERR_SHAPE;
+  const int group = num_q_heads / num_kv_heads;
+  if (group > 8 || head_dim != 128 || q_dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+  if (partition_tokens < 0 || partition_tokens % kBlock != 0) return PKV_ERR_SHAPE;
+  if (num_seqs == 0) return PKV_OK;
+  if (num_blocks == 0) return PKV_ERR_SHAPE;
+  if (!out || !query || !k_cache || !v_cache || !k_bscales || !v_bscales || !block_tables ||
+      !context_lens)
+    return PKV_ERR_NULL;
+  if (!aligned(out, 16) || !aligned(query, 16) || !aligned(k_cache, 16) ||
+      !aligned(v_cache, 16) || !aligned(k_bscales, 16) || !aligned(v_bscales, 16) ||
+      !aligned(block_tables, 4) || !aligned(context_lens, 4))
+    return PKV_ERR_ALIGN;
+  DecodePlan lay;
+  if (!make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                 partition_tokens, lay, kNvfp4WavesPerSimd) ||
+      int64_t(num_seqs) * num_q_heads > 0x7fffffff)
+    return PKV_ERR_SHAPE;
+  if (!workspace || workspace_bytes < lay.out_bytes + lay.ml_bytes) return PKV_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return PKV_ERR_ALIGN;
+  return mfma_decode(out, query, k_cache, v_cache, k_bscales, v_bscales, num_blocks,
+                     block_tables, max_blocks_per_seq, context_lens, num_seqs, max_context_len,
+                     num_q_heads, num_kv_heads, head_dim, softmax_scale * k_scale * kLog2e,
+                     PKV_NVFP4, v_scale, lay, workspace, stream);
 }

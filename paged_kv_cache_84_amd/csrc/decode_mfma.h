@@ -25,13 +25,15 @@ struct DecodeMfmaArgs {
   float* rec_out;                    // partials of sequences that span chunks
   float* rec_ml;
   void* stream;
-  const float* k_scales = nullptr;   // int4 caches: per (block, kv head, slot) scales
-  const float* v_scales = nullptr;
+  // int4 caches: float scales per (block, kv head, slot); nvfp4 caches: E4M3
+  // block-scale bytes per (block, kv head, slot, 16 elements)
+  const void* k_scales = nullptr;
+  const void* v_scales = nullptr;
   int32_t window = 0;                // sliding window in tokens (0 = none)
 };
 
-// bf16 queries with a bf16 or fp8 E4M3 cache (head_dim 64 or 128) or an int4
-// per token-head cache (head_dim 128); group <= 16.
+// bf16 queries with a bf16 or fp8 E4M3 cache (head_dim 64 or 128), or an int4
+// per token-head or nvfp4-style cache (head_dim 128); group <= 16.
 bool decode_mfma_supported(pkv_dtype q_dtype, pkv_dtype kv_dtype, int head_dim, int group);
 // Launches the chunk kernel only; the caller launches the merge.
 pkv_status launch_decode_mfma(const DecodeMfmaArgs& a);

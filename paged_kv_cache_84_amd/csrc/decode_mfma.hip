@@ -1,5 +1,5 @@
-// Paged decode attention on the matrix cores of gfx950 (bf16 queries; bf16
-// or fp8 E4M3 cache).
+// Paged decode attention on the matrix cores of gfx950 (bf16 queries; bf16,
+// fp8 E4M3, int4 per token-head or nvfp4-style cache).
 //
 // Decode reads every K/V block of a sequence once per step and is bound by
 // HBM bandwidth ("vLLM 引擎解剖", section "预填充、解码与三个时延指标"); the
@@ -27,7 +27,9 @@
 //     4e + j/4 (e = 0..3), so lane 4k + q addressing key k, dims 4q..4q+3 of
 //     a 16-dim slice hands every lane the 4 keys of its dim.
 // fp8 tiles are widened to bf16 in registers (exact); k_scale is folded into
-// the softmax scale and v_scale into the final normalisation.
+// the softmax scale and v_scale into the final normalisation.  nvfp4 tiles
+// are widened the same way: each E2M1 code times its 16-element block's E4M3
+// scale has at most six significant bits, so the bf16 result is exact.
 
 #include <math.h>
 
@@ -72,8 +74,21 @@ struct INT4 {
 };
 template <typename KVT>
 constexpr bool kInt4 = std::is_same<KVT, INT4>::value;
+
+// nvfp4-style cache: two E2M1 codes per byte (element 2i in the low nibble),
+// one E4M3 scale byte per 16 elements of a row in a separate array
+// [block][kv head][16][D / 16]; the per-tensor scales are the k_scale and
+// v_scale of the fp8 cache.
+struct NVFP4 {
+  using storage = uint8_t;
+  static constexpr int bytes = 0;
+};
 template <typename KVT>
-constexpr int kElemBits = kInt4<KVT> ? 4 : 8 * KVT::bytes;
+constexpr bool kNvfp4 = std::is_same<KVT, NVFP4>::value;
+template <typename KVT>
+constexpr bool kPacked4 = kInt4<KVT> || kNvfp4<KVT>;   // 4-bit codes, two per byte
+template <typename KVT>
+constexpr int kElemBits = kPacked4<KVT> ? 4 : 8 * KVT::bytes;
 
 // 136 in bf16: an int4 element enters the products as 128 + u = 136 + q (a
 // bf16 with the nibble in its low mantissa bits), and 136 * (sum of the
@@ -104,10 +119,10 @@ struct MGeom {
   static constexpr int kRowBytes = D * kElemBits<KVT> / 8;   // one cache row
   static constexpr int kTileBytes = kBlock * kRowBytes;
   static constexpr int kVLoads = kTileBytes / (kWave * 16);  // 16-byte V pieces per lane
-  static constexpr int kKLoads = kInt4<KVT> ? kKSteps / 4 : KVT::bytes == 2 ? kKSteps : kKSteps / 2;
+  static constexpr int kKLoads = kPacked4<KVT> ? kKSteps / 4 : KVT::bytes == 2 ? kKSteps : kKSteps / 2;
   static constexpr int kVStride = D * 2 + 32;          // LDS bytes per staged bf16 V row
   static_assert(kKSteps >= 2 && kVLoads >= 1, "unsupported head size");
-  static_assert(!kInt4<KVT> || D == 128, "int4 caches: head_dim 128");
+  static_assert(!kPacked4<KVT> || D == 128, "4-bit caches: head_dim 128");
 };
 
 // First dim of the 8 consecutive dims that lane group j feeds to QK product ks
@@ -115,25 +130,57 @@ struct MGeom {
 // each lane's 16-byte load cover two products).
 template <typename KVT>
 PKV_DEVICE int qk_dim(int j, int ks) {
-  if constexpr (kInt4<KVT>) return 32 * j + 8 * ks;   // one 16-byte load = 32 dims
+  if constexpr (kPacked4<KVT>) return 32 * j + 8 * ks;   // one 16-byte load = 32 dims
   else return KVT::bytes == 2 ? 8 * j + 32 * ks : 16 * j + 64 * (ks / 2) + 8 * (ks % 2);
 }
 
 template <typename KVT, int D>
 struct KRegs {
   u32x4 v[MGeom<KVT, D>::kKLoads];
-  u32x4 sc;       // int4: the scales of this lane's four keys
+  u32x4 sc;       // int4: the scales of this lane's four keys; nvfp4: see load_bscales
 };
 template <typename KVT, int D>
 struct VRegs {
   u32x4 v[MGeom<KVT, D>::kVLoads];
-  u32x4 sc;       // int4: the scales of this lane's four keys
+  u32x4 sc;       // int4: the scales of this lane's four keys; nvfp4: see load_bscales
 };
 
 // int4: the scales of keys 4 (lane/16) .. + 3 of one (block, kv head) row
 // set of a scale array (16 floats per (block, kv head)).
 PKV_DEVICE u32x4 load_scales(const float* row16, int lane) {
   return buffer_load16(tile_resource(row16, kBlock * 4), uint32_t((lane / 16) * 16));
+}
+
+// nvfp4: the two block-scale bytes of this lane's 32 dims -- dims 32 q .. +31
+// of row r are blocks 2q and 2q + 1, bytes 8 r + 2q and + 1 of the (block,
+// kv head) scale tile (128 bytes); K lanes hold row lane%16, q = lane/16, V
+// lanes row lane/4, q = lane%4.  The aligned dword holding the pair is
+// loaded and the pair moved to the low half of sc[0].
+PKV_DEVICE uint32_t load_bscales(const uint8_t* tile128, uint32_t byte_offset) {
+  const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(
+      tile_resource(tile128, kBlock * 8), byte_offset & ~3u, 0, 0);
+  return (byte_offset & 2u) ? (w >> 16) : w;
+}
+PKV_DEVICE uint32_t k_bscale_offset(int lane) { return uint32_t((lane % 16) * 8 + (lane / 16) * 2); }
+PKV_DEVICE uint32_t v_bscale_offset(int lane) { return uint32_t(lane * 2); }
+
+// nvfp4: eight E2M1 codes (a little-endian dword, element 2e in the low
+// nibble of byte e) times the block scale s -> four dwords of bf16 pairs.
+// The codes are widened with unit scale (the converter applies only the
+// exponent of its scale operand), then multiplied by s in binary32: exact,
+// as is the bf16 truncation of the product.
+template <int kByte>
+PKV_DEVICE uint32_t fp4x2_to_bf16(uint32_t w, float s) {
+  const auto f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, kByte);
+  return pack_bf16_rne(f[0] * s, f[1] * s);
+}
+PKV_DEVICE u32x4 fp4x8_to_bf16(uint32_t w, float s) {
+  return u32x4{fp4x2_to_bf16<0>(w, s), fp4x2_to_bf16<1>(w, s), fp4x2_to_bf16<2>(w, s),
+               fp4x2_to_bf16<3>(w, s)};
+}
+// The two block scales of a lane (bytes 0, 1 of `pair`) as binary32 values.
+PKV_DEVICE void bscales_f32(uint32_t pair, float& s0, float& s1) {
+  fp8x2_to_f32<false>(pair, s0, s1);
 }
 
 template <typename KVT, int D>
@@ -158,6 +205,11 @@ template <typename KVT, int D>
 PKV_DEVICE u32x4 k_operand(const KRegs<KVT, D>& r, int ks) {
   if constexpr (kInt4<KVT>) {
     return int4x8_to_bf16_offset(r.v[0][ks]);
+  } else if constexpr (kNvfp4<KVT>) {
+    // dword ks holds dims 32 (lane/16) + 8 ks .. + 7: block 2 (lane/16) + ks/2
+    float s0, s1;
+    bscales_f32(r.sc[0], s0, s1);
+    return fp4x8_to_bf16(r.v[0][ks], ks < 2 ? s0 : s1);
   } else if constexpr (KVT::bytes == 2) {
     return r.v[ks];
   } else {
@@ -175,6 +227,20 @@ PKV_DEVICE u32x4 k_operand(const KRegs<KVT, D>& r, int ks) {
 template <typename KVT, int D>
 PKV_DEVICE void stage_v(VRegs<KVT, D>& r, char* vl, int lane, int rows) {
   using M = MGeom<KVT, D>;
+  if constexpr (kNvfp4<KVT>) {
+    // lane L holds dims 32 (L%4) .. + 31 of key L/4 (dwords 0, 1: block
+    // 2 (L%4); dwords 2, 3: the next); rows past `rows` may hold any byte,
+    // NaN scales included, and become zeros
+    char* dst = vl + (lane / 4) * M::kVStride + (lane % 4) * 64;
+    float s0, s1;
+    bscales_f32(r.sc[0], s0, s1);
+    const bool live = lane / 4 < rows;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      *reinterpret_cast<u32x4*>(dst + 16 * w) =
+          live ? fp4x8_to_bf16(r.v[0][w], w < 2 ? s0 : s1) : u32x4{0, 0, 0, 0};
+    return;
+  }
   if constexpr (kInt4<KVT>) {
     // lane L holds dims 32 (L%4) .. + 31 of key L/4; every code is a finite
     // bf16 (128 + u), and rows past `rows` get zero weight, so nothing is
@@ -194,7 +260,7 @@ PKV_DEVICE void stage_v(VRegs<KVT, D>& r, char* vl, int lane, int rows) {
   for (int i = 0; i < M::kVLoads; ++i) {
     const int o = lane * 16 + i * 1024;         // byte offset in the cache tile
     const int row = o / M::kRowBytes;
-    const int col = (o % M::kRowBytes) / (kInt4<KVT> ? 1 : KVT::bytes);
+    const int col = (o % M::kRowBytes) / (kPacked4<KVT> ? 1 : KVT::bytes);
     char* dst = vl + row * M::kVStride + col * 2;
     if constexpr (KVT::bytes == 2) {
       *reinterpret_cast<u32x4*>(dst) = r.v[i];
@@ -242,7 +308,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
     int32_t num_q_heads, int32_t num_kv_heads, int32_t group, float scale_log2,
     float v_scale, int32_t num_chunks, int32_t fixed_chunk, int32_t chunks_per_wave,
     float* __restrict__ rec_out, float* __restrict__ rec_ml,
-    const float* __restrict__ k_scales, const float* __restrict__ v_scales, int32_t window) {
+    const void* __restrict__ k_scales, const void* __restrict__ v_scales, int32_t window) {
   using M = MGeom<KVT, D>;
   __shared__ __align__(16) char vl[kBlock * M::kVStride];
   const int kvh = blockIdx.x % num_kv_heads;
@@ -268,8 +334,13 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
     return base + int64_t(b) * block_stride + int64_t(kvh) * head_stride;
   };
   auto valid = [&](int32_t b) { return b >= 0 && b < num_blocks; };
-  auto scale_row = [&](const float* base, int32_t b) {
-    return base + (int64_t(b) * num_kv_heads + kvh) * kBlock;
+  // int4: the 16 float scales of (block b, kvh); nvfp4: its 128-byte tile
+  // of block scales
+  auto scale_row = [&](const void* base, int32_t b) {
+    return static_cast<const float*>(base) + (int64_t(b) * num_kv_heads + kvh) * kBlock;
+  };
+  auto bscale_tile = [&](const void* base, int32_t b) {
+    return static_cast<const uint8_t*>(base) + (int64_t(b) * num_kv_heads + kvh) * kBlock * 8;
   };
   auto table_id = [&](const SeqCursor& q, int x) -> int32_t {
     const int i = x - q.before + q.first;
@@ -324,9 +395,11 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
   // the loop covers exactly the pieces it needs
   load_v<KVT, D>(vr, tile(v_cache, b_any), lane);
   if constexpr (kInt4<KVT>) vr.sc = load_scales(scale_row(v_scales, b_any), lane);
+  if constexpr (kNvfp4<KVT>) vr.sc[0] = load_bscales(bscale_tile(v_scales, b_any), v_bscale_offset(lane));
   __builtin_amdgcn_sched_barrier(0);
   load_k<KVT, D>(kr, tile(k_cache, b_any), lane);
   if constexpr (kInt4<KVT>) kr.sc = load_scales(scale_row(k_scales, b_any), lane);
+  if constexpr (kNvfp4<KVT>) kr.sc[0] = load_bscales(bscale_tile(k_scales, b_any), k_bscale_offset(lane));
   __builtin_amdgcn_sched_barrier(0);
 
   f32x4_t acc[M::kMTiles];
@@ -353,6 +426,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
     __builtin_amdgcn_sched_barrier(0);
     load_v<KVT, D>(vr, tile(v_cache, bn), lane);
     if constexpr (kInt4<KVT>) vr.sc = load_scales(scale_row(v_scales, bn), lane);
+    if constexpr (kNvfp4<KVT>) vr.sc[0] = load_bscales(bscale_tile(v_scales, bn), v_bscale_offset(lane));
     __builtin_amdgcn_sched_barrier(0);
     // Q of a sequence entered by the next block
     const bool new_seq = more && x + 1 >= lc.before + lc.n;
@@ -374,6 +448,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
     const u32x4 ksc = kr.sc;          // int4: this block's K scales (before the reload)
     load_k<KVT, D>(kr, tile(k_cache, bn), lane);
     if constexpr (kInt4<KVT>) kr.sc = load_scales(scale_row(k_scales, bn), lane);
+    if constexpr (kNvfp4<KVT>) kr.sc[0] = load_bscales(bscale_tile(k_scales, bn), k_bscale_offset(lane));
     // online softmax over this lane's 4 keys of its head
     float sv[4];
     bool raise = false;
@@ -505,7 +580,7 @@ static pkv_status launch_one(const DecodeMfmaArgs& a) {
 }
 
 bool decode_mfma_supported(pkv_dtype q_dtype, pkv_dtype kv_dtype, int head_dim, int group) {
-  if (kv_dtype == PKV_INT4)
+  if (kv_dtype == PKV_INT4 || kv_dtype == PKV_NVFP4)
     return q_dtype == PKV_BF16 && head_dim == 128 && group >= 1 && group <= 16;
   return q_dtype == PKV_BF16 && (kv_dtype == PKV_BF16 || kv_dtype == PKV_FP8_E4M3) &&
          (head_dim == 64 || head_dim == 128) && group >= 1 && group <= 16;
@@ -513,6 +588,7 @@ bool decode_mfma_supported(pkv_dtype q_dtype, pkv_dtype kv_dtype, int head_dim, 
 
 pkv_status launch_decode_mfma(const DecodeMfmaArgs& a) {
   if (a.kv_dtype == PKV_INT4) return launch_one<INT4, 128>(a);
+  if (a.kv_dtype == PKV_NVFP4) return launch_one<NVFP4, 128>(a);
   if (a.kv_dtype == PKV_BF16)
     return a.head_dim == 64 ? launch_one<BF16, 64>(a) : launch_one<BF16, 128>(a);
   return a.head_dim == 64 ? launch_one<FP8, 64>(a) : launch_one<FP8, 128>(a);

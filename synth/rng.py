@@ -92,3 +92,12 @@ def int4_scales(shape, config_id, purpose, device="cpu", lo=0.05, hi=0.6):
     rows of 128 values lies near 0.4)."""
     g = value_generator(config_id, purpose, device)
     return lo + (hi - lo) * torch.rand(shape, generator=g, device=device, dtype=torch.float32)
+
+
+def nvfp4_bscales(shape, config_id, purpose, device="cpu", lo=0x28, hi=0x3A):
+    """nvfp4 block-scale bytes: E4M3 codes uniform in [lo, hi) (0x28 .. 0x39
+    are 0.25 .. 1.125, the range max|x| / 6 of N(0, 1) blocks of 16 lands
+    in under a unit per-tensor scale); uint8 ``shape``."""
+    g = value_generator(config_id, purpose, device)
+    return torch.randint(lo, hi, shape, generator=g, device=device, dtype=torch.int32).to(
+        torch.uint8)

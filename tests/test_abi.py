@@ -279,3 +279,49 @@ def test_sliding_errors(lib):
     assert call(a14=F32, a15=F32) == UNSUP  # the window is built into the matrix-core path
     assert call(a0=None) == NULL
     assert call(a21=need - 1) == WS
+
+
+def test_nvfp4_errors(lib):
+    f = lib.reshape_and_cache_nvfp4
+    p = 0x100000
+    base = [p, p, p, p, p, p, p, 4, 8, 128, 100, BF16, 1.0, 1.0, None]
+
+    def call(**k):
+        a = list(base)
+        for i, v in k.items():
+            a[int(i[1:])] = v
+        return f(*a)
+
+    assert call(a7=0) == OK
+    assert call(a5=None) == NULL
+    assert call(a4=p + 4) == ALIGN
+    assert call(a9=144) == UNSUP          # more than 128 elements per row
+    assert call(a9=40) == UNSUP           # not a multiple of 16
+    assert call(a11=FP8) == UNSUP
+    assert call(a8=0) == SHAPE
+    assert call(a12=0.0) == SHAPE
+    assert call(a13=-1.0) == SHAPE
+    assert call(a13=float("inf")) == SHAPE
+    d = lib.paged_attention_decode_nvfp4
+    need = lib.paged_attention_decode_workspace_size(4, 32, 8, 128, 1000, 0)
+    dbase = [p, p, p, p, p, p, 100, p, 63, p, 4, 1000, 32, 8, 128, 0.088, BF16, 1.0, 1.0, 0,
+             p, need, None]
+
+    def dcall(**k):
+        a = list(dbase)
+        for i, v in k.items():
+            a[int(i[1:])] = v
+        return d(*a)
+
+    assert dcall(a10=0) == OK
+    assert dcall(a4=None) == NULL
+    assert dcall(a5=p + 4) == ALIGN
+    assert dcall(a14=64) == UNSUP
+    assert dcall(a16=F32) == UNSUP
+    assert dcall(a12=72) == UNSUP         # group 9
+    assert dcall(a8=62) == SHAPE          # 992 tokens < max_context_len
+    assert dcall(a19=100) == SHAPE        # partition not a multiple of 16
+    assert dcall(a17=0.0) == SHAPE
+    assert dcall(a18=-2.0) == SHAPE
+    assert dcall(a21=need - 1) == WS
+    assert dcall(a20=None) == WS
