@@ -1,7 +1,8 @@
 """Benchmark of the paged-attention hot path on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
-                    [--no-mixed] [--no-longctx] [--no-mha] [--no-swap] [--no-window] [--no-int4] [--no-blocks]
+                    [--no-mixed] [--no-longctx] [--no-mha] [--no-swap] [--no-window] [--no-int4] [--no-nvfp4]
+                    [--no-blocks]
     python bench.py --copy-calibration     (a plain 1 GiB device copy, for
                                             the HBM byte counters' scale)
 
@@ -17,7 +18,7 @@ KV tokens/s, the decode call's roofline fraction, the oracle's CPU rate on a
 bounded sample, the mixed unified step with chunked prefill (MFMA
 utilisation of the prefill call), the fp8 long-context decode, the
 32-layer MHA decode step, the 8B batch with a sliding window and over an
-int4 per token-head cache,
+int4 per token-head cache and over an nvfp4-style cache,
 a device <-> host block swap of one long sequence, and the host block manager's operations per second on a serving
 trace (with the oracle's rate on a bounded sample beside it).  The roofline's "traffic" is the HBM bytes per
 decode call that rocprofv3's FETCH_SIZE and WRITE_SIZE counters measured
@@ -469,6 +470,48 @@ def bench_int4(args, pk, step, copies=3):
             "kv_tokens_per_s": round(tokens / (ms * 1e-3), 1)}
 
 
+def bench_nvfp4(args, pk, step, copies=3):
+    """The 8B decode batch over an nvfp4-style cache (E2M1 codes, an E4M3
+    scale per 16 elements, per-tensor scales): decode calls on resident
+    inputs, several pool copies in turn.  Algorithmic bytes: per token and kv
+    head, 64 code bytes and 8 block-scale bytes for K and for V, plus Q and
+    the output."""
+    from synth import rng as R
+    lens = step.decode_context_lens
+    tables = torch.as_tensor(step.decode_block_tables, device="cuda")
+    lens_d = torch.as_tensor(lens, device="cuda")
+    nb = int(step.num_blocks)
+    hq, hkv, d = step.num_q_heads, step.num_kv_heads, step.head_dim
+    q = R.normal((len(lens), hq, d), "bf16", 960, 1, "cuda")
+    pools = [(R.int4_codes((nb, hkv, 16, d // 2), 960, 10 + c, "cuda"),
+              R.int4_codes((nb, hkv, 16, d // 2), 960, 20 + c, "cuda"),
+              R.nvfp4_bscales((nb, hkv, 16, d // 16), 960, 30 + c, "cuda"),
+              R.nvfp4_bscales((nb, hkv, 16, d // 16), 960, 40 + c, "cuda"))
+             for c in range(copies)]
+    out = torch.empty_like(q)
+    ws = torch.empty(pk.decode_workspace_size(len(lens), hq, hkv, d, int(lens.max())),
+                     dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def run(i):
+        kc, vc, ks, vs = pools[i % copies]
+        pk.paged_attention_decode_nvfp4(q, kc, vc, ks, vs, tables, lens_d, int(lens.max()),
+                                        step.softmax_scale, 1.0, 1.0, out=out, workspace=ws)
+
+    for i in range(args.warmup):
+        run(i)
+    ms = time_region(run, args.steps, stream)
+    tokens = int(lens.sum())
+    nbytes = tokens * hkv * 2 * (d // 2 + d // 16) + 2 * len(lens) * hq * d * 2
+    return {"workload": "Llama-3.1-8B-shaped decode layer over an nvfp4-style cache (E2M1, "
+                        "E4M3 scale per 16 elements): 64 sequences, context 512..4096, "
+                        "32 q / 8 kv heads, d128, bf16 q",
+            "ms_per_call": round(ms, 4), "algorithmic_bytes": nbytes,
+            "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "kv_tokens_per_s": round(tokens / (ms * 1e-3), 1)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -486,6 +529,8 @@ def main():
                     help="skip the sliding-window decode of the 8B batch")
     ap.add_argument("--no-int4", action="store_true",
                     help="skip the int4 per token-head decode of the 8B batch")
+    ap.add_argument("--no-nvfp4", action="store_true",
+                    help="skip the nvfp4-style decode of the 8B batch")
     ap.add_argument("--no-blocks", action="store_true",
                     help="skip the host block manager on a serving trace")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -556,6 +601,8 @@ def main():
         line["window_decode"] = bench_window(args, pk, dss[0], step)
     if not args.no_int4:
         line["int4_decode"] = bench_int4(args, pk, step)
+    if not args.no_nvfp4:
+        line["nvfp4_decode"] = bench_nvfp4(args, pk, step)
     if not args.no_swap:
         line["swap_blocks"] = bench_swap(args, pk)
     if not args.no_blocks:
