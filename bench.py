@@ -72,6 +72,7 @@ def prefill_flops(step):
 # profiles/ are used only while these hash to the value recorded with them.
 DECODE_SOURCES = ("paged_kv_cache_84_amd/csrc/decode.hip",
                   "paged_kv_cache_84_amd/csrc/decode_mfma.hip",
+                  "paged_kv_cache_84_amd/csrc/decode_mfma.h",
                   "paged_kv_cache_84_amd/csrc/decode_sched.h",
                   "paged_kv_cache_84_amd/csrc/common.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_llama3_8b_64seq_traffic.md")
