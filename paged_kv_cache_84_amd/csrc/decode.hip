@@ -575,7 +575,10 @@ __global__ __launch_bounds__(256) void prefill_rows_kernel(
 // passed through LDS, so the partials' loads do not wait on each other.  The
 // waves' sums meet in LDS at the end.  (W = 4 for fixed partitions, which
 // leave hundreds of partials per sequence; 1 for the library's own split,
-// which leaves a few.)
+// which leaves a few: up to kFewParts of them are merged from one round of
+// loads, pairs and vectors together.)
+constexpr int kFewParts = 8;   // partials merged by the single-load path
+
 template <typename QT, int D, int W>
 __global__ __launch_bounds__(kWave * W) void decode_merge_kernel(
     typename QT::storage* __restrict__ out, const float* __restrict__ rec_out,
@@ -611,6 +614,33 @@ __global__ __launch_bounds__(kWave * W) void decode_merge_kernel(
   const int64_t base = int64_t(g0 + seq) * num_q_heads + h;
   const int64_t stride = num_q_heads;
   const float2* ml = reinterpret_cast<const float2*>(rec_ml) + base;
+  if (W == 1 && nparts <= kFewParts) {
+    // A few partials (the library's own split): their (max, sum) pairs and
+    // their vectors are loaded at once, so the vectors do not wait for the
+    // weights; lane k < nparts holds partial k's pair.
+    float x[kFewParts][kPer];
+    const float* po = rec_out + base * D + lane;
+#pragma unroll
+    for (int j = 0; j < kFewParts; ++j)
+#pragma unroll
+      for (int i = 0; i < kPer; ++i)
+        x[j][i] = j < nparts ? po[j * stride * D + i * kWave] : 0.f;
+    const float2 mine = lane < nparts ? ml[lane * stride] : make_float2(-INFINITY, 0.f);
+    const float big = wave_max(mine.x);
+    const float wk = lane < nparts ? fast_exp2(mine.x - big) : 0.f;
+    const float den = wave_sum(wk * mine.y);
+    float acc[kPer] = {};
+#pragma unroll
+    for (int j = 0; j < kFewParts; ++j) {
+      const float wj = __shfl(wk, j, kWave);
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) acc[i] = fmaf(wj, x[j][i], acc[i]);
+    }
+    const float f = v_scale / den;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) store_out<QT>(o + lane + i * kWave, acc[i] * f);
+    return;
+  }
   float big = -INFINITY;
   for (int k = lane; k < nparts; k += kWave) big = fmaxf(big, ml[k * stride].x);
   big = wave_max(big);
