@@ -267,3 +267,32 @@ def test_decode_all_sequences_empty():
                               torch.as_tensor(lens, device=DEV), 16, 0.1, out=out)
     torch.cuda.synchronize()
     assert torch.all(out == 0)
+
+
+@pytest.mark.parametrize("long_len", [9000, 40000])
+def test_decode_library_split_many_partials(long_len):
+    """The library's own split with one long sequence among short ones: the
+    long one spans tens of chunks (many partials, merged by the looping
+    path), the short ones one or two (merged from a single round of loads or
+    written directly).  Every output of the short sequences and sampled heads
+    of the long one against the oracle."""
+    announce("decode library split, long sequence", long_len)
+    lengths = [long_len, 100, 37, 300, 16, 1, 250, 999]
+    q, kc, vc, tables, lens, ks, vs = _random_decode(32, 8, 128, F.BF16, F.BF16, lengths,
+                                                     seed=long_len)
+    chunks = pk.decode_num_chunks(len(lengths), 32, 8, long_len, 0)
+    total_blocks = sum(P.blocks_needed(n) for n in lengths)
+    assert P.blocks_needed(long_len) * chunks // total_blocks > 8   # the looping path
+    out = pk.paged_attention_decode(q, kc, vc, torch.as_tensor(tables, device=DEV),
+                                    torch.as_tensor(lens, device=DEV), int(lens.max()),
+                                    0.088, 1.0, 1.0, 0)
+    torch.cuda.synchronize()
+    got = as_f64(out)
+    hq_, kc_, vc_ = host(q), host(kc), host(vc)
+    ref_short = P.decode_attention(hq_[1:], F.BF16, kc_, vc_, F.BF16, tables[1:], lens[1:],
+                                   0.088, 1.0, 1.0)
+    assert_attention_close(got[1:], ref_short, "bf16", "short sequences")
+    heads = [0, 7, 13, 31]
+    ref_long = np.stack([P.decode_attention_one(hq_, F.BF16, kc_, vc_, F.BF16, tables, lens,
+                                                0.088, 0, h) for h in heads])
+    assert_attention_close(got[0, heads], ref_long, "bf16", "long sequence")
