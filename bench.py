@@ -2,7 +2,7 @@
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
                     [--no-mixed] [--no-longctx] [--no-mha] [--no-swap] [--no-window] [--no-int4] [--no-nvfp4]
-                    [--no-blocks]
+                    [--no-blocks] [--no-ceilings]
     python bench.py --copy-calibration     (a plain 1 GiB device copy, for
                                             the HBM byte counters' scale)
 
@@ -19,7 +19,9 @@ bounded sample, the mixed unified step with chunked prefill (MFMA
 utilisation of the prefill call), the fp8 long-context decode, the
 32-layer MHA decode step, the 8B batch with a sliding window and over an
 int4 per token-head cache and over an nvfp4-style cache,
-a device <-> host block swap of one long sequence, and the host block manager's operations per second on a serving
+a device <-> host block swap of one long sequence, measured ceilings (a streaming HBM read
+with the decode's loads, a register-only bf16 MFMA loop) that the decode and prefill rates are
+also read against, and the host block manager's operations per second on a serving
 trace (with the oracle's rate on a bounded sample beside it).  The roofline's "traffic" is the HBM bytes per
 decode call that rocprofv3's FETCH_SIZE and WRITE_SIZE counters measured
 (profiles/decode_llama3_8b_64seq_traffic.md), used only while the decode
@@ -513,6 +515,41 @@ def bench_nvfp4(args, pk, step, copies=3):
             "kv_tokens_per_s": round(tokens / (ms * 1e-3), 1)}
 
 
+def xor_of_range(n):
+    """XOR of the integers 0 .. n-1 (closed form by n mod 4)."""
+    x = n - 1
+    return [x, 1, x + 1, 0][x % 4] if n > 0 else 0
+
+
+def bench_ceilings(args, pk, read_bytes=4 << 30, mfma_waves=4096, mfma_iters=4096):
+    """Measured ceilings: a streaming read of 4 GiB with the decode's
+    16-byte non-temporal loads (the buffer holds the word ramp 0, 1, 2, ...,
+    whose XOR checks that every word was read), and a register-only loop of
+    the prefill's bf16 MFMA on 4 waves per SIMD (each wave's result checks
+    that every product was issued)."""
+    stream = torch.cuda.current_stream()
+    words = torch.arange(read_bytes // 4, dtype=torch.int32, device="cuda")
+    checksum = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for _ in range(2):
+        pk.measure_hbm_read(words, checksum)
+    ms_read = time_region(lambda i: pk.measure_hbm_read(words, checksum), 5, stream)
+    got = int(checksum.cpu().numpy().view(np.uint32)[0])
+    assert got == xor_of_range(read_bytes // 4), "HBM read checksum mismatch"
+    del words
+    result = torch.zeros(mfma_waves, dtype=torch.float32, device="cuda")
+    pk.measure_mfma_bf16(mfma_iters, result)
+    ms_mfma = time_region(lambda i: pk.measure_mfma_bf16(mfma_iters, result), 3, stream)
+    assert bool(torch.all(result == 32.0 * mfma_iters)), "MFMA loop result mismatch"
+    read_gbs = read_bytes / (ms_read * 1e-3) / 1e9
+    tflops = mfma_waves * mfma_iters * 8 * 16384 / (ms_mfma * 1e-3) / 1e12
+    return {"hbm_read": {"bytes": read_bytes, "ms": round(ms_read, 4),
+                         "gbs": round(read_gbs, 1),
+                         "frac_of_peak": round(read_gbs / HBM_PEAK_GBS, 4)},
+            "mfma_bf16": {"waves": mfma_waves, "mfma_per_wave": mfma_iters * 8,
+                          "ms": round(ms_mfma, 4), "tflops": round(tflops, 1),
+                          "frac_of_peak": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4)}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -532,6 +569,8 @@ def main():
                     help="skip the int4 per token-head decode of the 8B batch")
     ap.add_argument("--no-nvfp4", action="store_true",
                     help="skip the nvfp4-style decode of the 8B batch")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the measured HBM-read and MFMA ceilings")
     ap.add_argument("--no-blocks", action="store_true",
                     help="skip the host block manager on a serving trace")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -604,6 +643,14 @@ def main():
         line["int4_decode"] = bench_int4(args, pk, step)
     if not args.no_nvfp4:
         line["nvfp4_decode"] = bench_nvfp4(args, pk, step)
+    if not args.no_ceilings:
+        ceil = bench_ceilings(args, pk)
+        ceil["decode_call_frac_of_read_ceiling"] = round(
+            line["roofline"]["achieved"] / ceil["hbm_read"]["gbs"], 4)
+        if "mixed_step" in line:
+            ceil["prefill_frac_of_mfma_ceiling"] = round(
+                line["mixed_step"]["prefill_tflops"] / ceil["mfma_bf16"]["tflops"], 4)
+        line["ceilings"] = ceil
     if not args.no_swap:
         line["swap_blocks"] = bench_swap(args, pk)
     if not args.no_blocks:

@@ -22,6 +22,8 @@ from ._binding import (  # noqa: F401
     kv_bytes_per_token,
     library,
     library_path,
+    measure_hbm_read,
+    measure_mfma_bf16,
     varlen_workspace_size,
     paged_attention_decode,
     paged_attention_decode_int4,

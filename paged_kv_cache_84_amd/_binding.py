@@ -64,6 +64,9 @@ _SIGNATURES = {
     "paged_attention_prefill_chunk": (_I32, [_P, _P, _P, _P, _I32, _P, _I32, _P, _P,
                                              _I32, _I32, _I32, _I32, _I32, _I32, _F,
                                              _I32, _I32, _F, _F, _P]),
+    # hardware ceilings (include/pagedkv_measure.h)
+    "pkv_measure_hbm_read": (_I32, [_P, _I64, _P, _P]),
+    "pkv_measure_mfma_bf16": (_I32, [_I32, _I32, _P, _P]),
     # host block manager (include/pagedkv_blocks.h)
     "pkv_bm_create": (_I32, [_I32, _P, _I32, _P]),
     "pkv_bm_destroy": (None, [_P]),
@@ -436,3 +439,21 @@ def paged_attention_decode_nvfp4(query, k_cache, v_cache, k_bscales, v_bscales, 
         workspace.numel() * workspace.element_size(), _stream(query))
     _check("paged_attention_decode_nvfp4", st)
     return out
+
+
+def measure_hbm_read(buf, checksum):
+    """Stream every byte of the device tensor `buf` (16-byte multiple) with
+    the decode's load kind; `checksum` (int32 [1], device) receives the XOR
+    of its 32-bit words."""
+    nbytes = buf.numel() * buf.element_size()
+    st = library().pkv_measure_hbm_read(_dev(buf, "buf"), nbytes,
+                                        _dev(checksum, "checksum", torch.int32), _stream(buf))
+    _check("pkv_measure_hbm_read", st)
+
+
+def measure_mfma_bf16(iterations, result):
+    """Register-only loop of bf16 MFMAs on `result.numel()` waves; each
+    writes 32 * iterations into its slot of `result` (float32, device)."""
+    st = library().pkv_measure_mfma_bf16(int(iterations), result.numel(),
+                                         _dev(result, "result", torch.float32), _stream(result))
+    _check("pkv_measure_mfma_bf16", st)

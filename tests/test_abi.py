@@ -325,3 +325,22 @@ def test_nvfp4_errors(lib):
     assert dcall(a18=-2.0) == SHAPE
     assert dcall(a21=need - 1) == WS
     assert dcall(a20=None) == WS
+
+
+def test_measure_errors(lib):
+    p = 0x100000
+    f = lib.pkv_measure_hbm_read
+    assert f(p, 0, p, None) == SHAPE
+    assert f(p, 24, p, None) == SHAPE            # not a multiple of 16
+    assert f(p, 1 << 40, p, None) == SHAPE
+    assert f(None, 64, p, None) == NULL
+    assert f(p, 64, None, None) == NULL
+    assert f(p + 8, 64, p, None) == ALIGN
+    assert f(p, 64, p + 2, None) == ALIGN
+    g = lib.pkv_measure_mfma_bf16
+    assert g(0, 8, p, None) == SHAPE
+    assert g(524289, 8, p, None) == SHAPE
+    assert g(10, 12, p, None) == SHAPE           # not a multiple of 8
+    assert g(10, 0, p, None) == SHAPE
+    assert g(10, 8, None, None) == NULL
+    assert g(10, 8, p + 2, None) == ALIGN
