@@ -134,6 +134,29 @@ pkv_status reshape_and_cache(const void* key, const void* value,
                              float v_scale, void* stream);
 
 /*
+ * reshape_and_cache_from_schedule -- compute_slot_mapping and
+ * reshape_and_cache in one launch: each scheduled token's slot is derived
+ * from the unified schedule and its block table exactly as
+ * compute_slot_mapping does (slot -1 in the same cases), stored to
+ * slot_mapping if that is not NULL, and the token's K and V are written
+ * there exactly as reshape_and_cache does (same encodings, negative slots
+ * skipped).  Meant for the first layer of a step: later layers take the
+ * stored slot_mapping to reshape_and_cache.
+ *
+ *   key, value, k_cache, v_cache, dtypes, scales: as reshape_and_cache
+ *   block_tables, max_blocks_per_seq, query_start_loc, num_computed_tokens,
+ *   num_reqs, num_blocks: as compute_slot_mapping
+ *   slot_mapping    int64 [num_tokens], device, written; or NULL
+ * Same supported set and preconditions as the two calls.
+ */
+pkv_status reshape_and_cache_from_schedule(
+    const void* key, const void* value, void* k_cache, void* v_cache,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* query_start_loc,
+    const int32_t* num_computed_tokens, int32_t num_reqs, int64_t* slot_mapping,
+    int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+    pkv_dtype src_dtype, pkv_dtype cache_dtype, float k_scale, float v_scale, void* stream);
+
+/*
  * copy_blocks -- copy whole physical blocks, in every layer.
  *
  * Shared blocks are read-only; a sequence about to write into a block that

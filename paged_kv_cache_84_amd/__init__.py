@@ -32,6 +32,7 @@ from ._binding import (  # noqa: F401
     paged_attention_prefill_chunk,
     paged_attention_varlen,
     reshape_and_cache,
+    reshape_and_cache_from_schedule,
     reshape_and_cache_int4,
     reshape_and_cache_nvfp4,
     swap_blocks,

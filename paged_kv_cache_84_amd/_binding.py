@@ -39,6 +39,9 @@ _SIGNATURES = {
     "reshape_and_cache": (_I32, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
                                  _I32, _F, _F, _P]),
     "copy_blocks": (_I32, [_P, _P, _I32, _P, _I32, _I32, _I64, _P]),
+    "reshape_and_cache_from_schedule": (_I32, [_P, _P, _P, _P, _P, _I32, _P, _P, _I32, _P,
+                                               _I32, _I32, _I32, _I32, _I32, _I32, _F, _F,
+                                               _P]),
     "swap_blocks": (_I32, [_P, _P, _P, _P, _I32, _P, _I32, _I32, _I32, _I64, _P]),
     "paged_attention_decode_workspace_size": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32]),
     "paged_attention_decode_num_chunks": (_I32, [_I32, _I32, _I32, _I32, _I32]),
@@ -457,3 +460,24 @@ def measure_mfma_bf16(iterations, result):
     st = library().pkv_measure_mfma_bf16(int(iterations), result.numel(),
                                          _dev(result, "result", torch.float32), _stream(result))
     _check("pkv_measure_mfma_bf16", st)
+
+
+def reshape_and_cache_from_schedule(key, value, k_cache, v_cache, block_tables,
+                                    query_start_loc, num_computed_tokens, k_scale=1.0,
+                                    v_scale=1.0, slot_mapping=None):
+    """compute_slot_mapping + reshape_and_cache in one launch; the slots go
+    to `slot_mapping` (int64 [T]) when given."""
+    t, hkv, d = key.shape
+    assert value.shape == key.shape and key.dtype == value.dtype
+    assert k_cache.shape == v_cache.shape and k_cache.shape[1:] == (hkv, BLOCK_SIZE, d)
+    r = num_computed_tokens.shape[0]
+    assert query_start_loc.shape[0] == r + 1 and block_tables.shape[0] >= r
+    sm = 0 if slot_mapping is None else _dev(slot_mapping, "slot_mapping", torch.int64)
+    st = library().reshape_and_cache_from_schedule(
+        _dev(key, "key"), _dev(value, "value"), _dev(k_cache, "k_cache"),
+        _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables", torch.int32),
+        block_tables.shape[1], _dev(query_start_loc, "query_start_loc", torch.int32),
+        _dev(num_computed_tokens, "num_computed_tokens", torch.int32), r, sm or None, t, hkv,
+        d, k_cache.shape[0], _dtype_code(key, "key"), _dtype_code(k_cache, "k_cache"),
+        float(k_scale), float(v_scale), _stream(key))
+    _check("reshape_and_cache_from_schedule", st)

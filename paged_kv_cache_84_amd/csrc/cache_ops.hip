@@ -43,19 +43,22 @@ __global__ __launch_bounds__(256) void slot_mapping_kernel(
 template <typename Src, typename Dst>
 struct Writer;
 
+// store(v, dst, scale) encodes the 16 source bytes v; run loads them first.
 template <>
 struct Writer<BF16, BF16> {
   static constexpr int kElems = 8;
-  PKV_DEVICE static void run(const uint16_t* src, uint16_t* dst, float) {
-    store16(dst, load16(src));
+  PKV_DEVICE static void store(u32x4 v, uint16_t* dst, float) { store16(dst, v); }
+  PKV_DEVICE static void run(const uint16_t* src, uint16_t* dst, float s) {
+    store(load16(src), dst, s);
   }
 };
 
 template <>
 struct Writer<F32, F32> {
   static constexpr int kElems = 4;
-  PKV_DEVICE static void run(const float* src, float* dst, float) {
-    store16(dst, load16(src));
+  PKV_DEVICE static void store(u32x4 v, float* dst, float) { store16(dst, v); }
+  PKV_DEVICE static void run(const float* src, float* dst, float s) {
+    store(load16(src), dst, s);
   }
 };
 
@@ -63,7 +66,9 @@ template <>
 struct Writer<BF16, FP8> {
   static constexpr int kElems = 8;
   PKV_DEVICE static void run(const uint16_t* src, uint8_t* dst, float scale) {
-    const u32x4 v = load16(src);
+    store(load16(src), dst, scale);
+  }
+  PKV_DEVICE static void store(u32x4 v, uint8_t* dst, float scale) {
     uint32_t lo = 0, hi = 0;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -80,7 +85,9 @@ template <>
 struct Writer<F32, FP8> {
   static constexpr int kElems = 4;
   PKV_DEVICE static void run(const float* src, uint8_t* dst, float scale) {
-    const u32x4 v = load16(src);
+    store(load16(src), dst, scale);
+  }
+  PKV_DEVICE static void store(u32x4 v, uint8_t* dst, float scale) {
     uint32_t w = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -120,6 +127,101 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     else
       W::run(key + src, k_cache + dst, k_scale);
   }
+}
+
+// ---------------------------------------- slot mapping + cache write in one
+// One workgroup per token t.  Its K/V loads go out first; meanwhile every
+// wave finds t's request: lanes load query_start_loc and num_computed_tokens
+// of kSearchBatch x 64 requests at once and the lane whose request holds t
+// wins a ballot.  Then one load of the block-table entry gives the slot
+// (the same formula and the same -1 cases as slot_mapping_kernel); thread 0
+// stores it, and the rows go to the cache.  Two dependent trips to memory
+// instead of the four of the two separate kernels.
+constexpr int kSearchBatch = 4;
+constexpr int kHeldVecs = 4;      // 16-byte source pieces a thread holds while searching
+
+template <typename Src, typename Dst>
+__global__ __launch_bounds__(256) void reshape_and_cache_sched_kernel(
+    const typename Src::storage* __restrict__ key,
+    const typename Src::storage* __restrict__ value,
+    typename Dst::storage* __restrict__ k_cache, typename Dst::storage* __restrict__ v_cache,
+    const int32_t* __restrict__ block_tables, int32_t max_blocks,
+    const int32_t* __restrict__ query_start_loc, const int32_t* __restrict__ num_computed,
+    int32_t num_reqs, int64_t* __restrict__ slots_out, int32_t num_kv_heads,
+    int32_t head_dim, int32_t num_blocks, float k_scale, float v_scale) {
+  using W = Writer<Src, Dst>;
+  const int t = blockIdx.x;
+  const int lane = lane_id();
+  const int vecs_per_head = head_dim / W::kElems;
+  const int vecs = num_kv_heads * vecs_per_head;
+  const int64_t src_base = int64_t(t) * num_kv_heads * head_dim;
+  auto src_of = [&](int i) {   // source piece i: K pieces, then V pieces
+    const int iv = i >= vecs ? i - vecs : i;
+    return (i >= vecs ? value : key) + src_base + int64_t(iv / vecs_per_head) * head_dim +
+           (iv % vecs_per_head) * W::kElems;
+  };
+  u32x4 held[kHeldVecs];
+#pragma unroll
+  for (int n = 0; n < kHeldVecs; ++n) {
+    const int i = int(threadIdx.x) + n * int(blockDim.x);
+    if (i < 2 * vecs) held[n] = load16(src_of(i));
+  }
+
+  // request of token t: query_start_loc[r] <= t < query_start_loc[r + 1]
+  int req = -1, begin = 0, computed = 0;
+  for (int base = 0; base < num_reqs; base += kSearchBatch * kWave) {
+    int lo[kSearchBatch], hi[kSearchBatch], cc[kSearchBatch];
+#pragma unroll
+    for (int b = 0; b < kSearchBatch; ++b) {
+      const int r = base + b * kWave + lane;
+      const bool ok = r < num_reqs;
+      lo[b] = ok ? query_start_loc[r] : 0;
+      hi[b] = ok ? query_start_loc[r + 1] : 0;
+      cc[b] = ok ? num_computed[r] : 0;
+    }
+    int found = -1, f_lo = 0, f_c = 0;
+#pragma unroll
+    for (int b = 0; b < kSearchBatch; ++b)
+      if (lo[b] <= t && t < hi[b]) {
+        found = base + b * kWave + lane;
+        f_lo = lo[b];
+        f_c = cc[b];
+      }
+    const uint64_t hit = __ballot(found >= 0);
+    if (hit) {
+      const int src = __builtin_ctzll(hit);
+      req = __shfl(found, src, kWave);
+      begin = __shfl(f_lo, src, kWave);
+      computed = __shfl(f_c, src, kWave);
+      break;
+    }
+  }
+  int64_t slot = -1;
+  if (req >= 0) {
+    const int64_t p = int64_t(computed) + (t - begin);
+    const int64_t j = p / kBlock;
+    if (p >= 0 && j < max_blocks) {
+      const int32_t b = block_tables[int64_t(req) * max_blocks + j];
+      if (b >= 0 && b < num_blocks) slot = int64_t(b) * kBlock + p % kBlock;
+    }
+  }
+  if (slots_out != nullptr && threadIdx.x == 0) slots_out[t] = slot;
+  if (slot < 0) return;
+  const int64_t block = slot / kBlock;
+  const int offset = int(slot % kBlock);
+  auto dst_of = [&](int i, typename Dst::storage* kc, typename Dst::storage* vc) {
+    const int iv = i >= vecs ? i - vecs : i;
+    return (i >= vecs ? vc : kc) +
+           ((block * num_kv_heads + iv / vecs_per_head) * kBlock + offset) * head_dim +
+           (iv % vecs_per_head) * W::kElems;
+  };
+#pragma unroll
+  for (int n = 0; n < kHeldVecs; ++n) {
+    const int i = int(threadIdx.x) + n * int(blockDim.x);
+    if (i < 2 * vecs) W::store(held[n], dst_of(i, k_cache, v_cache), i >= vecs ? v_scale : k_scale);
+  }
+  for (int i = int(threadIdx.x) + kHeldVecs * int(blockDim.x); i < 2 * vecs; i += blockDim.x)
+    W::run(src_of(i), dst_of(i, k_cache, v_cache), i >= vecs ? v_scale : k_scale);
 }
 
 // ------------------------------------------------- int4 per token-head write
@@ -360,6 +462,55 @@ extern "C" pkv_status reshape_and_cache(const void* key, const void* value,
     return launch_write<F32, FP8>(key, value, k_cache, v_cache, slot_mapping,
                                   num_tokens, num_kv_heads, head_dim, num_blocks,
                                   k_scale, v_scale, stream);
+  return PKV_ERR_UNSUPPORTED;
+}
+
+template <typename Src, typename Dst>
+static pkv_status launch_write_sched(const void* key, const void* value, void* kc, void* vc,
+                                     const int32_t* bt, int32_t maxb, const int32_t* qsl,
+                                     const int32_t* computed, int32_t reqs, int64_t* slots,
+                                     int32_t t, int32_t hkv, int32_t d, int32_t nb, float ks,
+                                     float vs, void* stream) {
+  hipLaunchKernelGGL((reshape_and_cache_sched_kernel<Src, Dst>), dim3(t), dim3(256), 0,
+                     as_stream(stream), static_cast<const typename Src::storage*>(key),
+                     static_cast<const typename Src::storage*>(value),
+                     static_cast<typename Dst::storage*>(kc),
+                     static_cast<typename Dst::storage*>(vc), bt, maxb, qsl, computed, reqs,
+                     slots, hkv, d, nb, ks, vs);
+  return launch_status();
+}
+
+extern "C" pkv_status reshape_and_cache_from_schedule(
+    const void* key, const void* value, void* k_cache, void* v_cache,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* query_start_loc,
+    const int32_t* num_computed_tokens, int32_t num_reqs, int64_t* slot_mapping,
+    int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+    pkv_dtype src_dtype, pkv_dtype cache_dtype, float k_scale, float v_scale, void* stream) {
+  if (num_tokens < 0 || num_reqs < 0 || max_blocks_per_seq < 0 || num_kv_heads <= 0 ||
+      head_dim <= 0 || num_blocks < 0)
+    return PKV_ERR_SHAPE;
+  if (head_dim % 8 != 0) return PKV_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PKV_OK;
+  if (!key || !value || !k_cache || !v_cache || !block_tables || !query_start_loc ||
+      !num_computed_tokens)
+    return PKV_ERR_NULL;
+  if (!aligned(key, 16) || !aligned(value, 16) || !aligned(k_cache, 16) ||
+      !aligned(v_cache, 16) || !aligned(slot_mapping, 8) || !aligned(block_tables, 4) ||
+      !aligned(query_start_loc, 4) || !aligned(num_computed_tokens, 4))
+    return PKV_ERR_ALIGN;
+  if (cache_dtype == PKV_FP8_E4M3 && !(k_scale > 0.f && v_scale > 0.f)) return PKV_ERR_SHAPE;
+#define PKV_SCHED_ARGS key, value, k_cache, v_cache, block_tables, max_blocks_per_seq, \
+    query_start_loc, num_computed_tokens, num_reqs, slot_mapping, num_tokens, num_kv_heads, \
+    head_dim, num_blocks, k_scale, v_scale, stream
+  if (src_dtype == PKV_BF16 && cache_dtype == PKV_BF16)
+    return launch_write_sched<BF16, BF16>(PKV_SCHED_ARGS);
+  if (src_dtype == PKV_F32 && cache_dtype == PKV_F32)
+    return launch_write_sched<F32, F32>(PKV_SCHED_ARGS);
+  if (src_dtype == PKV_BF16 && cache_dtype == PKV_FP8_E4M3)
+    return launch_write_sched<BF16, FP8>(PKV_SCHED_ARGS);
+  if (src_dtype == PKV_F32 && cache_dtype == PKV_FP8_E4M3)
+    return launch_write_sched<F32, FP8>(PKV_SCHED_ARGS);
+#undef PKV_SCHED_ARGS
   return PKV_ERR_UNSUPPORTED;
 }
 

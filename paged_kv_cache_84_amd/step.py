@@ -1,8 +1,9 @@
 """One engine step of the paged-attention hot path on the GPU.
 
 The order inside a step: block copies (copy-on-write) first, then the slot of
-every new token, then the cache writes of all new tokens, then attention for
-the chunk rows (prefill) and the decode rows, layer by layer, all on one
+every new token and the cache writes of all new tokens (the first layer's
+write derives and stores the slots, later layers reuse them), then attention
+for the chunk rows (prefill) and the decode rows, layer by layer, all on one
 stream ("vLLM 引擎解剖", section "PagedAttention：为 KV 缓存分页" for the
 copy-before-write rule; section "预填充、解码与三个时延指标" for write-then-read).
 
@@ -78,6 +79,22 @@ class DeviceStep:
         B.reshape_and_cache(self.new_k[layer], self.new_v[layer], self.k_caches[layer],
                             self.v_caches[layer], self.slots, s.k_scale, s.v_scale)
 
+    def write_scheduled(self, layer):
+        """Slots from the schedule and this layer's cache write, one launch;
+        the slots are stored for the other layers."""
+        s = self.step
+        B.reshape_and_cache_from_schedule(
+            self.new_k[layer], self.new_v[layer], self.k_caches[layer], self.v_caches[layer],
+            self.block_tables, self.query_start_loc, self.num_computed, s.k_scale, s.v_scale,
+            slot_mapping=self.slots)
+
+    def write_layer(self, layer):
+        """Layer 0 derives the slots while it writes; later layers use them."""
+        if layer == 0:
+            self.write_scheduled(0)
+        else:
+            self.write(layer)
+
     def prefill(self, layer):
         s = self.step
         t = self.num_prefill_tokens
@@ -118,18 +135,17 @@ class DeviceStep:
     def run_varlen(self):
         """The whole step with the unified attention launch."""
         self.copy()
-        self.slot_mapping()
         for layer in range(len(self.k_caches)):
-            self.write(layer)
+            self.write_layer(layer)
             self.varlen(layer)
         return self.out
 
     def run(self):
-        """The whole step: copies, slots, then per layer write and attend."""
+        """The whole step: copies, then per layer write (with the slots on
+        layer 0) and attend."""
         self.copy()
-        self.slot_mapping()
         for layer in range(len(self.k_caches)):
-            self.write(layer)
+            self.write_layer(layer)
             self.prefill(layer)
             self.decode(layer)
         return self.out

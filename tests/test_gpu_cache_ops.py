@@ -142,3 +142,65 @@ def test_copy_then_write_mixed_step_full_size():
     assert np.array_equal(ds.slots.cpu().numpy(), rslots)
     assert np.array_equal(host(ds.k_caches[0]), rk)
     assert np.array_equal(host(ds.v_caches[0]), rv)
+
+
+def test_write_from_schedule_mixed_step_full_size():
+    """reshape_and_cache_from_schedule on the full mixed step (257 requests:
+    the request search spans two batches): the same slots and cache bytes as
+    the oracle's slot mapping + write, after the copy-on-write copies."""
+    announce("config4 full copy + write from schedule")
+    s = C.config4()
+    ds = pk.step.DeviceStep(s)
+    ds.copy()
+    ds.slots.fill_(-7)
+    ds.write_scheduled(0)
+    rk, rv, rslots = oracle_caches_after_step(s)
+    assert np.array_equal(ds.slots.cpu().numpy(), rslots)
+    assert np.array_equal(host(ds.k_caches[0]), rk)
+    assert np.array_equal(host(ds.v_caches[0]), rv)
+
+
+@pytest.mark.parametrize("src,dst", [(F.BF16, F.BF16), (F.F32, F.F32),
+                                     (F.BF16, F.FP8_E4M3), (F.F32, F.FP8_E4M3)])
+def test_write_from_schedule_out_of_range_and_dtypes(src, dst):
+    """Positions past the table and ids outside the pool give slot -1 and no
+    write; an empty request is stepped over; with NULL slot_mapping only the
+    caches are written."""
+    announce("write from schedule", src, dst)
+    tables = np.array([[3, 99, 1], [2, -5, 0], [4, 5, 6], [7, 8, 8]], np.int32)
+    qsl = np.array([0, 40, 41, 41, 45], np.int32)          # request 2 is empty
+    comp = np.array([0, 20, 7, 46], np.int32)                # request 3 runs past its table
+    t, hkv, d, nb = 45, 2, 64, 10
+    g = torch.Generator().manual_seed(11)
+    src_t = torch.float32 if src == F.F32 else torch.bfloat16
+    key = (torch.randn((t, hkv, d), generator=g) * 3).to(src_t)
+    val = (torch.randn((t, hkv, d), generator=g) * 0.2).to(src_t)
+    if dst == F.FP8_E4M3:
+        kc = torch.randint(0, 256, (nb, hkv, 16, d), generator=g, dtype=torch.uint8)
+    else:
+        kc = torch.randn((nb, hkv, 16, d), generator=g).to(src_t)
+    vc = kc.clone()
+    ks, vs = (0.05, 0.002) if dst == F.FP8_E4M3 else (1.0, 1.0)
+    # the oracle's slot formula where the position is inside the table; the
+    # library's contract (-1) past the table and for ids outside the pool
+    want_slots = np.full(t, -1, np.int64)
+    for r in range(len(comp)):
+        for i in range(qsl[r + 1] - qsl[r]):
+            p = int(comp[r]) + i
+            if p // 16 < tables.shape[1]:
+                slot = P.slot_of(tables[r], p)
+                want_slots[qsl[r] + i] = slot if 0 <= slot < nb * 16 else -1
+    rk, rv = P.reshape_and_cache(host(key), host(val), host(kc), host(vc), want_slots, src,
+                                 dst, ks, vs)
+    for with_slots in (True, False):
+        gk, gv = kc.to(DEV), vc.to(DEV)
+        slots = torch.full((t,), -7, dtype=torch.int64, device=DEV) if with_slots else None
+        pk.reshape_and_cache_from_schedule(key.to(DEV), val.to(DEV), gk, gv, _i32(tables),
+                                           _i32(qsl), _i32(comp), ks, vs, slot_mapping=slots)
+        torch.cuda.synchronize()
+        if with_slots:
+            assert np.array_equal(slots.cpu().numpy(), want_slots)
+        assert np.array_equal(bits(host(gk)), bits(rk))
+        assert np.array_equal(bits(host(gv)), bits(rv))
+    assert (want_slots[16:32] == -1).all() and want_slots[40] == -1
+    assert list(want_slots[41:]) == [8 * 16 + 14, 8 * 16 + 15, -1, -1]
