@@ -578,20 +578,28 @@ __global__ __launch_bounds__(256) void prefill_rows_kernel(
 // which leaves a few: up to kFewParts of them are merged from one round of
 // loads, pairs and vectors together.)
 constexpr int kFewParts = 8;   // partials merged by the single-load path
+// With W = 1 a workgroup carries this many (head, sequence) units, one per
+// wave, each on its own (no workgroup barrier): a quarter of the workgroups
+// to dispatch.
+constexpr int kMergeUnits = 4;
+
+template <int W>
+constexpr int merge_waves() { return W == 1 ? kMergeUnits : W; }
 
 template <typename QT, int D, int W>
-__global__ __launch_bounds__(kWave * W) void decode_merge_kernel(
+__global__ __launch_bounds__(kWave * merge_waves<W>()) void decode_merge_kernel(
     typename QT::storage* __restrict__ out, const float* __restrict__ rec_out,
     const float* __restrict__ rec_ml, const int32_t* __restrict__ context_lens,
     int32_t num_seqs, int32_t max_len, int32_t num_q_heads, int32_t num_chunks,
     int32_t fixed_chunk, float v_scale, int32_t window) {
   constexpr int kPer = D / kWave;
-  __shared__ float wts[W][kWave];
+  __shared__ float wts[merge_waves<W>()][kWave];
   __shared__ float part[W][D + 1];
-  const int h = blockIdx.x;
-  const int seq = blockIdx.y;
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
+  const int h = W == 1 ? int(blockIdx.x) * kMergeUnits + wave : int(blockIdx.x);
+  const int seq = blockIdx.y;
+  if (W == 1 && h >= num_q_heads) return;
   const BatchScan sc = scan_batch(context_lens, num_seqs, max_len, window);
   const int owner = seq / sc.k;
   int before = __builtin_amdgcn_readlane(sc.first, owner);
@@ -600,7 +608,7 @@ __global__ __launch_bounds__(kWave * W) void decode_merge_kernel(
   const int n = window_blocks(seq_len(sc, context_lens, seq, max_len), window);
   typename QT::storage* o = out + (int64_t(seq) * num_q_heads + h) * D;
   if (n == 0) {
-    if (wave == 0) {
+    if (W == 1 || wave == 0) {
 #pragma unroll
       for (int i = 0; i < kPer; ++i) store_out<QT>(o + lane + i * kWave, 0.f);
     }
@@ -646,7 +654,9 @@ __global__ __launch_bounds__(kWave * W) void decode_merge_kernel(
   big = wave_max(big);
   float acc[kPer] = {};
   float den = 0.f;
-  for (int k0 = wave * kWave; k0 < nparts; k0 += kWave * W) {
+  // W > 1: the waves take every W-th group of 64 partials of one unit;
+  // W = 1: each wave is a unit of its own and takes them all
+  for (int k0 = W == 1 ? 0 : wave * kWave; k0 < nparts; k0 += kWave * W) {
     const int k = k0 + lane;
     float wk = 0.f;
     if (k < nparts) {
@@ -677,6 +687,12 @@ __global__ __launch_bounds__(kWave * W) void decode_merge_kernel(
     __builtin_amdgcn_wave_barrier();
   }
   den = wave_sum(den);
+  if constexpr (W == 1) {     // the wave holds the whole unit
+    const float f = v_scale / den;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) store_out<QT>(o + lane + i * kWave, acc[i] * f);
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < kPer; ++i) part[wave][lane + i * kWave] = acc[i];
   if (lane == 0) part[wave][D] = den;
@@ -768,7 +784,8 @@ static pkv_status launch_merge(void* out, const int32_t* lens, int32_t s, int32_
                        static_cast<typename QT::storage*>(out), rec_out, rec_ml, lens, s,
                        max_len, hq, plan.num_chunks, plan.fixed_chunk, v_scale, window);
   else
-    hipLaunchKernelGGL((decode_merge_kernel<QT, D, 1>), dim3(hq, s), dim3(kWave), 0, st,
+    hipLaunchKernelGGL((decode_merge_kernel<QT, D, 1>),
+                       dim3((hq + kMergeUnits - 1) / kMergeUnits, s), dim3(kWave * kMergeUnits), 0, st,
                        static_cast<typename QT::storage*>(out), rec_out, rec_ml, lens, s,
                        max_len, hq, plan.num_chunks, plan.fixed_chunk, v_scale, window);
   return launch_status();
