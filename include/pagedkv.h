@@ -316,6 +316,38 @@ pkv_status paged_attention_prefill_chunk(void* out, const void* query,
                                          void* stream);
 
 /*
+ * paged_attention_decode_append -- one decode step of a decode-only batch:
+ * each sequence's new token (position L-1, L = context_lens[s] >= 1) is
+ * written into the cache and attention over positions 0 .. L-1 follows, in
+ * the same launch.  Prefill writes K and V into the cache and decode reads
+ * them back ("vLLM 引擎解剖", section "预填充、解码与三个时延指标"); here the write
+ * of the token a decode row brings is the reshape_and_cache of that row,
+ * at the slot compute_slot_mapping gives it (block_tables[s][(L-1)/16] * 16
+ * + (L-1) % 16; skipped if the block id is outside [0, num_blocks) or the
+ * logical block beyond max_blocks_per_seq), encoded as reshape_and_cache
+ * does.  The results equal reshape_and_cache of the new rows followed by
+ * paged_attention_decode.
+ *   new_key, new_value  bf16 [num_seqs][num_kv_heads][head_dim], device,
+ *                       16-byte aligned; rows of sequences with L = 0 are
+ *                       not read
+ *   k_cache, v_cache    written at the new tokens' slots, then read
+ * Supported: bf16 queries with bf16 or fp8 E4M3 caches (PKV_ERR_UNSUPPORTED
+ * otherwise); other arguments, workspace and errors as
+ * paged_attention_decode.  Precondition: the new tokens' slots are distinct
+ * (a sequence writing into a block it shares is copied first).
+ */
+pkv_status paged_attention_decode_append(void* out, const void* query, const void* new_key,
+                                         const void* new_value, void* k_cache, void* v_cache,
+                                         int32_t num_blocks, const int32_t* block_tables,
+                                         int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                         int32_t num_seqs, int32_t max_context_len,
+                                         int32_t num_q_heads, int32_t num_kv_heads,
+                                         int32_t head_dim, float softmax_scale,
+                                         pkv_dtype q_dtype, pkv_dtype kv_dtype, float k_scale,
+                                         float v_scale, int32_t partition_tokens,
+                                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * paged_attention_decode_sliding -- paged_attention_decode for sliding-window
  * layers: the query of a sequence of length L attends to positions
  * max(0, L - sliding_window) .. L-1 only (its own included; the pages note

@@ -26,6 +26,7 @@ from ._binding import (  # noqa: F401
     measure_mfma_bf16,
     varlen_workspace_size,
     paged_attention_decode,
+    paged_attention_decode_append,
     paged_attention_decode_int4,
     paged_attention_decode_nvfp4,
     paged_attention_decode_sliding,

@@ -48,6 +48,9 @@ _SIGNATURES = {
     "paged_attention_decode": (_I32, [_P, _P, _P, _P, _I32, _P, _I32, _P, _I32, _I32,
                                       _I32, _I32, _I32, _F, _I32, _I32, _F, _F, _I32,
                                       _P, _SZ, _P]),
+    "paged_attention_decode_append": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _P, _I32, _P, _I32,
+                                             _I32, _I32, _I32, _I32, _F, _I32, _I32, _F, _F,
+                                             _I32, _P, _SZ, _P]),
     "paged_attention_decode_sliding": (_I32, [_P, _P, _P, _P, _I32, _P, _I32, _P, _I32, _I32,
                                               _I32, _I32, _I32, _F, _I32, _I32, _F, _F, _I32,
                                               _I32, _P, _SZ, _P]),
@@ -481,3 +484,30 @@ def reshape_and_cache_from_schedule(key, value, k_cache, v_cache, block_tables,
         d, k_cache.shape[0], _dtype_code(key, "key"), _dtype_code(k_cache, "k_cache"),
         float(k_scale), float(v_scale), _stream(key))
     _check("reshape_and_cache_from_schedule", st)
+
+
+def paged_attention_decode_append(query, new_key, new_value, k_cache, v_cache, block_tables,
+                                  context_lens, max_context_len, softmax_scale, k_scale=1.0,
+                                  v_scale=1.0, partition_tokens=0, out=None, workspace=None):
+    """Write each sequence's new K/V row at position L-1, then decode; same
+    results as reshape_and_cache of the rows followed by
+    paged_attention_decode."""
+    s, hq, d = query.shape
+    hkv = k_cache.shape[1]
+    assert new_key.shape == new_value.shape == (s, hkv, d)
+    if out is None:
+        out = torch.empty_like(query)
+    need = decode_workspace_size(s, hq, hkv, d, max_context_len, partition_tokens)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=query.device)
+    st = library().paged_attention_decode_append(
+        _dev(out, "out", query.dtype), _dev(query, "query"), _dev(new_key, "new_key", query.dtype),
+        _dev(new_value, "new_value", query.dtype), _dev(k_cache, "k_cache"),
+        _dev(v_cache, "v_cache"), k_cache.shape[0],
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(context_lens, "context_lens", torch.int32), s, int(max_context_len), hq, hkv, d,
+        float(softmax_scale), _dtype_code(query, "query"), _dtype_code(k_cache, "k_cache"),
+        float(k_scale), float(v_scale), int(partition_tokens), _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(query))
+    _check("paged_attention_decode_append", st)
+    return out

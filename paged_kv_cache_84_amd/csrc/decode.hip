@@ -896,7 +896,9 @@ static pkv_status mfma_decode(void* out, const void* query, const void* k_cache,
                               int32_t max_context_len, int32_t num_q_heads,
                               int32_t num_kv_heads, int32_t head_dim, float scale_log2,
                               pkv_dtype kv_dtype, float v_scale, const DecodePlan& lay,
-                              void* workspace, void* stream, int32_t window = 0) {
+                              void* workspace, void* stream, int32_t window = 0,
+                              const void* new_k = nullptr, const void* new_v = nullptr,
+                              float k_scale = 1.0f) {
   const int64_t target = int64_t(PKV_DECODE_TARGET_WAVES) *
                          (kv_dtype == PKV_BF16 ? 1 : PKV_FP8_WAVES_PER_SIMD);
   const int64_t per_wave =
@@ -909,7 +911,7 @@ static pkv_status mfma_decode(void* out, const void* query, const void* k_cache,
                    lay.num_chunks, lay.fixed_chunk, int32_t(per_wave),
                    static_cast<float*>(workspace),
                    reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.out_bytes),
-                   stream, k_scales, v_scales, window};
+                   stream, k_scales, v_scales, window, new_k, new_v, k_scale};
   if (launch_decode_mfma(a) != PKV_OK) return PKV_ERR_LAUNCH;
   hipStream_t st = as_stream(stream);
   return head_dim == 64
@@ -955,7 +957,8 @@ static pkv_status decode_impl(
     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
     float softmax_scale, pkv_dtype q_dtype, pkv_dtype kv_dtype, float k_scale,
     float v_scale, int32_t partition_tokens, void* workspace,
-    size_t workspace_bytes, void* stream, int32_t window) {
+    size_t workspace_bytes, void* stream, int32_t window, const void* new_key = nullptr,
+    const void* new_value = nullptr) {
   if (window < 0) return PKV_ERR_SHAPE;
   if (num_seqs < 0 || num_blocks < 0 || max_blocks_per_seq < 0 ||
       max_context_len < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
@@ -989,13 +992,18 @@ static pkv_status decode_impl(
     return PKV_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return PKV_ERR_ALIGN;
 
+  const bool append = new_key != nullptr;
+  if (append && !(aligned(new_key, 16) && aligned(new_value, 16))) return PKV_ERR_ALIGN;
 #if PKV_DECODE_USE_MFMA
   if (decode_mfma_supported(q_dtype, kv_dtype, head_dim, group))
     return mfma_decode(out, query, k_cache, v_cache, nullptr, nullptr, num_blocks, block_tables,
                        max_blocks_per_seq, context_lens, num_seqs, max_context_len,
                        num_q_heads, num_kv_heads, head_dim, softmax_scale * k_scale * kLog2e,
-                       kv_dtype, v_scale, lay, workspace, stream, window);
+                       kv_dtype, v_scale, lay, workspace, stream, window, new_key, new_value,
+                       k_scale);
 #endif
+  // the append is built into the matrix-core kernel only
+  if (append) return PKV_ERR_UNSUPPORTED;
   // the sliding window is built into the matrix-core kernel only
   if (window > 0) return PKV_ERR_UNSUPPORTED;
   // fp32 q with head_dim 128 keeps at most two heads per wave (registers)
@@ -1122,4 +1130,21 @@ extern "C" pkv_status paged_attention_decode_nvfp4(
                      block_tables, max_blocks_per_seq, context_lens, num_seqs, max_context_len,
                      num_q_heads, num_kv_heads, head_dim, softmax_scale * k_scale * kLog2e,
                      PKV_NVFP4, v_scale, lay, workspace, stream);
+}
+
+extern "C" pkv_status paged_attention_decode_append(
+    void* out, const void* query, const void* new_key, const void* new_value, void* k_cache,
+    void* v_cache, int32_t num_blocks, const int32_t* block_tables, int32_t max_blocks_per_seq,
+    const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float softmax_scale,
+    pkv_dtype q_dtype, pkv_dtype kv_dtype, float k_scale, float v_scale,
+    int32_t partition_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_seqs > 0 && (!new_key || !new_value)) return PKV_ERR_NULL;
+  if (q_dtype != PKV_BF16 || (kv_dtype != PKV_BF16 && kv_dtype != PKV_FP8_E4M3))
+    return PKV_ERR_UNSUPPORTED;
+  return decode_impl(out, query, k_cache, v_cache, num_blocks, block_tables,
+                     max_blocks_per_seq, context_lens, num_seqs, max_context_len, num_q_heads,
+                     num_kv_heads, head_dim, softmax_scale, q_dtype, kv_dtype, k_scale, v_scale,
+                     partition_tokens, workspace, workspace_bytes, stream, 0, new_key,
+                     new_value);
 }

@@ -30,6 +30,12 @@ struct DecodeMfmaArgs {
   const void* k_scales = nullptr;
   const void* v_scales = nullptr;
   int32_t window = 0;                // sliding window in tokens (0 = none)
+  // append: the new token's K and V rows ([num_seqs][kv heads][D] bf16) are
+  // written at position len - 1 before the attention (nullptr = no append);
+  // an fp8 cache encodes them with k_scale (K) and v_scale (V)
+  const void* new_k = nullptr;
+  const void* new_v = nullptr;
+  float k_scale = 1.0f;
 };
 
 // bf16 queries with a bf16 or fp8 E4M3 cache (head_dim 64 or 128), or an int4

@@ -301,14 +301,16 @@ PKV_DEVICE void cursor_to(SeqCursor& c, int x, const BatchScan& sc, const int32_
 template <typename KVT, int D>
 __global__ __launch_bounds__(64) void decode_mfma_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
-    const typename KVT::storage* __restrict__ k_cache,
-    const typename KVT::storage* __restrict__ v_cache, int32_t num_blocks,
+    // not __restrict__: the append path stores into the caches it then reads
+    const typename KVT::storage* k_cache, const typename KVT::storage* v_cache,
+    int32_t num_blocks,
     const int32_t* __restrict__ block_tables, int32_t max_blocks,
     const int32_t* __restrict__ context_lens, int32_t num_seqs, int32_t max_len,
     int32_t num_q_heads, int32_t num_kv_heads, int32_t group, float scale_log2,
     float v_scale, int32_t num_chunks, int32_t fixed_chunk, int32_t chunks_per_wave,
     float* __restrict__ rec_out, float* __restrict__ rec_ml,
-    const void* __restrict__ k_scales, const void* __restrict__ v_scales, int32_t window) {
+    const void* __restrict__ k_scales, const void* __restrict__ v_scales, int32_t window,
+    const uint16_t* __restrict__ new_k, const uint16_t* __restrict__ new_v, float k_scale) {
   using M = MGeom<KVT, D>;
   __shared__ __align__(16) char vl[kBlock * M::kVStride];
   const int kvh = blockIdx.x % num_kv_heads;
@@ -370,6 +372,52 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
   cc.n = window_blocks(cc.len, window);
   cc.first = first_block(cc.len, window);
   SeqCursor lc = cc, ic = cc;
+
+  // Append (new_k != nullptr): a decode row's new token sits at position
+  // len - 1, in its sequence's last block, and the wave whose range holds
+  // that block is the only one that reads it.  So this wave writes the new
+  // K and V rows of those sequences (slot = table[s][(len-1)/16] * 16 +
+  // (len-1) % 16, skipped for an unusable id) before it reads anything, and
+  // waits for the stores once.
+  if constexpr (!kPacked4<KVT>) {
+    if (new_k != nullptr) {
+      SeqCursor wc = cc;
+      for (;;) {
+        const int last = wc.before + wc.n - 1;        // flattened index of its last block
+        if (wc.n > 0 && last >= b0 && last < b1) {
+          const int pos = wc.len - 1;
+          const int i = pos / kBlock;
+          const int32_t id =
+              i < max_blocks ? load_scalar(block_tables, int64_t(wc.s) * max_blocks + i) : -1;
+          if (valid(id) && 2 * lane < D) {
+            const int64_t row = int64_t(pos % kBlock) * D + 2 * lane;
+            const int64_t src = (int64_t(wc.s) * num_kv_heads + kvh) * D + 2 * lane;
+            const uint32_t kw = *reinterpret_cast<const uint32_t*>(new_k + src);
+            const uint32_t vw = *reinterpret_cast<const uint32_t*>(new_v + src);
+            typename KVT::storage* kd = const_cast<typename KVT::storage*>(tile(k_cache, id)) + row;
+            typename KVT::storage* vd = const_cast<typename KVT::storage*>(tile(v_cache, id)) + row;
+            if constexpr (KVT::bytes == 2) {
+              *reinterpret_cast<uint32_t*>(kd) = kw;
+              *reinterpret_cast<uint32_t*>(vd) = vw;
+            } else {
+              *reinterpret_cast<uint16_t*>(kd) =
+                  uint16_t(f32_to_e4m3(bf16_lo(kw) / k_scale) | (f32_to_e4m3(bf16_hi(kw) / k_scale) << 8));
+              *reinterpret_cast<uint16_t*>(vd) =
+                  uint16_t(f32_to_e4m3(bf16_lo(vw) / v_scale) | (f32_to_e4m3(bf16_hi(vw) / v_scale) << 8));
+            }
+          }
+        }
+        if (wc.before + wc.n >= b1 || wc.s + 1 >= num_seqs) break;
+        wc.before += wc.n;
+        ++wc.s;
+        wc.len = seq_len(sc, context_lens, wc.s, max_len);
+        wc.n = window_blocks(wc.len, window);
+      }
+      __builtin_amdgcn_s_waitcnt(0x0F70);    // vmcnt(0): the rows are stored
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);   // and no read moves above them
+    }
+  }
+
   u32x4 qb[M::kKSteps], qn[M::kKSteps];
   load_q(cc.s, qb);
   // int4: 136 * (sum of the column's query), the offset's share of S^T
@@ -575,7 +623,8 @@ static pkv_status launch_one(const DecodeMfmaArgs& a) {
                      a.num_q_heads, a.num_kv_heads, a.num_q_heads / a.num_kv_heads,
                      a.scale_log2, a.v_scale, a.num_chunks, a.fixed_chunk,
                      a.chunks_per_wave, a.rec_out, a.rec_ml, a.k_scales, a.v_scales,
-                     a.window);
+                     a.window, static_cast<const uint16_t*>(a.new_k),
+                     static_cast<const uint16_t*>(a.new_v), a.k_scale);
   return launch_status();
 }
 
