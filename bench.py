@@ -8,8 +8,9 @@
 
 A step is one pass of the hot path over one batch: the Llama-3.1-8B-shaped
 decode layer (64 sequences, context 512..4096, 32 q / 8 kv heads, head_dim
-128, bf16, 16-token blocks): slot mapping of the 64 new tokens and their
-cache writes (one launch), and paged decode attention (partitions + merge).  Inputs are resident
+128, bf16, 16-token blocks): the slots of the 64 new tokens, their cache
+writes and paged decode attention, all in the one decode launch
+(paged_attention_decode_append: balanced chunks + merge).  Inputs are resident
 in HBM before timing starts; two copies of the KV pool alternate between
 steps so that the 256 MB last-level cache cannot serve a re-read.
 
@@ -188,9 +189,8 @@ def bench_decode(args, pk, step):
     stream = torch.cuda.current_stream()
 
     def one_step(i):
-        ds = dss[i % 2]
-        ds.write_layer(0)     # slots of the 64 new tokens + their cache write
-        ds.decode(0)
+        # the 64 new tokens' slots and cache writes, then the decode: one launch
+        dss[i % 2].decode_append(0)
 
     for i in range(args.warmup):
         one_step(i)
@@ -613,8 +613,9 @@ def main():
         "config": {"workload": "Llama-3.1-8B-shaped decode layer: 64 sequences, "
                                "context uniform in [512, 4096], 32 q / 8 kv heads, "
                                "head_dim 128, bf16 Q/K/V, 16-token blocks, shuffled "
-                               "block placement; step = slot mapping + cache write of "
-                               "the 64 new tokens (one launch) + paged decode (balanced chunks + merge)",
+                               "block placement; step = slots + cache writes of the 64 "
+                               "new tokens inside the paged decode launch "
+                               "(paged_attention_decode_append: balanced chunks + merge)",
                    "num_seqs": 64, "kv_tokens": r["tokens"],
                    "algorithmic_bytes": r["bytes"],
                    "decode_chunks_per_kv_head": pk.decode_num_chunks(

@@ -116,6 +116,36 @@ class DeviceStep:
             s.k_scale, s.v_scale, self.partition_tokens, out=self.out[layer][t:],
             workspace=self.workspace)
 
+    def can_append(self):
+        """True for a decode-only step whose formats the fused call takes
+        (bf16 queries; bf16 caches, or fp8 E4M3 caches held as bytes)."""
+        return (self.num_prefill_tokens == 0 and self.num_decode > 0 and
+                self.q[0].dtype == torch.bfloat16 and
+                self.k_caches[0].dtype in (torch.bfloat16, torch.uint8))
+
+    def decode_append(self, layer):
+        """This layer's new-token cache write and decode in one launch: each
+        sequence's new token sits at position context_len - 1, the slot the
+        block table gives it."""
+        s = self.step
+        B.paged_attention_decode_append(
+            self.q[layer], self.new_k[layer], self.new_v[layer], self.k_caches[layer],
+            self.v_caches[layer], self.dec_tables, self.dec_lens, self.max_context_len,
+            s.softmax_scale, s.k_scale, s.v_scale, self.partition_tokens,
+            out=self.out[layer], workspace=self.workspace)
+
+    def run_decode_append(self):
+        """A decode-only step: copies, then per layer one fused write-and-
+        decode launch.  Same caches and outputs as run(); the slot array is
+        not materialised."""
+        if not self.can_append():
+            raise ValueError("run_decode_append takes a decode-only step with bf16 queries "
+                             "and bf16 or fp8 E4M3 caches")
+        self.copy()
+        for layer in range(len(self.k_caches)):
+            self.decode_append(layer)
+        return self.out
+
     def varlen(self, layer):
         """Attention of every request of the step (chunks and decodes) in one
         launch, written to the same output rows as prefill() + decode()."""

@@ -12,6 +12,7 @@ import paged_kv_cache_84_amd as pk
 from gpu_util import announce, as_f64, host
 from oracle import formats as F
 from oracle import paged as P
+from synth import configs as C
 from synth import rng as R
 from synth.allocator import BlockPool, Sequence, tables_array
 from tolerance import assert_attention_close
@@ -96,3 +97,32 @@ def test_append_llama8b_batch():
     assert torch.equal(kb.view(torch.uint8), ka.view(torch.uint8))
     assert torch.equal(vb.view(torch.uint8), va.view(torch.uint8))
     assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+
+
+STEPS = {
+    "llama3.1-8b": lambda: C.config2(device=DEV),
+    "llama2-7b-3-layers": lambda: C.config3(num_layers=3, num_seqs=4, length=1000, device=DEV),
+    "llama3.1-70b-fp8": lambda: C.config5(num_seqs=2, length=5000, device=DEV),
+}
+
+
+@pytest.mark.parametrize("name", list(STEPS))
+def test_step_append_equals_run(name):
+    """DeviceStep.run_decode_append against DeviceStep.run on decode-only
+    steps (bf16 GQA, bf16 MHA over three layers, fp8 long context): the
+    same cache bytes and outputs on every layer."""
+    announce("step append", name)
+    s = STEPS[name]()
+    a = pk.step.DeviceStep(s)
+    b = pk.step.DeviceStep(s)
+    # the steps' tensors already live on the device: give b its own caches
+    b.k_caches = [t.clone() for t in a.k_caches]
+    b.v_caches = [t.clone() for t in a.v_caches]
+    assert b.can_append()
+    ra = a.run()
+    rb = b.run_decode_append()
+    torch.cuda.synchronize()
+    for layer in range(len(a.k_caches)):
+        assert torch.equal(a.k_caches[layer].view(torch.uint8), b.k_caches[layer].view(torch.uint8))
+        assert torch.equal(a.v_caches[layer].view(torch.uint8), b.v_caches[layer].view(torch.uint8))
+        assert torch.equal(ra[layer].view(torch.int16), rb[layer].view(torch.int16))
