@@ -368,25 +368,28 @@ def bench_block_manager(args, oracle_budget_s=5.0):
 def bench_extra_decode(args, pk, C, which):
     """Optional legs: the fp8 long-context decode (64/8 heads, 6 x 131,072
     tokens, 512-token partitions) or the 32-layer MHA decode step (32 x 8,192
-    tokens), each timed as decode calls on inputs resident in HBM."""
+    tokens), each timed as whole decode steps on inputs resident in HBM: per
+    layer, one paged_attention_decode_append call (the new tokens' cache
+    writes inside the decode launch)."""
     if which == "longctx":
         s = C.config5(device="cuda")
         ds = pk.step.DeviceStep(s, partition_tokens=512)
         layers = [0]
         name = ("Llama-3.1-70B-shaped long-context decode, one layer: 6 x 131072 "
                 "tokens, 64 q / 8 kv heads, d128, bf16 q, fp8 e4m3 K/V, 512-token "
-                "partitions")
+                "partitions; new tokens' fp8 write + decode in one call")
     else:
         s = C.config3(device="cuda")
         ds = pk.step.DeviceStep(s)
         layers = list(range(s.num_layers))
         name = ("Llama-2-7B-shaped MHA decode, 32 layers back to back: 32 x 8192 "
-                "tokens, 32/32 heads, d128, bf16")
+                "tokens, 32/32 heads, d128, bf16; per layer, new tokens' write + "
+                "decode in one call")
     stream = torch.cuda.current_stream()
 
     def run(i):
         for layer in layers:
-            ds.decode(layer)
+            ds.decode_append(layer)
 
     for i in range(2):
         run(i)

@@ -22,7 +22,7 @@ DEV = "cuda"
 SCALE = 0.088
 
 
-def _batch(lengths, hq, hkv, kv_dtype, seed, bad_last=()):
+def _batch(lengths, hq, hkv, kv_dtype, seed, bad_last=(), d=128):
     rng = np.random.default_rng(seed)
     nb = sum(P.blocks_needed(max(n, 1)) for n in lengths) + 5
     pool = BlockPool(nb, rng.permutation(nb))
@@ -30,7 +30,7 @@ def _batch(lengths, hq, hkv, kv_dtype, seed, bad_last=()):
     tables = tables_array(seqs)
     for s in bad_last:                       # the new token's block id is unusable
         tables[s, (lengths[s] - 1) // 16] = nb + 3
-    shape = (nb, hkv, 16, 128)
+    shape = (nb, hkv, 16, d)
     if kv_dtype == F.FP8_E4M3:
         kc, ks = R.fp8_normal(shape, 1200 + seed, 1, DEV)
         vc, vs = R.fp8_normal(shape, 1200 + seed, 2, DEV)
@@ -38,9 +38,9 @@ def _batch(lengths, hq, hkv, kv_dtype, seed, bad_last=()):
         kc = R.normal(shape, F.BF16, 1200 + seed, 1, DEV)
         vc = R.normal(shape, F.BF16, 1200 + seed, 2, DEV)
         ks = vs = 1.0
-    q = R.normal((len(lengths), hq, 128), F.BF16, 1200 + seed, 3, DEV)
-    nk = R.normal((len(lengths), hkv, 128), F.BF16, 1200 + seed, 4, DEV, std=2.0)
-    nv = R.normal((len(lengths), hkv, 128), F.BF16, 1200 + seed, 5, DEV, std=0.5)
+    q = R.normal((len(lengths), hq, d), F.BF16, 1200 + seed, 3, DEV)
+    nk = R.normal((len(lengths), hkv, d), F.BF16, 1200 + seed, 4, DEV, std=2.0)
+    nv = R.normal((len(lengths), hkv, d), F.BF16, 1200 + seed, 5, DEV, std=0.5)
     lens = np.array(lengths, np.int32)
     # the new tokens' slots: the oracle's formula, -1 where the library skips
     slots = np.full(len(lengths), -1, np.int64)
@@ -68,12 +68,13 @@ def _both(q, nk, nv, kc, vc, ks, vs, tables, lens, slots, partition):
 
 
 @pytest.mark.parametrize("kv", [F.BF16, F.FP8_E4M3])
-@pytest.mark.parametrize("hq,hkv", [(32, 8), (64, 8), (16, 16)])
+@pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (64, 8, 128), (16, 16, 128), (12, 4, 64),
+                                      (8, 1, 64)])
 @pytest.mark.parametrize("partition", [0, 64])
-def test_append_equals_write_then_decode(kv, hq, hkv, partition):
-    announce("decode append", kv, hq, hkv, partition)
+def test_append_equals_write_then_decode(kv, hq, hkv, d, partition):
+    announce("decode append", kv, hq, hkv, d, partition)
     lengths = [1, 0, 15, 16, 17, 100, 333, 512, 700, 33, 0, 2]
-    args = _batch(lengths, hq, hkv, kv, seed=hq + hkv + partition, bad_last=(6,))
+    args = _batch(lengths, hq, hkv, kv, seed=hq + hkv + d + partition, bad_last=(6,), d=d)
     ka, va, ref, kb, vb, got = _both(*args, partition)
     assert torch.equal(kb.view(torch.uint8), ka.view(torch.uint8))
     assert torch.equal(vb.view(torch.uint8), va.view(torch.uint8))
