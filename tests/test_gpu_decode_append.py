@@ -127,3 +127,33 @@ def test_step_append_equals_run(name):
         assert torch.equal(a.k_caches[layer].view(torch.uint8), b.k_caches[layer].view(torch.uint8))
         assert torch.equal(a.v_caches[layer].view(torch.uint8), b.v_caches[layer].view(torch.uint8))
         assert torch.equal(ra[layer].view(torch.int16), rb[layer].view(torch.int16))
+
+
+FULL = {
+    # the fp8 long-context leg as the benchmark runs it (512-token partitions)
+    "llama3.1-70b-fp8-6x131072": (lambda: C.config5(device=DEV), 512),
+    # two layers of the MHA step at full per-layer size (32 x 8192 tokens)
+    "llama2-7b-2-layers-32x8192": (lambda: C.config3(num_layers=2, device=DEV), 0),
+}
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_step_append_fullsize(name):
+    """The fused call at the benchmark's full sizes and launch configuration
+    against the write-then-decode step: identical cache bytes and outputs."""
+    announce("step append full size", name)
+    make, partition = FULL[name]
+    s = make()
+    a = pk.step.DeviceStep(s, partition_tokens=partition)
+    b = pk.step.DeviceStep(s, partition_tokens=partition)
+    b.k_caches = [t.clone() for t in a.k_caches]
+    b.v_caches = [t.clone() for t in a.v_caches]
+    ra = a.run()
+    rb = b.run_decode_append()
+    torch.cuda.synchronize()
+    for layer in range(len(a.k_caches)):
+        assert torch.equal(a.k_caches[layer].view(torch.uint8), b.k_caches[layer].view(torch.uint8))
+        assert torch.equal(a.v_caches[layer].view(torch.uint8), b.v_caches[layer].view(torch.uint8))
+        assert torch.equal(ra[layer].view(torch.int16), rb[layer].view(torch.int16))
+    del a, b, ra, rb, s
+    torch.cuda.empty_cache()
