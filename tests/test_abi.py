@@ -260,6 +260,38 @@ def test_int4_errors(lib):
     assert dcall(a19=need - 1) == WS
 
 
+def _append(lib, **k):
+    p = 0x100000
+    a = dict(out=p, q=p, nk=p, nv=p, kc=p, vc=p, nb=100, bt=p, maxb=64, lens=p, s=4,
+             maxlen=1000, hq=32, hkv=8, d=128, scale=0.088, qd=BF16, kvd=BF16, ks=1.0,
+             vs=1.0, part=0, ws=p, wsb=1 << 30)
+    a.update(k)
+    return lib.paged_attention_decode_append(
+        a["out"], a["q"], a["nk"], a["nv"], a["kc"], a["vc"], a["nb"], a["bt"], a["maxb"],
+        a["lens"], a["s"], a["maxlen"], a["hq"], a["hkv"], a["d"], a["scale"], a["qd"],
+        a["kvd"], a["ks"], a["vs"], a["part"], a["ws"], a["wsb"], None)
+
+
+def test_decode_append_errors(lib):
+    assert _append(lib, s=0) == OK
+    assert _append(lib, s=0, nk=None) == OK            # no rows to write
+    assert _append(lib, nk=None) == NULL
+    assert _append(lib, nv=None) == NULL
+    assert _append(lib, out=None) == NULL
+    assert _append(lib, nk=0x100008) == ALIGN
+    assert _append(lib, nv=0x100004) == ALIGN
+    assert _append(lib, qd=F32, kvd=F32) == UNSUP       # the write is in the matrix-core kernel
+    assert _append(lib, kvd=F32) == UNSUP
+    assert _append(lib, d=96) == UNSUP
+    assert _append(lib, hq=72) == UNSUP                 # group 9
+    assert _append(lib, hq=30) == SHAPE
+    assert _append(lib, maxb=10) == SHAPE
+    assert _append(lib, part=100) == SHAPE
+    assert _append(lib, kvd=FP8, ks=0.0) == SHAPE
+    need = lib.paged_attention_decode_workspace_size(4, 32, 8, 128, 1000, 0)
+    assert _append(lib, wsb=need - 1) == WS
+
+
 def test_sliding_errors(lib):
     f = lib.paged_attention_decode_sliding
     p = 0x100000
