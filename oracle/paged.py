@@ -484,23 +484,6 @@ def decode_attention_window(q, q_dtype, k_cache, v_cache, kv_dtype, block_tables
     return out
 
 
-def decode_attention_window_one(q, q_dtype, k_cache, v_cache, kv_dtype, block_tables,
-                                context_lens, softmax_scale, window, seq, head,
-                                k_scale=1.0, v_scale=1.0):
-    """One (sequence, q head) element of decode_attention_window."""
-    kvh = head // (q.shape[1] // k_cache.shape[1])
-    length = int(context_lens[seq])
-    if length == 0:
-        return np.zeros(q.shape[-1])
-    first = window_start(length, window)
-    keys = gather_kv(k_cache, kv_dtype, _as_f32_param(k_scale), block_tables[seq], length,
-                     kvh)[first:]
-    values = gather_kv(v_cache, kv_dtype, _as_f32_param(v_scale), block_tables[seq], length,
-                       kvh)[first:]
-    return attention_row(storage_to_f64(q[seq, head], q_dtype), keys, values,
-                         _as_f32_param(softmax_scale))
-
-
 # --- nvfp4-style caches (encoding: oracle/formats.py) -----------------------
 # Codes [num_blocks][num_kv_heads][16][D/2] (uint8), block scale codes
 # [num_blocks][num_kv_heads][16][D/16] (E4M3 bytes), per-tensor k/v scales.

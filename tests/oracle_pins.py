@@ -314,6 +314,63 @@ def pin_torch_sdpa():
     assert np.allclose(pre, ref[0].permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-13)
 
 
+def pin_decode_one_matches_batch():
+    """The per-element decode helper (used to check large launches on samples
+    and in worker processes) returns exactly the batch decode's element, for
+    every (sequence, head), GQA groups, fp32 / bf16 / fp8 caches with their
+    scales, and a zero-length sequence (zeros)."""
+    rng = np.random.default_rng(31)
+    lengths = [0, 1, 16, 17, 45]
+    q, kc, vc, tables = _random_case(rng, 8, 8, 2, lengths, 16)
+    ctx = np.array(lengths, np.int32)
+    kb = (kc.view(np.uint32) >> 16).astype(np.uint16)     # any bit pattern is a bf16
+    vb = (vc.view(np.uint32) >> 16).astype(np.uint16)
+    k8 = F.quantise_to_e4m3(kc, np.float32(0.02))
+    v8 = F.quantise_to_e4m3(vc, np.float32(0.03))
+    for kv_dtype, kcache, vcache, ks, vs in ((F.F32, kc, vc, 1.0, 1.0),
+                                             (F.BF16, kb, vb, 1.0, 1.0),
+                                             (F.FP8_E4M3, k8, v8, 0.02, 0.03)):
+        full = P.decode_attention(q, F.F32, kcache, vcache, kv_dtype, tables, ctx, 0.3,
+                                  ks, vs)
+        for s in range(len(lengths)):
+            for h in range(q.shape[1]):
+                one = P.decode_attention_one(q, F.F32, kcache, vcache, kv_dtype, tables, ctx,
+                                             0.3, s, h, ks, vs)
+                assert np.array_equal(one, full[s, h]), (kv_dtype, s, h)
+    assert np.all(full[0] == 0)
+
+
+def pin_prefill_one_matches_batch():
+    """The per-row prefill helper returns exactly the chunked prefill's row
+    for every (query row, head), over several requests with cached contexts
+    of different lengths, chunks crossing block boundaries, and requests that
+    bring no tokens this step ([Anatomy] "V1：统一调度预填充与解码", Fig. 3:
+    a chunk's rows are causal rows that see keys 0..p)."""
+    rng = np.random.default_rng(32)
+    hq, hkv, d = 4, 2, 8
+    computed = [0, 13, 5, 30, 16]
+    new = [7, 0, 20, 3, 0]
+    lengths = [c + n for c, n in zip(computed, new)]
+    _, kc, vc, tables = _random_case(rng, d, hq, hkv, [max(L, 1) for L in lengths], 16)
+    qsl = np.concatenate([[0], np.cumsum(new)]).astype(np.int32)
+    q = rng.standard_normal((int(qsl[-1]), hq, d)).astype(np.float32)
+    nc = np.array(computed, np.int32)
+    full = P.prefill_attention(q, F.F32, kc, vc, F.F32, tables, qsl, nc, 0.4)
+    for row in range(q.shape[0]):
+        for h in range(hq):
+            one = P.prefill_attention_one(q, F.F32, kc, vc, F.F32, tables, qsl, nc, 0.4,
+                                          row, h)
+            assert np.array_equal(one, full[row, h]), (row, h)
+    # and, independently of the batch function, the first row of request 3
+    # (position 30) is dense attention over the 31 keys 0..30
+    row = int(qsl[3])
+    ref = P.contiguous_attention(q[row, 1][None].astype(np.float64),
+                                 _contiguous_kv(kc, tables[3], 31, 0),
+                                 _contiguous_kv(vc, tables[3], 31, 0), float(np.float32(0.4)))
+    one = P.prefill_attention_one(q, F.F32, kc, vc, F.F32, tables, qsl, nc, 0.4, row, 1)
+    assert np.allclose(one, ref[0], rtol=1e-12, atol=1e-13)
+
+
 # ------------------------------------------------------------- invariants
 
 def pin_permutation():
@@ -599,7 +656,7 @@ ALL_PINS = [
     pin_gqa_mapping, pin_bruteforce_gather, pin_torch_sdpa, pin_permutation,
     pin_prefix_sharing, pin_split_lse, pin_prefill_vs_decode, pin_fig3_replay,
     pin_recompute, pin_spec_verify, pin_poison, pin_fp8_codec, pin_fp8_vs_torch, pin_bf16_decode,
-    pin_budget_example,
+    pin_budget_example, pin_decode_one_matches_batch, pin_prefill_one_matches_batch,
 ]
 
 

@@ -105,8 +105,29 @@ def pin_write_then_read():
         assert np.all(ks2[:, h][~touched] == 0) and np.all(kc2[:, h][~touched] == 0)
 
 
+def pin_one_matches_batch():
+    """The per-element int4 decode helper returns exactly the batch decode's
+    element for every (sequence, head), including a zero-length sequence, with
+    distinct key and value scales."""
+    rng = np.random.default_rng(4)
+    nb, hkv, hq, d = 10, 2, 8, 16
+    kc = rng.integers(0, 256, (nb, hkv, 16, d // 2)).astype(np.uint8)
+    vc = rng.integers(0, 256, (nb, hkv, 16, d // 2)).astype(np.uint8)
+    ks = rng.uniform(0.01, 2, (nb, hkv, 16)).astype(np.float32)
+    vs = rng.uniform(3, 5, (nb, hkv, 16)).astype(np.float32)
+    tables = np.array([[7, 2, 5, 0], [1, 3, 9, 4], [6, 8, 0, 0]], np.int32)
+    lens = np.array([37, 0, 17], np.int32)
+    q = rng.standard_normal((3, hq, d)).astype(np.float32)
+    full = P.decode_attention_int4(q, F.F32, kc, vc, ks, vs, tables, lens, 0.3)
+    for s in range(3):
+        for h in range(hq):
+            one = P.decode_attention_int4_one(q, F.F32, kc, vc, ks, vs, tables, lens, 0.3, s, h)
+            assert np.array_equal(one, full[s, h]), (s, h)
+    assert np.all(full[1] == 0)
+
+
 PINS = [pin_hand_row, pin_zero_row, pin_error_bound_and_extremes, pin_exact_multiples,
-        pin_attention_on_dequantised_rows, pin_write_then_read]
+        pin_attention_on_dequantised_rows, pin_write_then_read, pin_one_matches_batch]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -153,15 +174,24 @@ def _scales_of_next_row(packed_rows, scales):
     return q * sc.astype(np.float64)[..., None]
 
 
+def _one_with_swapped_scales(q, q_dtype, k_cache, v_cache, k_scales, v_scales,
+                             block_tables, context_lens, softmax_scale, seq, head):
+    return P.__dict__["_orig_one"](q, q_dtype, k_cache, v_cache, v_scales, k_scales,
+                                   block_tables, context_lens, softmax_scale, seq, head)
+
+
 MUTANTS = [("int4_quantize_row", _swapped_nibbles), ("int4_quantize_row", _scale_over_8),
            ("int4_quantize_row", _floor_rounding), ("int4_unpack_codes", _unpack_no_offset),
-           ("int4_rows_to_f64", _scales_of_next_row)]
+           ("int4_rows_to_f64", _scales_of_next_row),
+           ("decode_attention_int4_one", _one_with_swapped_scales)]
 
 
 @pytest.mark.parametrize("name,fn", MUTANTS, ids=[f.__name__ for _, f in MUTANTS])
 def test_int4_mutant_is_caught(monkeypatch, name, fn):
     monkeypatch.setitem(F.__dict__, "_orig_quantize", F.int4_quantize_row)
-    monkeypatch.setattr(F, name, fn)
+    monkeypatch.setitem(P.__dict__, "_orig_one", P.decode_attention_int4_one)
+    if hasattr(F, name):
+        monkeypatch.setattr(F, name, fn)
     if hasattr(P, name):
         monkeypatch.setattr(P, name, fn)
     caught = []

@@ -121,6 +121,35 @@ def _write_ignoring_skip(key, value, k_cache, v_cache, slots, src, dst, ks=1.0, 
     return k_out, v_out
 
 
+def _prefill_one_without_own_key(q, q_dtype, k_cache, v_cache, kv_dtype, block_tables,
+                                 query_start_loc, num_computed_tokens, softmax_scale,
+                                 row, head, k_scale=1.0, v_scale=1.0):
+    """Off by one: the query at position p sees keys 0..p-1 (its own missing)."""
+    qsl = [int(x) for x in query_start_loc]
+    r = max(i for i in range(len(qsl) - 1) if qsl[i] <= row < qsl[i + 1])
+    p = int(num_computed_tokens[r]) + (row - qsl[r])
+    kvh = head // (q.shape[1] // k_cache.shape[1])
+    keys = P.gather_kv(k_cache, kv_dtype, k_scale, block_tables[r], max(p, 1), kvh)
+    values = P.gather_kv(v_cache, kv_dtype, v_scale, block_tables[r], max(p, 1), kvh)
+    return P.attention_row(F.storage_to_f64(q[row, head], q_dtype), keys, values,
+                           float(np.float32(softmax_scale)))
+
+
+def _decode_one_wrong_group(q, q_dtype, k_cache, v_cache, kv_dtype, block_tables,
+                            context_lens, softmax_scale, seq, head, k_scale=1.0, v_scale=1.0):
+    """Strided instead of consecutive GQA grouping: kv head = h mod Hkv."""
+    kvh = head % k_cache.shape[1]
+    length = int(context_lens[seq])
+    if length == 0:
+        return np.zeros(q.shape[-1])
+    keys = P.gather_kv(k_cache, kv_dtype, float(np.float32(k_scale)), block_tables[seq],
+                       length, kvh)
+    values = P.gather_kv(v_cache, kv_dtype, float(np.float32(v_scale)), block_tables[seq],
+                         length, kvh)
+    return P.attention_row(F.storage_to_f64(q[seq, head], q_dtype), keys, values,
+                           float(np.float32(softmax_scale)))
+
+
 MUTANTS = [
     ("attention_row", P, _drop_last),
     ("attention_row", P, _wrong_sign),
@@ -136,6 +165,8 @@ MUTANTS = [
     ("copy_blocks", P, _copy_only_keys),
     ("swap_blocks", P, _swap_source_index_from_destination),
     ("reshape_and_cache", P, _write_ignoring_skip),
+    ("prefill_attention_one", P, _prefill_one_without_own_key),
+    ("decode_attention_one", P, _decode_one_wrong_group),
 ]
 
 

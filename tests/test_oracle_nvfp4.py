@@ -102,8 +102,45 @@ def pin_attention_on_dequantised_rows():
         assert np.allclose(got[0, h], want, rtol=1e-12, atol=1e-12)
 
 
+def pin_write_then_read():
+    """reshape_and_cache_nvfp4 with distinct key and value tensor scales: a
+    row whose largest magnitude is 6 gets block scale E4M3(6 / 6 / g), i.e.
+    0x38 (1.0) under g_k = 1 and 0x40 (2.0) under g_v = 0.5; in both cases
+    S * g = 1, so the element codes are the hand-derived bytes of
+    pin_hand_row.  Slot -1 is skipped, the written slots land at
+    (slot / 16, slot % 16), every other byte keeps its poison value."""
+    row = np.array([6, -6, 3, 1.5, 0.75, 5, 3.5, 0.25] + [0] * 7 + [0.1], np.float32)
+    want = [0xF7, 0x35, 0x62, 0x06, 0, 0, 0, 0]
+    nb, hkv, d = 3, 2, 16
+    key = np.stack([np.stack([row, -row]), np.stack([row * 0.5, row])])  # [T=2][Hkv][D]
+    key = np.concatenate([key, key[:1]])                                  # token 2: slot -1
+    value = key.copy()
+    poison = 0xA5
+    kc = np.full((nb, hkv, 16, d // 2), poison, np.uint8)
+    ksc = np.full((nb, hkv, 16, d // 16), poison, np.uint8)
+    slots = np.array([19, 40, -1])
+    kc2, vc2, ksc2, vsc2 = P.reshape_and_cache_nvfp4(key, value, kc, kc, ksc, ksc, slots,
+                                                     F.F32, 1.0, 0.5)
+    # token 0, head 0 -> block 1, offset 3
+    assert kc2[1, 0, 3].tolist() == want and vc2[1, 0, 3].tolist() == want
+    assert ksc2[1, 0, 3].tolist() == [0x38] and vsc2[1, 0, 3].tolist() == [0x40]
+    # token 0, head 1 is the negated row: same bytes with every sign bit set
+    # on the nonzero codes, and -0 codes (0x8) for the zeros
+    neg = [b ^ 0x88 for b in want]
+    assert kc2[1, 1, 3].tolist() == neg
+    # token 1 -> block 2, offset 8; head 0 is row / 2, so its block scale
+    # halves (E4M3(0.5) = 0x30 under g_k = 1) and the codes stay the same
+    assert kc2[2, 0, 8].tolist() == want and ksc2[2, 0, 8].tolist() == [0x30]
+    assert vsc2[2, 0, 8].tolist() == [0x38]
+    touched = np.zeros((nb, 16), bool)
+    touched[1, 3] = touched[2, 8] = True
+    for a in (kc2, vc2, ksc2, vsc2):
+        for h in range(hkv):
+            assert np.all(a[:, h][~touched] == poison)
+
+
 PINS = [pin_e2m1_fields, pin_e2m1_rounding, pin_hand_row, pin_nearest_and_block_scale,
-        pin_zero_block, pin_attention_on_dequantised_rows]
+        pin_zero_block, pin_attention_on_dequantised_rows, pin_write_then_read]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -138,15 +175,32 @@ def _scale_without_g(packed_rows, scale_rows, g):
     return F.__dict__["_orig_rows"](packed_rows, scale_rows, 1.0)
 
 
+def _writer_swapped_g(key, value, k_cache, v_cache, k_bscales, v_bscales, slots,
+                      src_dtype, k_scale, v_scale):
+    return P.__dict__["_orig_writer"](key, value, k_cache, v_cache, k_bscales, v_bscales,
+                                      slots, src_dtype, v_scale, k_scale)
+
+
+def _writer_ignoring_skip(key, value, k_cache, v_cache, k_bscales, v_bscales, slots,
+                          src_dtype, k_scale, v_scale):
+    slots = np.array([s if s >= 0 else 16 * k_cache.shape[0] - 1 for s in slots])
+    return P.__dict__["_orig_writer"](key, value, k_cache, v_cache, k_bscales, v_bscales,
+                                      slots, src_dtype, k_scale, v_scale)
+
+
 MUTANTS = [("e2m1_encode_scalar", _ties_away), ("e2m1_code_value", _code7_is_5),
-           ("nvfp4_quantize_row", _swapped_nibbles), ("nvfp4_rows_to_f64", _scale_without_g)]
+           ("nvfp4_quantize_row", _swapped_nibbles), ("nvfp4_rows_to_f64", _scale_without_g),
+           ("reshape_and_cache_nvfp4", _writer_swapped_g),
+           ("reshape_and_cache_nvfp4", _writer_ignoring_skip)]
 
 
 @pytest.mark.parametrize("name,fn", MUTANTS, ids=[f.__name__ for _, f in MUTANTS])
 def test_nvfp4_mutant_is_caught(monkeypatch, name, fn):
     monkeypatch.setitem(F.__dict__, "_orig_quantize", F.nvfp4_quantize_row)
     monkeypatch.setitem(F.__dict__, "_orig_rows", F.nvfp4_rows_to_f64)
-    monkeypatch.setattr(F, name, fn)
+    monkeypatch.setitem(P.__dict__, "_orig_writer", P.reshape_and_cache_nvfp4)
+    if hasattr(F, name):
+        monkeypatch.setattr(F, name, fn)
     if hasattr(P, name):
         monkeypatch.setattr(P, name, fn)
     caught = []
