@@ -27,11 +27,27 @@ def kind_of(step):
     return "fp8_e4m3" if step.kv_dtype == F.FP8_E4M3 else step.q_dtype
 
 
+def snapshot(step):
+    """Keep host copies of the step's caches, taken before any GPU call can
+    write them: a step built on the GPU shares its cache tensors with
+    DeviceStep, so reading them after the step would feed the GPU's own
+    writes into the oracle."""
+    step.extra["host_k"] = [host(t) for t in step.k_caches]
+    step.extra["host_v"] = [host(t) for t in step.v_caches]
+    return step
+
+
 def oracle_caches_after_step(step, layer=0):
-    """Oracle copy -> slot map -> write for one layer, from the step's own
-    host inputs.  Returns (k_cache, v_cache, slots)."""
-    kc = host(step.k_caches[layer])
-    vc = host(step.v_caches[layer])
+    """Oracle copy -> slot map -> write for one layer, from the step's
+    inputs as they were before the GPU step.  Returns (k_cache, v_cache,
+    slots)."""
+    if "host_k" in step.extra:
+        kc, vc = step.extra["host_k"][layer], step.extra["host_v"][layer]
+    elif step.k_caches[layer].is_cuda:
+        raise AssertionError("a step built on the GPU needs snapshot(step) before it runs")
+    else:
+        kc = host(step.k_caches[layer])
+        vc = host(step.v_caches[layer])
     if len(step.copy_pairs):
         (kc,), (vc,) = P.copy_blocks([kc], [vc], step.copy_pairs)
     slots = P.slot_mapping(step.block_tables, step.query_start_loc, step.num_computed)

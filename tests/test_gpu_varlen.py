@@ -6,7 +6,7 @@ import pytest
 import torch
 
 import paged_kv_cache_84_amd as pk
-from gpu_util import announce, as_f64, host, oracle_caches_after_step
+from gpu_util import announce, as_f64, host, oracle_caches_after_step, snapshot
 from oracle import formats as F
 from oracle import paged as P
 from synth import configs as C
@@ -108,8 +108,9 @@ def test_varlen_small_mixed_step_full_compare():
     tokens, so some span two runs): caches bit-exact, every output against
     the oracle."""
     announce("varlen small mixed step")
-    s = C.config4(num_prefix_reqs=5, prefix_blocks=6, new_tokens=37, chunk_tokens=150,
-                  num_decodes=9, num_writers=3, lo=20, hi=1500, device=DEV)
+    s = snapshot(C.config4(num_prefix_reqs=5, prefix_blocks=6, new_tokens=37,
+                           chunk_tokens=150, num_decodes=9, num_writers=3, lo=20, hi=1500,
+                           device=DEV))
     ds = pk.step.DeviceStep(s)
     ds.run_varlen()
     torch.cuda.synchronize()
@@ -119,29 +120,3 @@ def test_varlen_small_mixed_step_full_compare():
                               s.query_start_loc, s.num_computed, s.softmax_scale)
     got = as_f64(ds.out[0])
     assert_attention_close(got, ref, "bf16", "varlen step")
-
-
-def test_varlen_mixed_step_full_size_sampled():
-    """The full mixed step (64 x 100-token chunks on the shared prefix, the
-    1,022-token first chunk, 192 decodes up to 8,192 tokens, 64
-    copy-on-write copies) with the unified launch, as the bench times it;
-    sampled rows against the oracle."""
-    announce("varlen mixed full sampled")
-    s = C.config4(device=DEV)
-    ds = pk.step.DeviceStep(s)
-    ds.run_varlen()
-    torch.cuda.synchronize()
-    rk, rv, _ = oracle_caches_after_step(s)
-    q = host(s.q[0])
-    rng = np.random.default_rng(12)
-    t = s.num_prefill_tokens
-    rows = list(rng.integers(0, t, 24)) + list(t + rng.integers(0, 192, 24)) + [0, 6399, 6400,
-                                                                              t, t + 191]
-    got, ref = [], []
-    for row in rows:
-        head = int(rng.integers(0, 32))
-        ref.append(P.prefill_attention_one(q, F.BF16, rk, rv, F.BF16, s.block_tables,
-                                           s.query_start_loc, s.num_computed,
-                                           s.softmax_scale, int(row), head))
-        got.append(as_f64(ds.out[0][row, head]))
-    assert_attention_close(np.array(got), np.array(ref), "bf16", "varlen mixed sampled")
