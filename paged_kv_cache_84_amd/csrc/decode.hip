@@ -5,10 +5,14 @@
 // of a sequence sit in 16-token blocks reached through its block table
 // (section "PagedAttention：为 KV 缓存分页", Fig. 2).
 //
-// Work decomposition: one workgroup per (sequence, kv head, partition of the
-// context).  Each wavefront of the workgroup owns up to four query heads of
-// the kv head's group and walks the partition block by block; both waves of a
-// two-wave workgroup read the same tiles, so the second read hits cache.
+// Work decomposition (decode_sched.h): the batch's blocks are laid end to
+// end -- sequence 0's, then sequence 1's, ... -- and cut into equal chunks.
+// The vector kernel below runs one workgroup per (chunk, kv head); each wave
+// of it owns up to four query heads of the kv head's group and walks the
+// chunk block by block, crossing sequence boundaries (a wave that finishes a
+// sequence inside its chunk writes that sequence's output).  A sequence that
+// spans several chunks leaves one partial per chunk, in record (chunk +
+// sequence) of the workspace; decode_merge_kernel combines them.
 //
 // Per block, one (block, kv head) tile of K and of V (16 rows x head_dim) is
 // fetched with 16-byte loads:
@@ -23,9 +27,8 @@
 // layout.  Softmax is online, in base 2, with a running maximum shared by
 // the wave that is only raised when a score exceeds it by more than 8 (a
 // factor 256 in the weights, harmless in fp32), so the rescale branch is
-// rare.  Each partition leaves (max, sum of weights, weighted sum of values)
-// in the workspace; a second kernel merges the partitions of a sequence with
-// the log-sum-exp rule.
+// rare.  Each partial is (max, sum of weights, weighted sum of values), and
+// the merge combines a sequence's partials with the log-sum-exp rule.
 
 #include <math.h>
 
@@ -1148,3 +1151,4 @@ extern "C" pkv_status paged_attention_decode_append(
                      partition_tokens, workspace, workspace_bytes, stream, 0, new_key,
                      new_value);
 }
+
