@@ -276,6 +276,38 @@ pkv_status paged_attention_decode(void* out, const void* query,
                                   size_t workspace_bytes, void* stream);
 
 /*
+ * paged_attention_decode_noalloc -- paged_attention_decode for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same arguments, layouts, results
+ * (bitwise: same kernels, same split) and errors as paged_attention_decode,
+ * without the workspace: the partials live in a file-scope device array of
+ * PKV_DECODE_SCRATCH_BYTES that each GPU the library runs on holds until the
+ * process ends.  Its address is looked up once per device, on the first call
+ * with that device current (the calling thread's current device must be the
+ * one holding the tensors and running `stream`); no call allocates.
+ *   PKV_ERR_WORKSPACE  the split for these arguments needs more than
+ *                      PKV_DECODE_SCRATCH_BYTES (paged_attention_decode_
+ *                      workspace_size gives the need); nothing is launched
+ * Every call on a GPU shares that GPU's array, which keeps the last call's
+ * contents (the kernels write every record before reading it, so nothing is
+ * cleared): calls that overlap on one GPU -- on two streams, or from two
+ * threads without ordering -- race on it and must not be made.
+ */
+#define PKV_DECODE_SCRATCH_BYTES (64u << 20)
+pkv_status paged_attention_decode_noalloc(void* out, const void* query,
+                                          const void* k_cache, const void* v_cache,
+                                          int32_t num_blocks,
+                                          const int32_t* block_tables,
+                                          int32_t max_blocks_per_seq,
+                                          const int32_t* context_lens,
+                                          int32_t num_seqs, int32_t max_context_len,
+                                          int32_t num_q_heads, int32_t num_kv_heads,
+                                          int32_t head_dim, float softmax_scale,
+                                          pkv_dtype q_dtype, pkv_dtype kv_dtype,
+                                          float k_scale, float v_scale,
+                                          int32_t partition_tokens, void* stream);
+
+/*
  * paged_attention_prefill_chunk -- attention for the query rows of prompt
  * chunks scheduled this step.  A long prompt is split into chunks that share
  * steps with decodes ("vLLM 引擎解剖", section "V1：统一调度预填充与解码",

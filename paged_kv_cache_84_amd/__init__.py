@@ -28,6 +28,7 @@ from ._binding import (  # noqa: F401
     paged_attention_decode,
     paged_attention_decode_append,
     paged_attention_decode_int4,
+    paged_attention_decode_noalloc,
     paged_attention_decode_nvfp4,
     paged_attention_decode_sliding,
     paged_attention_prefill_chunk,

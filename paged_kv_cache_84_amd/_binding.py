@@ -48,6 +48,9 @@ _SIGNATURES = {
     "paged_attention_decode": (_I32, [_P, _P, _P, _P, _I32, _P, _I32, _P, _I32, _I32,
                                       _I32, _I32, _I32, _F, _I32, _I32, _F, _F, _I32,
                                       _P, _SZ, _P]),
+    "paged_attention_decode_noalloc": (_I32, [_P, _P, _P, _P, _I32, _P, _I32, _P, _I32, _I32,
+                                              _I32, _I32, _I32, _F, _I32, _I32, _F, _F, _I32,
+                                              _P]),
     "paged_attention_decode_append": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _P, _I32, _P, _I32,
                                              _I32, _I32, _I32, _I32, _F, _I32, _I32, _F, _F,
                                              _I32, _P, _SZ, _P]),
@@ -279,6 +282,28 @@ def paged_attention_decode(query, k_cache, v_cache, block_tables, context_lens,
         int(partition_tokens), _dev(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), _stream(query))
     _check("paged_attention_decode", st)
+    return out
+
+
+def paged_attention_decode_noalloc(query, k_cache, v_cache, block_tables, context_lens,
+                                   max_context_len, softmax_scale, out, k_scale=1.0,
+                                   v_scale=1.0, partition_tokens=0):
+    """paged_attention_decode with its partials in the library's per-device
+    scratch array (see the header): no workspace, and nothing allocated here
+    either, so `out` must be given."""
+    s, hq, d = query.shape
+    hkv = k_cache.shape[1]
+    assert block_tables.shape[0] >= s and context_lens.shape[0] >= s
+    with torch.cuda.device(query.device):
+        st = library().paged_attention_decode_noalloc(
+            _dev(out, "out", query.dtype), _dev(query, "query"), _dev(k_cache, "k_cache"),
+            _dev(v_cache, "v_cache"), k_cache.shape[0],
+            _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+            _dev(context_lens, "context_lens", torch.int32), s, int(max_context_len), hq,
+            hkv, d, float(softmax_scale), _dtype_code(query, "query"),
+            _dtype_code(k_cache, "k_cache"), float(k_scale), float(v_scale),
+            int(partition_tokens), _stream(query))
+    _check("paged_attention_decode_noalloc", st)
     return out
 
 

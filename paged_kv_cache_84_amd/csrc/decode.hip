@@ -1152,3 +1152,60 @@ extern "C" pkv_status paged_attention_decode_append(
                      new_value);
 }
 
+// ---- allocation-free decode ------------------------------------------------
+// paged_attention_decode with its partials in a file-scope device array
+// instead of a caller workspace, for callers that cannot allocate.  Each GPU
+// the library runs on holds its own copy of the array (kDecodeScratchBytes)
+// until the process ends; host code reaches it only through the address
+// hipGetSymbolAddress returns on that device, looked up once per device on
+// the first call there.  The decode kernels write every record they later
+// read, so nothing in the array needs clearing between calls.
+#include <mutex>
+
+namespace {
+constexpr size_t kDecodeScratchBytes = size_t(PKV_DECODE_SCRATCH_BYTES);
+constexpr int kScratchDevices = 64;
+__device__ __align__(256) char scratch[kDecodeScratchBytes];
+std::mutex scratch_mutex;
+void* scratch_ptr[kScratchDevices];   // per device; null until looked up
+
+pkv_status device_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return PKV_ERR_LAUNCH;
+  if (dev < 0 || dev >= kScratchDevices) return PKV_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return PKV_ERR_LAUNCH;
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return PKV_OK;
+}
+}  // namespace
+
+extern "C" pkv_status paged_attention_decode_noalloc(
+    void* out, const void* query, const void* k_cache, const void* v_cache,
+    int32_t num_blocks, const int32_t* block_tables, int32_t max_blocks_per_seq,
+    const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    float softmax_scale, pkv_dtype q_dtype, pkv_dtype kv_dtype, float k_scale,
+    float v_scale, int32_t partition_tokens, void* stream) {
+  // the size check comes first and touches no device state
+  DecodePlan lay;
+  if (partition_tokens < 0 || partition_tokens % kBlock != 0 ||
+      !make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                 partition_tokens, lay))
+    return PKV_ERR_SHAPE;
+  if (lay.out_bytes + lay.ml_bytes > kDecodeScratchBytes) return PKV_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (num_seqs > 0) {   // an empty batch launches nothing and needs no scratch
+    const pkv_status st = device_scratch(&ws);
+    if (st != PKV_OK) return st;
+  }
+  return decode_impl(out, query, k_cache, v_cache, num_blocks, block_tables,
+                     max_blocks_per_seq, context_lens, num_seqs, max_context_len, num_q_heads,
+                     num_kv_heads, head_dim, softmax_scale, q_dtype, kv_dtype, k_scale, v_scale,
+                     partition_tokens, ws, kDecodeScratchBytes, stream, 0);
+}

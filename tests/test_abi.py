@@ -154,6 +154,23 @@ def test_decode_errors(lib):
     assert lib.paged_attention_decode_num_chunks(4, 32, 8, 1000, 40) == -1
 
 
+def test_decode_noalloc_host_errors(lib):
+    """The allocation-free decode refuses a split larger than its scratch
+    array, and bad sizes, before it touches any device state."""
+    f = lib.paged_attention_decode_noalloc
+    p = 0x100000
+    base = [p, p, p, p, 100, p, 1 << 20, p, 1, 1 << 24, 64, 8, 128, 0.088, BF16, BF16,
+            1.0, 1.0, 16, None]
+    assert f(*base) == WS                               # one partial per 16 tokens of 16 M
+    assert lib.paged_attention_decode_workspace_size(1, 64, 8, 128, 1 << 24, 16) > 64 << 20
+    bad = list(base)
+    bad[18] = 24                                        # partition not a multiple of 16
+    assert f(*bad) == SHAPE
+    bad = list(base)
+    bad[10] = 60                                        # q heads not a multiple of kv heads
+    assert f(*bad) == SHAPE
+
+
 def test_prefill_errors(lib):
     f = lib.paged_attention_prefill_chunk
     p = 0x100000
