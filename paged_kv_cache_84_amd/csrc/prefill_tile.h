@@ -18,7 +18,7 @@
 // straight from global memory into LDS (buffer loads with the LDS-destination
 // bit: no register round trip), through a buffer resource that spans only
 // the block's valid rows, so rows past the context and unusable block ids
-// arrive as zeros.  Two LDS stages alternate: the next tile is in flight
+// arrive as zeros (and the keys of an unusable id are then masked to -inf).  Two LDS stages alternate: the next tile is in flight
 // while the current one is multiplied; one barrier per tile.  Rows are 256
 // bytes; the sixteen 16-byte pieces of a row are stored XOR-swizzled by the
 // row index so that both fragment reads below are free of bank conflicts
@@ -100,10 +100,12 @@ PKV_DEVICE int wave_scan(int v) {
   return v;
 }
 
-// One LDS stage: the K and V rows of a 64-key tile (row-major, swizzled).
+// One LDS stage: the K and V rows of a 64-key tile (row-major, swizzled),
+// and which of its four blocks have unusable ids.
 struct Stage {
   u32x4 k[kTileBytes / 16];
   u32x4 v[kTileBytes / 16];
+  uint32_t bad[kWaves];   // block w of the tile: inside the context, unusable id
 };
 
 }  // namespace pf
@@ -177,7 +179,10 @@ PKV_DEVICE void prefill_tile_at(
   // issue the copies of logical block lb (id already read) into a stage
   auto copy_block = [&](pf::Stage& st, int lb, int32_t id) {
     int rows = min(max(kv_len - lb * kBlock, 0), kBlock);
-    if (!(id >= 0 && id < num_blocks)) rows = 0;
+    const bool usable = id >= 0 && id < num_blocks;
+    // flag for compute(): inside the context but unusable
+    if (lane == 0) st.bad[wave] = (rows > 0 && !usable) ? 1u : 0u;
+    if (!usable) rows = 0;
     const int32_t b = rows > 0 ? id : 0;
     const auto rk = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<char*>(kbase + int64_t(b) * block_bytes), 0, rows * kRowBytes, kRawBufferFlags);
@@ -232,6 +237,19 @@ PKV_DEVICE void prefill_tile_at(
         const u32x4 a = *reinterpret_cast<lds_u32x4_t*>(kl + ka[ks] + kb * kBlockBytes);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) s[kb][qb] = mfma(a, qf[qb][ks], s[kb][qb]);
+      }
+    }
+    // a block inside the context whose id is unusable contributes nothing:
+    // the wave that staged it left a flag in the stage, and its keys get -inf
+    {
+      const u32x4 bad = *reinterpret_cast<lds_u32x4_t*>((lds_char_t*)(&st.bad[0]));
+      if (__builtin_expect((bad[0] | bad[1] | bad[2] | bad[3]) != 0, 0)) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+          if (bad[kb])
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+              s[kb][qb] = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
       }
     }
     // causal mask on tiles that reach past the first query's position

@@ -172,3 +172,66 @@ def test_fig3_schedule_on_the_gpu():
         assert np.array_equal(host(kc), hk) and np.array_equal(host(vc), hv)
         for n in reqs:
             done[n] += step[n]
+
+
+def _excluding_bad_blocks(q, qd, kc, vc, kvd, tables, qsl, comp, scale, nb):
+    """Chunk rows where the keys of unusable block ids (outside [0, nb))
+    contribute nothing: per row, the oracle's softmax over the positions
+    0..p that sit in usable blocks."""
+    hq, hkv = q.shape[1], kc.shape[1]
+    out = np.zeros(q.shape, np.float64)
+    for r in range(len(qsl) - 1):
+        for i in range(int(qsl[r]), int(qsl[r + 1])):
+            p = int(comp[r]) + i - int(qsl[r])
+            for h in range(hq):
+                kvh = h // (hq // hkv)
+                keys, vals = [], []
+                for j in range(P.blocks_needed(p + 1)):
+                    b = int(tables[r][j])
+                    if not 0 <= b < nb:
+                        continue
+                    n = min(16, p + 1 - 16 * j)
+                    keys.append(F.storage_to_f64(P.cache_tile(kc, b, kvh)[:n], kvd))
+                    vals.append(F.storage_to_f64(P.cache_tile(vc, b, kvh)[:n], kvd))
+                out[i, h] = P.attention_row(F.storage_to_f64(q[i, h], qd), np.concatenate(keys),
+                                            np.concatenate(vals), float(np.float32(scale)))
+    return out
+
+
+@pytest.mark.parametrize("path", ["chunk", "varlen"])
+@pytest.mark.parametrize("qd,d", [(F.BF16, 128), (F.F32, 128), (F.BF16, 64)])
+def test_unusable_block_id_contributes_nothing(path, qd, d):
+    """A block id outside the cache inside a chunk's context (the header's
+    contract: such a block contributes nothing) gives the same rows as the
+    oracle's softmax over the other keys, on the matrix-core tile (bf16, d128),
+    the vector rows (fp32 or d64) and the unified launch (wide and narrow
+    requests)."""
+    if path == "varlen" and not (qd == F.BF16 and d == 128):
+        pytest.skip("the unified launch takes bf16, head_dim 128")
+    announce("prefill unusable block id", path, qd, d)
+    from synth import rng as R
+    from synth.allocator import BlockPool, Sequence, tables_array
+    rng = np.random.default_rng(17)
+    computed, new = [40, 0, 100, 7], [30, 50, 3, 60]
+    lens_total = [c + n for c, n in zip(computed, new)]
+    nb = sum(P.blocks_needed(L) for L in lens_total) + 2
+    pool = BlockPool(nb, rng.permutation(nb))
+    tables = tables_array([Sequence.fresh(pool, L) for L in lens_total])
+    tables[0, 1] = nb + 5          # positions 16..31 of request 0
+    tables[1, 2] = -1              # positions 32..47 of request 1, inside the chunk
+    tables[2, 0] = nb              # request 2's first block (a narrow request)
+    shape = (nb, 2, 16, d)
+    kc, vc = R.normal(shape, qd, 47, 1, DEV), R.normal(shape, qd, 47, 2, DEV)
+    qsl = np.concatenate([[0], np.cumsum(new)]).astype(np.int32)
+    comp = np.array(computed, np.int32)
+    q = R.normal((int(qsl[-1]), 8, d), qd, 47, 3, DEV)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    bt, qs, cp = (torch.as_tensor(a, device=DEV) for a in (tables, qsl, comp))
+    if path == "chunk":
+        out = pk.paged_attention_prefill_chunk(q, kc, vc, bt, qs, cp, int(max(new)), scale)
+    else:
+        out = pk.paged_attention_varlen(q, kc, vc, bt, qs, cp, int(max(lens_total)), scale)
+    torch.cuda.synchronize()
+    ref = _excluding_bad_blocks(host(q), qd, host(kc), host(vc), qd, tables, qsl, comp, scale, nb)
+    assert_attention_close(as_f64(out), ref, "f32" if qd == F.F32 else "bf16",
+                           "unusable block id")
