@@ -775,6 +775,22 @@ static bool make_plan(int32_t s, int32_t hq, int32_t hkv, int32_t d, int32_t max
   return true;
 }
 
+// Waves per SIMD the library's own split plans for: a wave serving two kv
+// heads of an fp8 cache covers a chunk of both, so the split doubles the
+// chunks to keep PKV_FP8_PAIR_WAVES_PER_SIMD waves on every SIMD.
+#ifndef PKV_FP8_PAIR_WAVES_PER_SIMD
+#define PKV_FP8_PAIR_WAVES_PER_SIMD 2
+#endif
+static int split_waves_per_simd(pkv_dtype kv_dtype, int group, int num_kv_heads) {
+#if PKV_DECODE_USE_MFMA
+  if (decode_mfma_heads_per_wave(kv_dtype, group, num_kv_heads) == 2)
+    return 2 * PKV_FP8_PAIR_WAVES_PER_SIMD;
+#endif
+  return 1;
+}
+static_assert(2 * PKV_FP8_PAIR_WAVES_PER_SIMD <= kInt4WavesPerSimd,
+              "workspace sized by the int4 plan");
+
 template <typename QT, int D>
 static pkv_status launch_merge(void* out, const int32_t* lens, int32_t s, int32_t max_len,
                                int32_t hq, float v_scale, const DecodePlan& plan, void* ws,
@@ -891,6 +907,7 @@ namespace pkv {
 #ifndef PKV_FP8_WAVES_PER_SIMD
 #define PKV_FP8_WAVES_PER_SIMD 3
 #endif
+
 static pkv_status mfma_decode(void* out, const void* query, const void* k_cache,
                               const void* v_cache, const void* k_scales,
                               const void* v_scales, int32_t num_blocks,
@@ -902,11 +919,14 @@ static pkv_status mfma_decode(void* out, const void* query, const void* k_cache,
                               void* workspace, void* stream, int32_t window = 0,
                               const void* new_k = nullptr, const void* new_v = nullptr,
                               float k_scale = 1.0f) {
+  const int nh = decode_mfma_heads_per_wave(kv_dtype, num_q_heads / num_kv_heads, num_kv_heads);
   const int64_t target = int64_t(PKV_DECODE_TARGET_WAVES) *
-                         (kv_dtype == PKV_BF16 ? 1 : PKV_FP8_WAVES_PER_SIMD);
+                         (nh == 2 ? PKV_FP8_PAIR_WAVES_PER_SIMD
+                                  : kv_dtype == PKV_BF16 ? 1 : PKV_FP8_WAVES_PER_SIMD);
   const int64_t per_wave =
       lay.fixed_chunk > 0
-          ? std::max<int64_t>(1, (int64_t(lay.num_chunks) * num_kv_heads + target - 1) / target)
+          ? std::max<int64_t>(1, (int64_t(lay.num_chunks) * (num_kv_heads / nh) + target - 1) /
+                                     target)
           : 1;
   DecodeMfmaArgs a{out, query, k_cache, v_cache, num_blocks, block_tables,
                    max_blocks_per_seq, context_lens, num_seqs, max_context_len,
@@ -915,6 +935,7 @@ static pkv_status mfma_decode(void* out, const void* query, const void* k_cache,
                    static_cast<float*>(workspace),
                    reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.out_bytes),
                    stream, k_scales, v_scales, window, new_k, new_v, k_scale};
+  a.heads_per_wave = nh;
   if (launch_decode_mfma(a) != PKV_OK) return PKV_ERR_LAUNCH;
   hipStream_t st = as_stream(stream);
   return head_dim == 64
@@ -988,7 +1009,7 @@ static pkv_status decode_impl(
     return PKV_ERR_ALIGN;
   DecodePlan lay;
   if (!make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
-                 partition_tokens, lay) ||
+                 partition_tokens, lay, split_waves_per_simd(kv_dtype, group, num_kv_heads)) ||
       int64_t(num_seqs) * num_q_heads > 0x7fffffff)
     return PKV_ERR_SHAPE;
   if (!workspace || workspace_bytes < lay.out_bytes + lay.ml_bytes)
@@ -1194,9 +1215,11 @@ extern "C" pkv_status paged_attention_decode_noalloc(
     float v_scale, int32_t partition_tokens, void* stream) {
   // the size check comes first and touches no device state
   DecodePlan lay;
-  if (partition_tokens < 0 || partition_tokens % kBlock != 0 ||
+  if (partition_tokens < 0 || partition_tokens % kBlock != 0 || num_kv_heads <= 0 ||
+      num_q_heads % num_kv_heads != 0 ||
       !make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
-                 partition_tokens, lay))
+                 partition_tokens, lay,
+                 split_waves_per_simd(kv_dtype, num_q_heads / num_kv_heads, num_kv_heads)))
     return PKV_ERR_SHAPE;
   if (lay.out_bytes + lay.ml_bytes > kDecodeScratchBytes) return PKV_ERR_WORKSPACE;
   void* ws = nullptr;

@@ -36,11 +36,17 @@ struct DecodeMfmaArgs {
   const void* new_k = nullptr;
   const void* new_v = nullptr;
   float k_scale = 1.0f;
+  // kv heads per wave: 1, or 2 (see decode_mfma_heads_per_wave)
+  int32_t heads_per_wave = 1;
 };
 
 // bf16 queries with a bf16 or fp8 E4M3 cache (head_dim 64 or 128), or an int4
 // per token-head or nvfp4-style cache (head_dim 128); group <= 16.
 bool decode_mfma_supported(pkv_dtype q_dtype, pkv_dtype kv_dtype, int head_dim, int group);
+// kv heads one wave of the chunk kernel serves: 2 for fp8 caches whose query
+// groups fit two to a wave's 16 columns (group <= 8, an even number of kv
+// heads), else 1.
+int decode_mfma_heads_per_wave(pkv_dtype kv_dtype, int group, int num_kv_heads);
 // Launches the chunk kernel only; the caller launches the merge.
 pkv_status launch_decode_mfma(const DecodeMfmaArgs& a);
 

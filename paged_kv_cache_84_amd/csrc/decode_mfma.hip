@@ -298,7 +298,12 @@ PKV_DEVICE void cursor_to(SeqCursor& c, int x, const BatchScan& sc, const int32_
   }
 }
 
-template <typename KVT, int D>
+// NH kv heads per wave (1, or 2 for groups of at most 8): with two, the
+// wave's 16 MFMA columns hold both heads' query groups (columns 0..7 the
+// first kv head's, 8..15 the second's), so the softmax, the cursor and table
+// walk and the loop control are shared by two heads' tiles; each product is
+// taken once per head and each column keeps the one of its own head.
+template <typename KVT, int D, int NH>
 __global__ __launch_bounds__(64) void decode_mfma_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
     // not __restrict__: the append path stores into the caches it then reads
@@ -312,14 +317,19 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
     const void* __restrict__ k_scales, const void* __restrict__ v_scales, int32_t window,
     const uint16_t* __restrict__ new_k, const uint16_t* __restrict__ new_v, float k_scale) {
   using M = MGeom<KVT, D>;
-  __shared__ __align__(16) char vl[kBlock * M::kVStride];
-  const int kvh = blockIdx.x % num_kv_heads;
-  const int wg = blockIdx.x / num_kv_heads;
+  static_assert(NH == 1 || (NH == 2 && !kPacked4<KVT>), "two heads per wave: bf16 or fp8");
+  __shared__ __align__(16) char vl_all[NH][kBlock * M::kVStride];
+  const int kv_groups = num_kv_heads / NH;
+  const int kvh0 = (blockIdx.x % kv_groups) * NH;   // first kv head of this wave
+  const int wg = blockIdx.x / kv_groups;
   const int lane = lane_id();
   const int n16 = lane % 16;          // head column of this lane
   const int j = lane / 16;            // lane group
-  const bool head_ok = n16 < group;
-  const int head = kvh * group + (head_ok ? n16 : 0);
+  const int half = NH == 2 ? n16 / 8 : 0;            // which of the wave's kv heads
+  const int hcol = NH == 2 ? n16 % 8 : n16;          // column within that head's group
+  const bool head_ok = hcol < group;
+  const int kvh = kvh0 + half;                        // this lane's kv head
+  const int head = kvh * group + (head_ok ? hcol : 0);
 
   // This wave walks the blocks [b0, b1) of the flattened batch: chunks
   // wg * chunks_per_wave .. + chunks_per_wave - 1, each of c blocks.
@@ -332,8 +342,8 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
   const int64_t head_stride = int64_t(kBlock) * M::kRowBytes /
                               int64_t(sizeof(typename KVT::storage));
   const int64_t block_stride = int64_t(num_kv_heads) * head_stride;
-  auto tile = [&](const typename KVT::storage* base, int32_t b) {
-    return base + int64_t(b) * block_stride + int64_t(kvh) * head_stride;
+  auto tile = [&](const typename KVT::storage* base, int32_t b, int e = 0) {
+    return base + int64_t(b) * block_stride + int64_t(kvh0 + e) * head_stride;
   };
   auto valid = [&](int32_t b) { return b >= 0 && b < num_blocks; };
   // int4: the 16 float scales of (block b, kvh); nvfp4: its 128-byte tile
@@ -358,8 +368,10 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
   };
   // tr-read address of this lane: key lane/4, dims 4 (lane%4) of each slice
   typedef __attribute__((address_space(3))) char lds_char_t;
-  lds_i16x4_t* const vt_base = reinterpret_cast<lds_i16x4_t*>(
-      (lds_char_t*)vl + (lane / 4) * M::kVStride + (lane % 4) * 8);
+  auto vt_base = [&](int e) {
+    return reinterpret_cast<lds_i16x4_t*>((lds_char_t*)vl_all[e] + (lane / 4) * M::kVStride +
+                                          (lane % 4) * 8);
+  };
 
   // Three cursors walk the range: `cc` at the block being multiplied, `lc`
   // one block ahead (its K/V pieces and, on entering a sequence, its Q are
@@ -389,13 +401,17 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
           const int i = pos / kBlock;
           const int32_t id =
               i < max_blocks ? load_scalar(block_tables, int64_t(wc.s) * max_blocks + i) : -1;
+#pragma unroll
+          for (int e = 0; e < NH; ++e) {
           if (valid(id) && 2 * lane < D) {
             const int64_t row = int64_t(pos % kBlock) * D + 2 * lane;
-            const int64_t src = (int64_t(wc.s) * num_kv_heads + kvh) * D + 2 * lane;
+            const int64_t src = (int64_t(wc.s) * num_kv_heads + kvh0 + e) * D + 2 * lane;
             const uint32_t kw = *reinterpret_cast<const uint32_t*>(new_k + src);
             const uint32_t vw = *reinterpret_cast<const uint32_t*>(new_v + src);
-            typename KVT::storage* kd = const_cast<typename KVT::storage*>(tile(k_cache, id)) + row;
-            typename KVT::storage* vd = const_cast<typename KVT::storage*>(tile(v_cache, id)) + row;
+            typename KVT::storage* kd =
+                const_cast<typename KVT::storage*>(tile(k_cache, id, e)) + row;
+            typename KVT::storage* vd =
+                const_cast<typename KVT::storage*>(tile(v_cache, id, e)) + row;
             if constexpr (KVT::bytes == 2) {
               *reinterpret_cast<uint32_t*>(kd) = kw;
               *reinterpret_cast<uint32_t*>(vd) = vw;
@@ -405,6 +421,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
               *reinterpret_cast<uint16_t*>(vd) =
                   uint16_t(f32_to_e4m3(bf16_lo(vw) / v_scale) | (f32_to_e4m3(bf16_hi(vw) / v_scale) << 8));
             }
+          }
           }
         }
         if (wc.before + wc.n >= b1 || wc.s + 1 >= num_seqs) break;
@@ -437,22 +454,27 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
     id_next = table_id(ic, b0 + 1);
   }
   const int32_t b_any = valid(id_cur) ? id_cur : 0;   // a block to re-read
-  KRegs<KVT, D> kr;
-  VRegs<KVT, D> vr;
+  KRegs<KVT, D> kr[NH];
+  VRegs<KVT, D> vr[NH];
   // V before K, the order of the loop's own loads, so that each wait inside
   // the loop covers exactly the pieces it needs
-  load_v<KVT, D>(vr, tile(v_cache, b_any), lane);
-  if constexpr (kInt4<KVT>) vr.sc = load_scales(scale_row(v_scales, b_any), lane);
-  if constexpr (kNvfp4<KVT>) vr.sc[0] = load_bscales(bscale_tile(v_scales, b_any), v_bscale_offset(lane));
+#pragma unroll
+  for (int e = 0; e < NH; ++e) load_v<KVT, D>(vr[e], tile(v_cache, b_any, e), lane);
+  if constexpr (kInt4<KVT>) vr[0].sc = load_scales(scale_row(v_scales, b_any), lane);
+  if constexpr (kNvfp4<KVT>) vr[0].sc[0] = load_bscales(bscale_tile(v_scales, b_any), v_bscale_offset(lane));
   __builtin_amdgcn_sched_barrier(0);
-  load_k<KVT, D>(kr, tile(k_cache, b_any), lane);
-  if constexpr (kInt4<KVT>) kr.sc = load_scales(scale_row(k_scales, b_any), lane);
-  if constexpr (kNvfp4<KVT>) kr.sc[0] = load_bscales(bscale_tile(k_scales, b_any), k_bscale_offset(lane));
+#pragma unroll
+  for (int e = 0; e < NH; ++e) load_k<KVT, D>(kr[e], tile(k_cache, b_any, e), lane);
+  if constexpr (kInt4<KVT>) kr[0].sc = load_scales(scale_row(k_scales, b_any), lane);
+  if constexpr (kNvfp4<KVT>) kr[0].sc[0] = load_bscales(bscale_tile(k_scales, b_any), k_bscale_offset(lane));
   __builtin_amdgcn_sched_barrier(0);
 
-  f32x4_t acc[M::kMTiles];
+  // O^T per head of the wave (a column keeps the one of its own head)
+  f32x4_t acc[NH][M::kMTiles];
 #pragma unroll
-  for (int mt = 0; mt < M::kMTiles; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int e = 0; e < NH; ++e)
+#pragma unroll
+    for (int mt = 0; mt < M::kMTiles; ++mt) acc[e][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   // running max starts finite: a fully masked block then gives weights
   // 2^-inf = 0 instead of 2^(-inf + inf)
   float m = kNoMax, l = 0.f;
@@ -469,12 +491,14 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
     // the next block (possibly of the next sequence), or a re-read past b1
     const bool more = x + 1 < b1;
     const int32_t bn = (more && valid(id_next)) ? id_next : b_any;
-    stage_v<KVT, D>(vr, vl, lane, rows);
-    const u32x4 vsc = vr.sc;          // int4: this block's V scales (before the reload)
+#pragma unroll
+    for (int e = 0; e < NH; ++e) stage_v<KVT, D>(vr[e], vl_all[e], lane, rows);
+    const u32x4 vsc = vr[0].sc;       // int4: this block's V scales (before the reload)
     __builtin_amdgcn_sched_barrier(0);
-    load_v<KVT, D>(vr, tile(v_cache, bn), lane);
-    if constexpr (kInt4<KVT>) vr.sc = load_scales(scale_row(v_scales, bn), lane);
-    if constexpr (kNvfp4<KVT>) vr.sc[0] = load_bscales(bscale_tile(v_scales, bn), v_bscale_offset(lane));
+#pragma unroll
+    for (int e = 0; e < NH; ++e) load_v<KVT, D>(vr[e], tile(v_cache, bn, e), lane);
+    if constexpr (kInt4<KVT>) vr[0].sc = load_scales(scale_row(v_scales, bn), lane);
+    if constexpr (kNvfp4<KVT>) vr[0].sc[0] = load_bscales(bscale_tile(v_scales, bn), v_bscale_offset(lane));
     __builtin_amdgcn_sched_barrier(0);
     // Q of a sequence entered by the next block
     const bool new_seq = more && x + 1 >= lc.before + lc.n;
@@ -489,14 +513,23 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
       cursor_to(ic, x + 2, sc, context_lens, max_len, window);
       id_new = table_id(ic, x + 2);
     }
-    // S^T = K . Q^T
+    // S^T = K . Q^T, per head of the wave; a column keeps its own head's
     f32x4_t st = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < M::kKSteps; ++ks) st = mfma_k32(k_operand<KVT, D>(kr, ks), qb[ks], st);
-    const u32x4 ksc = kr.sc;          // int4: this block's K scales (before the reload)
-    load_k<KVT, D>(kr, tile(k_cache, bn), lane);
-    if constexpr (kInt4<KVT>) kr.sc = load_scales(scale_row(k_scales, bn), lane);
-    if constexpr (kNvfp4<KVT>) kr.sc[0] = load_bscales(bscale_tile(k_scales, bn), k_bscale_offset(lane));
+    for (int ks = 0; ks < M::kKSteps; ++ks) st = mfma_k32(k_operand<KVT, D>(kr[0], ks), qb[ks], st);
+    if constexpr (NH == 2) {
+      f32x4_t st1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < M::kKSteps; ++ks)
+        st1 = mfma_k32(k_operand<KVT, D>(kr[1], ks), qb[ks], st1);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) st[r] = half ? st1[r] : st[r];
+    }
+    const u32x4 ksc = kr[0].sc;       // int4: this block's K scales (before the reload)
+#pragma unroll
+    for (int e = 0; e < NH; ++e) load_k<KVT, D>(kr[e], tile(k_cache, bn, e), lane);
+    if constexpr (kInt4<KVT>) kr[0].sc = load_scales(scale_row(k_scales, bn), lane);
+    if constexpr (kNvfp4<KVT>) kr[0].sc[0] = load_bscales(bscale_tile(k_scales, bn), k_bscale_offset(lane));
     // online softmax over this lane's 4 keys of its head
     float sv[4];
     bool raise = false;
@@ -520,7 +553,9 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
       l *= alpha;
       if constexpr (kInt4<KVT>) lp *= alpha;
 #pragma unroll
-      for (int mt = 0; mt < M::kMTiles; ++mt) acc[mt] *= alpha;
+      for (int e = 0; e < NH; ++e)
+#pragma unroll
+        for (int mt = 0; mt < M::kMTiles; ++mt) acc[e][mt] *= alpha;
     }
     float p[4];
 #pragma unroll
@@ -549,11 +584,13 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
     const i16x4_t plo = __builtin_bit_cast(i16x4_t, uint2{lo[0], lo[1]});
     // O^T += V^T . P^T
 #pragma unroll
-    for (int mt = 0; mt < M::kMTiles; ++mt) {
-      const i16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(vt_base + mt * 4);
-      acc[mt] = mfma_k16(a, phi, acc[mt]);
-      acc[mt] = mfma_k16(a, plo, acc[mt]);
-    }
+    for (int e = 0; e < NH; ++e)
+#pragma unroll
+      for (int mt = 0; mt < M::kMTiles; ++mt) {
+        const i16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(vt_base(e) + mt * 4);
+        acc[e][mt] = mfma_k16(a, phi, acc[e][mt]);
+        acc[e][mt] = mfma_k16(a, plo, acc[e][mt]);
+      }
     id_cur = id_next;
     id_next = id_new;
 
@@ -568,31 +605,39 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
         float lpt = lp + shfl_xor(lp, 16);
         lpt += shfl_xor(lpt, 32);
 #pragma unroll
-        for (int mt = 0; mt < M::kMTiles; ++mt) acc[mt] -= kInt4Offset * lpt;
+        for (int mt = 0; mt < M::kMTiles; ++mt) acc[0][mt] -= kInt4Offset * lpt;
       }
+      // this lane's column: its own head's products
+      f32x4_t o[M::kMTiles];
+#pragma unroll
+      for (int mt = 0; mt < M::kMTiles; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[mt][r] = (NH == 2 && half) ? acc[NH - 1][mt][r] : acc[0][mt][r];
       if (head_ok) {
         if (seg_start == cc.before && x + 1 == seq_end) {
           const float f = v_scale / lt;
-          uint16_t* o = out + (int64_t(cc.s) * num_q_heads + head) * D + 4 * j;
+          uint16_t* op = out + (int64_t(cc.s) * num_q_heads + head) * D + 4 * j;
 #pragma unroll
           for (int mt = 0; mt < M::kMTiles; ++mt) {
-            const uint2 w = {pack_bf16_rne(acc[mt][0] * f, acc[mt][1] * f),
-                             pack_bf16_rne(acc[mt][2] * f, acc[mt][3] * f)};
-            *reinterpret_cast<uint2*>(o + mt * 16) = w;
+            const uint2 w = {pack_bf16_rne(o[mt][0] * f, o[mt][1] * f),
+                             pack_bf16_rne(o[mt][2] * f, o[mt][3] * f)};
+            *reinterpret_cast<uint2*>(op + mt * 16) = w;
           }
         } else {
           // the partial of (chunk seg_start / c, sequence) -> record chunk + sequence
           const int64_t idx = int64_t(chunk + cc.s) * num_q_heads + head;
-          float* o = rec_out + idx * D + 4 * j;
+          float* po = rec_out + idx * D + 4 * j;
 #pragma unroll
           for (int mt = 0; mt < M::kMTiles; ++mt)
-            *reinterpret_cast<float4*>(o + mt * 16) =
-                make_float4(acc[mt][0], acc[mt][1], acc[mt][2], acc[mt][3]);
+            *reinterpret_cast<float4*>(po + mt * 16) =
+                make_float4(o[mt][0], o[mt][1], o[mt][2], o[mt][3]);
           if (j == 0) reinterpret_cast<float2*>(rec_ml)[idx] = make_float2(m, lt);
         }
       }
 #pragma unroll
-      for (int mt = 0; mt < M::kMTiles; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int e = 0; e < NH; ++e)
+#pragma unroll
+        for (int mt = 0; mt < M::kMTiles; ++mt) acc[e][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       m = kNoMax;
       l = 0.f;
       lp = 0.f;
@@ -611,10 +656,10 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
   }
 }
 
-template <typename KVT, int D>
+template <typename KVT, int D, int NH = 1>
 static pkv_status launch_one(const DecodeMfmaArgs& a) {
   const int waves = (a.num_chunks + a.chunks_per_wave - 1) / a.chunks_per_wave;
-  hipLaunchKernelGGL((decode_mfma_kernel<KVT, D>), dim3(waves * a.num_kv_heads),
+  hipLaunchKernelGGL((decode_mfma_kernel<KVT, D, NH>), dim3(waves * (a.num_kv_heads / NH)),
                      dim3(kWave), 0, as_stream(a.stream), static_cast<uint16_t*>(a.out),
                      static_cast<const uint16_t*>(a.query),
                      static_cast<const typename KVT::storage*>(a.k_cache),
@@ -628,6 +673,18 @@ static pkv_status launch_one(const DecodeMfmaArgs& a) {
   return launch_status();
 }
 
+#ifndef PKV_DECODE_PAIR_FP8
+#define PKV_DECODE_PAIR_FP8 1
+#endif
+#ifndef PKV_DECODE_PAIR_BF16
+#define PKV_DECODE_PAIR_BF16 0
+#endif
+int decode_mfma_heads_per_wave(pkv_dtype kv_dtype, int group, int num_kv_heads) {
+  const bool pair = kv_dtype == PKV_FP8_E4M3 ? PKV_DECODE_PAIR_FP8
+                                             : kv_dtype == PKV_BF16 && PKV_DECODE_PAIR_BF16;
+  return (pair && group <= 8 && num_kv_heads % 2 == 0) ? 2 : 1;
+}
+
 bool decode_mfma_supported(pkv_dtype q_dtype, pkv_dtype kv_dtype, int head_dim, int group) {
   if (kv_dtype == PKV_INT4 || kv_dtype == PKV_NVFP4)
     return q_dtype == PKV_BF16 && head_dim == 128 && group >= 1 && group <= 16;
@@ -638,8 +695,13 @@ bool decode_mfma_supported(pkv_dtype q_dtype, pkv_dtype kv_dtype, int head_dim, 
 pkv_status launch_decode_mfma(const DecodeMfmaArgs& a) {
   if (a.kv_dtype == PKV_INT4) return launch_one<INT4, 128>(a);
   if (a.kv_dtype == PKV_NVFP4) return launch_one<NVFP4, 128>(a);
-  if (a.kv_dtype == PKV_BF16)
+  if (a.kv_dtype == PKV_BF16) {
+    if (a.heads_per_wave == 2)
+      return a.head_dim == 64 ? launch_one<BF16, 64, 2>(a) : launch_one<BF16, 128, 2>(a);
     return a.head_dim == 64 ? launch_one<BF16, 64>(a) : launch_one<BF16, 128>(a);
+  }
+  if (a.heads_per_wave == 2)
+    return a.head_dim == 64 ? launch_one<FP8, 64, 2>(a) : launch_one<FP8, 128, 2>(a);
   return a.head_dim == 64 ? launch_one<FP8, 64>(a) : launch_one<FP8, 128>(a);
 }
 
