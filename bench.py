@@ -117,6 +117,8 @@ def copy_calibration(nbytes=1 << 30, reps=5):
 
 
 def time_region(fn, iters, stream):
+    """Mean ms per call over `iters` calls bracketed by two HIP events on the
+    stream (synchronised before and after)."""
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -126,6 +128,28 @@ def time_region(fn, iters, stream):
     end.record(stream)
     end.synchronize()
     return start.elapsed_time(end) / iters        # ms
+
+
+def time_each(fn, iters, stream):
+    """Per-call ms of `iters` calls, each between its own pair of HIP events
+    on the stream: median, min and p90 (a pass of its own, after the
+    bracketed mean, so the events do not enter the mean)."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(iters)]
+    torch.cuda.synchronize()
+    for i in range(iters):
+        ev[i][0].record(stream)
+        fn(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in ev])
+    return {"median_ms": round(float(np.median(t)), 4), "min_ms": round(float(t.min()), 4),
+            "p90_ms": round(float(np.percentile(t, 90)), 4), "calls": iters}
+
+
+def timed(fn, iters, stream):
+    """(bracketed mean ms, per-call statistics)."""
+    return time_region(fn, iters, stream), time_each(fn, iters, stream)
 
 
 # ----------------------------------------------------------- CPU baseline
@@ -173,12 +197,157 @@ def cpu_baseline(step, budget_s=15.0):
     wall = time.perf_counter() - t0
     tokens = int(step.decode_context_lens.astype(np.int64).sum()) * passes
     kv_bytes = tokens * 2 * step.num_kv_heads * step.head_dim * 2
+    seq0_bytes = int(step.decode_context_lens[0]) * 2 * step.num_kv_heads * step.head_dim * 2
     return {"value": round(kv_bytes / wall / 1e9, 4), "unit": "GB/s", "cores": workers,
             "kind": "oracle",
+            "single_core": {"value": round(seq0_bytes / one / 1e9, 4), "unit": "GB/s",
+                            "seconds": round(one, 3),
+                            "sample": "sequence 0 of the batch (32 heads), one process, "
+                                      "one BLAS thread"},
             "sample": f"{passes} pass(es) over all {nseq} sequences x 32 heads of the "
                       f"decode batch ({tokens} KV tokens), {wall:.1f} s wall on "
                       f"{workers} worker processes with one BLAS thread each",
             "kv_tokens_per_s": round(tokens / wall, 1)}
+
+
+def _cpu_decode_unit(u):
+    """The oracle's decode over one (sequence, kv head) sample unit: the
+    sequence's tiles of that head as a compact cache with the identity table."""
+    from oracle import paged as P
+    q, k, v, length, qd, kd, scale, ks, vs = u
+    table = np.arange(k.shape[0], dtype=np.int32)[None, :]
+    return P.decode_attention(q[None], qd, k[:, None], v[:, None], kd, table,
+                              np.array([length], np.int32), scale, ks, vs)
+
+
+def _cpu_prefill_unit(u):
+    """The oracle's chunked prefill over one (request, kv head) sample unit."""
+    from oracle import paged as P
+    q, k, v, computed, qd, kd, scale = u
+    n = q.shape[0]
+    table = np.arange(k.shape[0], dtype=np.int32)[None, :]
+    return P.prefill_attention(q, qd, k[:, None], v[:, None], kd, table,
+                               np.array([0, n], np.int32), np.array([computed], np.int32),
+                               scale)
+
+
+def _bf16_bits(rng, shape):
+    """N(0,1) samples as bf16 bit patterns (truncated from binary32)."""
+    return (rng.standard_normal(shape, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _fp8_codes(rng, shape):
+    """Uniformly drawn finite E4M3 codes (any finite code serves for timing)."""
+    c = rng.integers(0, 0x7F, size=shape, dtype=np.uint8)           # magnitudes, no NaN
+    return c | (rng.integers(0, 2, size=shape, dtype=np.uint8) << 7)
+
+
+def _timed_pool(fn, units, workers):
+    ctx = mp.get_context("fork")
+    with ctx.Pool(workers, initializer=_one_blas_thread) as pool:
+        t0 = time.perf_counter()
+        pool.map(fn, units, chunksize=1)
+        return time.perf_counter() - t0
+
+
+def cpu_extra_baselines(workers):
+    """The oracle on bounded samples of the other workloads, in their own
+    units, each extrapolated to the whole workload by its rate (labelled):
+    the mixed step's chunked prefill (flop/s over two 100-row requests on the
+    2,000-token shared prefix, 94% of the step's pairs are of this kind), the
+    70B fp8 long-context decode (one of the six sequences) and the 32-layer
+    MHA step (two (layer, sequence) pairs of the 1,024).  Values are seeded
+    N(0,1) bf16 or finite fp8 codes; the oracle's time does not depend on them."""
+    rng = np.random.default_rng(2026)
+    d, out = 128, {}
+    # mixed-step prefill: request rows at positions 2000..2099, 32 q / 8 kv heads
+    n, c, hkv, group = 100, 2000, 8, 4
+    nb = (c + n + 15) // 16
+    units = [(_bf16_bits(rng, (n, group, d)), _bf16_bits(rng, (nb, 16, d)),
+              _bf16_bits(rng, (nb, 16, d)), c, "bf16", "bf16", float(np.float32(d ** -0.5)))
+             for _ in range(2 * hkv)]
+    wall = _timed_pool(_cpu_prefill_unit, units, workers)
+    pairs = 2 * (n * c + n * (n + 1) // 2)
+    flops = 4.0 * d * hkv * group * pairs
+    out["mixed_step_prefill"] = {
+        "value": round(flops / wall / 1e9, 3), "unit": "GFLOP/s", "cores": workers,
+        "kind": "oracle",
+        "sample": f"2 requests x 100 chunk rows on a 2,000-token prefix x 32 heads "
+                  f"({pairs} (query, key) pairs per head), {wall:.2f} s wall",
+        "extrapolated_prefill_s": round(223.6e9 / (flops / wall), 2)}
+    # 70B fp8 long context: one sequence of 131,072 tokens, 64 q / 8 kv heads
+    L, hkv, group = 131072, 8, 8
+    nb = L // 16
+    units = [(_bf16_bits(rng, (group, d)), _fp8_codes(rng, (nb, 16, d)),
+              _fp8_codes(rng, (nb, 16, d)), L, "bf16", "fp8_e4m3", 1.0, 0.01, 0.01)
+             for _ in range(hkv)]
+    wall = _timed_pool(_cpu_decode_unit, units, workers)
+    nbytes = L * hkv * d * 2
+    out["longctx_decode"] = {
+        "value": round(nbytes / wall / 1e9, 3), "unit": "GB/s", "cores": workers,
+        "kind": "oracle",
+        "sample": f"1 of the 6 sequences (131,072 tokens) x 8 kv heads x 64 q heads, "
+                  f"{wall:.2f} s wall",
+        "extrapolated_step_s": round(6 * wall, 2)}
+    # 32-layer MHA: two (layer, sequence) pairs of 8,192 tokens, 32 / 32 heads
+    L, hkv = 8192, 32
+    nb = L // 16
+    units = [(_bf16_bits(rng, (1, d)), _bf16_bits(rng, (nb, 16, d)),
+              _bf16_bits(rng, (nb, 16, d)), L, "bf16", "bf16", float(np.float32(d ** -0.5)),
+              1.0, 1.0) for _ in range(2 * hkv)]
+    wall = _timed_pool(_cpu_decode_unit, units, workers)
+    nbytes = 2 * L * hkv * d * 2 * 2
+    out["mha_decode"] = {
+        "value": round(nbytes / wall / 1e9, 3), "unit": "GB/s", "cores": workers,
+        "kind": "oracle",
+        "sample": f"2 of the 1,024 (layer, sequence) pairs (8,192 tokens, 32 heads), "
+                  f"{wall:.2f} s wall",
+        "extrapolated_step_s": round(512 * wall, 1)}
+    return out
+
+
+def host_info():
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "cpus_usable": len(os.sched_getaffinity(0))}
+
+
+def gpu_clock_under_load(busy, seconds=1.5):
+    """The shader clock rocm-smi reports while `busy` keeps the GPU loaded
+    (its own thread samples it mid-way); None where rocm-smi is missing or
+    prints no sclk."""
+    import re
+    import subprocess
+    import threading
+    got = {}
+
+    def sample():
+        time.sleep(seconds / 3)
+        try:
+            r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True,
+                               text=True, timeout=30)
+            got["text"] = r.stdout
+        except (OSError, subprocess.SubprocessError) as e:
+            got["error"] = str(e)
+
+    th = threading.Thread(target=sample)
+    th.start()
+    t0 = time.perf_counter()
+    while th.is_alive() or time.perf_counter() - t0 < seconds:
+        busy()
+        torch.cuda.synchronize()
+    th.join()
+    text = got.get("text") or ""
+    mhz = [int(x) for x in re.findall(r"sclk[^(]*\((\d+)\s*Mhz\)", text, flags=re.I)]
+    return {"sclk_mhz": max(mhz) if mhz else None, "source": "rocm-smi --showclocks, "
+            "sampled while the decode step runs", "error": got.get("error")}
 
 
 # ----------------------------------------------------------- GPU legs
@@ -195,11 +364,12 @@ def bench_decode(args, pk, step):
     for i in range(args.warmup):
         one_step(i)
     ms_step = time_region(one_step, args.steps, stream)
-    ms_decode = time_region(lambda i: dss[i % 2].decode(0), args.steps, stream)
+    stats_step = time_each(one_step, args.steps, stream)
+    ms_decode, stats_decode = timed(lambda i: dss[i % 2].decode(0), args.steps, stream)
     nbytes = decode_bytes(step)
     tokens = int(step.decode_context_lens.sum())
     return dss, {"ms_step": ms_step, "ms_decode": ms_decode, "bytes": nbytes,
-                       "tokens": tokens}
+                 "tokens": tokens, "stats_step": stats_step, "stats_decode": stats_decode}
 
 
 def bench_mixed(args, pk, C):
@@ -209,9 +379,9 @@ def bench_mixed(args, pk, C):
     for _ in range(max(2, args.warmup)):
         ds.run()
     iters = max(5, args.steps // 2)
-    ms_step = time_region(lambda i: ds.run(), iters, stream)
-    ms_prefill = time_region(lambda i: ds.prefill(0), iters, stream)
-    ms_decode = time_region(lambda i: ds.decode(0), iters, stream)
+    ms_step, st_step = timed(lambda i: ds.run(), iters, stream)
+    ms_prefill, st_prefill = timed(lambda i: ds.prefill(0), iters, stream)
+    ms_decode, st_decode = timed(lambda i: ds.decode(0), iters, stream)
     # the same step with one unified attention launch for all requests
     for _ in range(2):
         ds.run_varlen()
@@ -222,12 +392,12 @@ def bench_mixed(args, pk, C):
     return {"workload": "mixed unified step: 64 x 100-token chunks on a 125-block "
                         "shared prefix + 1,022-token first chunk + 192 decodes "
                         "(1024..8192) + 64 copy-on-write copies, 32q/8kv, d128, bf16",
-            "ms_per_step": round(ms_step, 4),
-            "prefill_ms": round(ms_prefill, 4),
+            "ms_per_step": round(ms_step, 4), "step_stats": st_step,
+            "prefill_ms": round(ms_prefill, 4), "prefill_stats": st_prefill,
             "prefill_tflops": round(tflops, 2),
             "prefill_mfma_frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
             "prefill_pairs": pairs,
-            "decode_ms": round(ms_decode, 4),
+            "decode_ms": round(ms_decode, 4), "decode_stats": st_decode,
             "decode_gbs": round(decode_bytes(s) / (ms_decode * 1e-3) / 1e9, 1),
             "unified": unified_roofline(ms_varlen, ms_prefill + ms_decode, ms_step_varlen,
                                         flops, decode_bytes(s))}
@@ -394,10 +564,10 @@ def bench_extra_decode(args, pk, C, which):
     for i in range(2):
         run(i)
     iters = max(3, min(args.steps, 10))
-    ms = time_region(run, iters, stream)
+    ms, stats = timed(run, iters, stream)
     nbytes = decode_bytes(s) * len(layers)
     tokens = int(s.decode_context_lens.sum()) * len(layers)
-    return {"workload": name, "ms_per_step": round(ms, 4),
+    return {"workload": name, "ms_per_step": round(ms, 4), "step_stats": stats,
             "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
             "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "kv_tokens_per_s": round(tokens / (ms * 1e-3), 1),
@@ -423,13 +593,14 @@ def bench_window(args, pk, ds, step, window=1024):
 
     for i in range(args.warmup):
         run(i)
-    ms = time_region(run, args.steps, stream)
+    ms, stats = timed(run, args.steps, stream)
     seen = np.minimum(lens.astype(np.int64), window)
     nbytes = (int(seen.sum()) * 2 * step.num_kv_heads * step.head_dim * 2
               + 2 * len(lens) * step.num_q_heads * step.head_dim * 2)
     return {"workload": f"Llama-3.1-8B-shaped decode batch with a {window}-token sliding "
                         "window (64 sequences, context 512..4096, 32/8 heads, d128, bf16)",
-            "window": window, "ms_per_call": round(ms, 4), "algorithmic_bytes": nbytes,
+            "window": window, "ms_per_call": round(ms, 4), "call_stats": stats,
+            "algorithmic_bytes": nbytes,
             "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
             "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
@@ -463,13 +634,13 @@ def bench_int4(args, pk, step, copies=3):
 
     for i in range(args.warmup):
         run(i)
-    ms = time_region(run, args.steps, stream)
+    ms, stats = timed(run, args.steps, stream)
     tokens = int(lens.sum())
     nbytes = tokens * hkv * 2 * (d // 2 + 4) + 2 * len(lens) * hq * d * 2
     return {"workload": "Llama-3.1-8B-shaped decode layer over an int4 per token-head "
                         "cache: 64 sequences, context 512..4096, 32 q / 8 kv heads, d128, "
                         "bf16 q",
-            "ms_per_call": round(ms, 4), "algorithmic_bytes": nbytes,
+            "ms_per_call": round(ms, 4), "call_stats": stats, "algorithmic_bytes": nbytes,
             "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
             "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "kv_tokens_per_s": round(tokens / (ms * 1e-3), 1)}
@@ -505,13 +676,13 @@ def bench_nvfp4(args, pk, step, copies=3):
 
     for i in range(args.warmup):
         run(i)
-    ms = time_region(run, args.steps, stream)
+    ms, stats = timed(run, args.steps, stream)
     tokens = int(lens.sum())
     nbytes = tokens * hkv * 2 * (d // 2 + d // 16) + 2 * len(lens) * hq * d * 2
     return {"workload": "Llama-3.1-8B-shaped decode layer over an nvfp4-style cache (E2M1, "
                         "E4M3 scale per 16 elements): 64 sequences, context 512..4096, "
                         "32 q / 8 kv heads, d128, bf16 q",
-            "ms_per_call": round(ms, 4), "algorithmic_bytes": nbytes,
+            "ms_per_call": round(ms, 4), "call_stats": stats, "algorithmic_bytes": nbytes,
             "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
             "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "kv_tokens_per_s": round(tokens / (ms * 1e-3), 1)}
@@ -593,6 +764,9 @@ def main():
     # is touched (its worker processes are forked from this one).
     step = C.config2(device="cpu")
     cpu = None if args.no_cpu_baseline else cpu_baseline(step)
+    if cpu is not None:
+        cpu["other_workloads"] = cpu_extra_baselines(cpu["cores"])
+        cpu["host"] = host_info()
     torch.cuda.set_device(0)
     pk.library()
 
@@ -625,11 +799,20 @@ def main():
                        64, 32, 8, int(step.decode_context_lens.max()))},
         "pct_of_hbm_peak": round(100 * gbs_step / HBM_PEAK_GBS, 2),
         "kv_tokens_per_s": round(r["tokens"] / (r["ms_step"] * 1e-3), 1),
-        "roofline": {"bound": "hbm", "kernel": "paged_attention_decode (chunks + merge)",
-                     "achieved": round(gbs_decode, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs_decode / HBM_PEAK_GBS, 4), "traffic": None,
-                     "launch_ms": round(r["ms_decode"], 4)},
+        "step_stats": r["stats_step"],
+        "roofline": {"bound": "hbm",
+                     "kernel": "the step's call, paged_attention_decode_append (chunk kernel "
+                               "with the new rows' writes + merge kernel)",
+                     "achieved": round(gbs_step, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs_step / HBM_PEAK_GBS, 4), "traffic": None,
+                     "launch_ms": round(r["ms_step"], 4),
+                     "plain_decode_call": {"ms": round(r["ms_decode"], 4),
+                                           "gbs": round(gbs_decode, 1),
+                                           "frac": round(gbs_decode / HBM_PEAK_GBS, 4),
+                                           "stats": r["stats_decode"]}},
     }
+    line["gpu_clock"] = gpu_clock_under_load(lambda: [dss[i % 2].decode_append(0)
+                                                      for i in range(20)])
     tr = measured_traffic()
     if tr is not None:
         line["roofline"]["traffic"] = tr["bytes_per_call"]

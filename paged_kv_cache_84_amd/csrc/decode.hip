@@ -747,8 +747,11 @@ constexpr int kInt4WavesPerSimd = PKV_INT4_WAVES_PER_SIMD;
 #define PKV_NVFP4_WAVES_PER_SIMD 4
 #endif
 constexpr int kNvfp4WavesPerSimd = PKV_NVFP4_WAVES_PER_SIMD;
-// paged_attention_decode_workspace_size sizes for the finest split
-static_assert(kNvfp4WavesPerSimd <= kInt4WavesPerSimd, "workspace sized by the int4 plan");
+// paged_attention_decode_workspace_size sizes for the finest split any
+// cache type asks for
+constexpr int kSplitWavesMax = 4;
+static_assert(kNvfp4WavesPerSimd <= kSplitWavesMax && kInt4WavesPerSimd <= kSplitWavesMax,
+              "workspace sized by the finest split");
 static bool make_plan(int32_t s, int32_t hq, int32_t hkv, int32_t d, int32_t max_len,
                       int32_t partition_tokens, DecodePlan& p, int waves_per_simd = 1) {
   if (s < 0 || hq <= 0 || hkv <= 0 || d <= 0 || max_len < 0 || hq % hkv != 0) return false;
@@ -781,15 +784,19 @@ static bool make_plan(int32_t s, int32_t hq, int32_t hkv, int32_t d, int32_t max
 #ifndef PKV_FP8_PAIR_WAVES_PER_SIMD
 #define PKV_FP8_PAIR_WAVES_PER_SIMD 2
 #endif
+#ifndef PKV_BF16_WAVES_PER_SIMD
+#define PKV_BF16_WAVES_PER_SIMD 1
+#endif
 static int split_waves_per_simd(pkv_dtype kv_dtype, int group, int num_kv_heads) {
 #if PKV_DECODE_USE_MFMA
   if (decode_mfma_heads_per_wave(kv_dtype, group, num_kv_heads) == 2)
     return 2 * PKV_FP8_PAIR_WAVES_PER_SIMD;
+  if (kv_dtype == PKV_BF16) return PKV_BF16_WAVES_PER_SIMD;
 #endif
   return 1;
 }
-static_assert(2 * PKV_FP8_PAIR_WAVES_PER_SIMD <= kInt4WavesPerSimd,
-              "workspace sized by the int4 plan");
+static_assert(2 * PKV_FP8_PAIR_WAVES_PER_SIMD <= kSplitWavesMax,
+              "workspace sized by the finest split");
 
 template <typename QT, int D>
 static pkv_status launch_merge(void* out, const int32_t* lens, int32_t s, int32_t max_len,
@@ -965,11 +972,11 @@ extern "C" size_t paged_attention_decode_workspace_size(int32_t num_seqs,
                                                         int32_t head_dim,
                                                         int32_t max_context_len,
                                                         int32_t partition_tokens) {
-  // large enough for every cache dtype's plan (int4 splits finer)
+  // large enough for every cache dtype's plan
   DecodePlan p;
   if (partition_tokens < 0 || partition_tokens % kBlock != 0 ||
       !make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
-                 partition_tokens, p, kInt4WavesPerSimd))
+                 partition_tokens, p, kSplitWavesMax))
     return 0;
   return p.out_bytes + p.ml_bytes;
 }

@@ -278,6 +278,25 @@ PKV_DEVICE void stage_v(VRegs<KVT, D>& r, char* vl, int lane, int rows) {
 
 }  // namespace
 
+// K/V blocks a wave keeps in flight ahead of the one it multiplies (1 or 2),
+// per cache type; each adds one register set of the block's pieces.  Two
+// measured slower for every cache type on the 8B and 70B batches (the
+// per-CU address and L1 path, not the loads in flight, bounds these
+// kernels; the second set also costs occupancy).
+#ifndef PKV_DEPTH_BF16
+#define PKV_DEPTH_BF16 1
+#endif
+#ifndef PKV_DEPTH_FP8
+#define PKV_DEPTH_FP8 1
+#endif
+#ifndef PKV_DEPTH_4BIT
+#define PKV_DEPTH_4BIT 1
+#endif
+template <typename KVT>
+constexpr int prefetch_depth() {
+  return kPacked4<KVT> ? PKV_DEPTH_4BIT : KVT::bytes == 2 ? PKV_DEPTH_BF16 : PKV_DEPTH_FP8;
+}
+
 // Where a block-range cursor stands: sequence s holds the n blocks
 // [before, before + n) of the flattened batch.
 struct SeqCursor {
@@ -447,27 +466,47 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
   };
   float kcorr = 0.f;
   if constexpr (kInt4<KVT>) kcorr = offset_share();
-  int32_t id_cur = table_id(cc, b0);
-  int32_t id_next = -1;
-  if (b0 + 1 < b1) {
-    cursor_to(ic, b0 + 1, sc, context_lens, max_len, window);
-    id_next = table_id(ic, b0 + 1);
+  // Block ids: ids[k] is the id of block x + k for k = 0 .. kDepth (those
+  // of the blocks in flight and of the next to request); the id of block
+  // x + kDepth + 1 is requested once ids[kDepth] has been used.
+  constexpr int kDepth = prefetch_depth<KVT>();
+  int32_t ids[kDepth + 1];
+  ids[0] = table_id(cc, b0);
+#pragma unroll
+  for (int k = 1; k <= kDepth; ++k) {
+    ids[k] = -1;
+    if (b0 + k < b1) {
+      cursor_to(ic, b0 + k, sc, context_lens, max_len, window);
+      ids[k] = table_id(ic, b0 + k);
+    }
   }
-  const int32_t b_any = valid(id_cur) ? id_cur : 0;   // a block to re-read
-  KRegs<KVT, D> kr[NH];
-  VRegs<KVT, D> vr[NH];
-  // V before K, the order of the loop's own loads, so that each wait inside
-  // the loop covers exactly the pieces it needs
+  const int32_t b_any = valid(ids[0]) ? ids[0] : 0;   // a block to re-read
+  // kDepth register sets: set k holds the K/V of the blocks b0 + k,
+  // b0 + k + kDepth, ... (past b1 or for an unusable id, a re-read of b_any)
+  KRegs<KVT, D> kr[kDepth][NH];
+  VRegs<KVT, D> vr[kDepth][NH];
+  auto load_block_v = [&](VRegs<KVT, D> (&r)[NH], int32_t b) {
 #pragma unroll
-  for (int e = 0; e < NH; ++e) load_v<KVT, D>(vr[e], tile(v_cache, b_any, e), lane);
-  if constexpr (kInt4<KVT>) vr[0].sc = load_scales(scale_row(v_scales, b_any), lane);
-  if constexpr (kNvfp4<KVT>) vr[0].sc[0] = load_bscales(bscale_tile(v_scales, b_any), v_bscale_offset(lane));
-  __builtin_amdgcn_sched_barrier(0);
+    for (int e = 0; e < NH; ++e) load_v<KVT, D>(r[e], tile(v_cache, b, e), lane);
+    if constexpr (kInt4<KVT>) r[0].sc = load_scales(scale_row(v_scales, b), lane);
+    if constexpr (kNvfp4<KVT>) r[0].sc[0] = load_bscales(bscale_tile(v_scales, b), v_bscale_offset(lane));
+  };
+  auto load_block_k = [&](KRegs<KVT, D> (&r)[NH], int32_t b) {
 #pragma unroll
-  for (int e = 0; e < NH; ++e) load_k<KVT, D>(kr[e], tile(k_cache, b_any, e), lane);
-  if constexpr (kInt4<KVT>) kr[0].sc = load_scales(scale_row(k_scales, b_any), lane);
-  if constexpr (kNvfp4<KVT>) kr[0].sc[0] = load_bscales(bscale_tile(k_scales, b_any), k_bscale_offset(lane));
-  __builtin_amdgcn_sched_barrier(0);
+    for (int e = 0; e < NH; ++e) load_k<KVT, D>(r[e], tile(k_cache, b, e), lane);
+    if constexpr (kInt4<KVT>) r[0].sc = load_scales(scale_row(k_scales, b), lane);
+    if constexpr (kNvfp4<KVT>) r[0].sc[0] = load_bscales(bscale_tile(k_scales, b), k_bscale_offset(lane));
+  };
+  // V before K, block by block, the order of the loop's own loads, so that
+  // each wait inside the loop covers exactly the pieces it needs
+#pragma unroll
+  for (int k = 0; k < kDepth; ++k) {
+    const int32_t b = (k == 0 || (b0 + k < b1 && valid(ids[k]))) ? (k == 0 ? b_any : ids[k]) : b_any;
+    load_block_v(vr[k], b);
+    __builtin_amdgcn_sched_barrier(0);
+    load_block_k(kr[k], b);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 
   // O^T per head of the wave (a column keeps the one of its own head)
   f32x4_t acc[NH][M::kMTiles];
@@ -483,22 +522,23 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
   int chunk = b0 / c;                 // chunk of the current segment
   int chunk_end = b0 + c;             // its end
 
-  for (int x = b0; x < b1; ++x) {
+  // One block: x, whose K/V sit in register set P (x - b0 = P mod kDepth).
+  auto step = [&](auto set, int x) {
+    constexpr int P = decltype(set)::value;
+
     const int i = x - cc.before + cc.first;            // block of sequence cc.s
-    const int rows = valid(id_cur) ? min(kBlock, cc.len - i * kBlock) : 0;
+    const int rows = valid(ids[0]) ? min(kBlock, cc.len - i * kBlock) : 0;
     // sliding window: keys before `first_key` (in this block) are out of sight
     const int first_key = window > 0 ? cc.len - window - i * kBlock : 0;
-    // the next block (possibly of the next sequence), or a re-read past b1
     const bool more = x + 1 < b1;
-    const int32_t bn = (more && valid(id_next)) ? id_next : b_any;
+    // the block kDepth ahead (possibly of a later sequence), into the set
+    // this block frees, or a re-read past b1
+    const int32_t bn = (x + kDepth < b1 && valid(ids[kDepth])) ? ids[kDepth] : b_any;
 #pragma unroll
-    for (int e = 0; e < NH; ++e) stage_v<KVT, D>(vr[e], vl_all[e], lane, rows);
-    const u32x4 vsc = vr[0].sc;       // int4: this block's V scales (before the reload)
+    for (int e = 0; e < NH; ++e) stage_v<KVT, D>(vr[P][e], vl_all[e], lane, rows);
+    const u32x4 vsc = vr[P][0].sc;    // int4: this block's V scales (before the reload)
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int e = 0; e < NH; ++e) load_v<KVT, D>(vr[e], tile(v_cache, bn, e), lane);
-    if constexpr (kInt4<KVT>) vr[0].sc = load_scales(scale_row(v_scales, bn), lane);
-    if constexpr (kNvfp4<KVT>) vr[0].sc[0] = load_bscales(bscale_tile(v_scales, bn), v_bscale_offset(lane));
+    load_block_v(vr[P], bn);
     __builtin_amdgcn_sched_barrier(0);
     // Q of a sequence entered by the next block
     const bool new_seq = more && x + 1 >= lc.before + lc.n;
@@ -506,30 +546,27 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
       cursor_to(lc, x + 1, sc, context_lens, max_len, window);
       load_q(lc.s, qn);
     }
-    // the id two blocks ahead, requested only once bn has been consumed:
-    // waiting for one scalar load waits for all of them
+    // the id kDepth + 1 blocks ahead, requested only once bn has been
+    // consumed: waiting for one scalar load waits for all of them
     int32_t id_new = -1;
-    if (x + 2 < b1) {
-      cursor_to(ic, x + 2, sc, context_lens, max_len, window);
-      id_new = table_id(ic, x + 2);
+    if (x + kDepth + 1 < b1) {
+      cursor_to(ic, x + kDepth + 1, sc, context_lens, max_len, window);
+      id_new = table_id(ic, x + kDepth + 1);
     }
     // S^T = K . Q^T, per head of the wave; a column keeps its own head's
     f32x4_t st = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < M::kKSteps; ++ks) st = mfma_k32(k_operand<KVT, D>(kr[0], ks), qb[ks], st);
+    for (int ks = 0; ks < M::kKSteps; ++ks) st = mfma_k32(k_operand<KVT, D>(kr[P][0], ks), qb[ks], st);
     if constexpr (NH == 2) {
       f32x4_t st1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < M::kKSteps; ++ks)
-        st1 = mfma_k32(k_operand<KVT, D>(kr[1], ks), qb[ks], st1);
+        st1 = mfma_k32(k_operand<KVT, D>(kr[P][NH - 1], ks), qb[ks], st1);
 #pragma unroll
       for (int r = 0; r < 4; ++r) st[r] = half ? st1[r] : st[r];
     }
-    const u32x4 ksc = kr[0].sc;       // int4: this block's K scales (before the reload)
-#pragma unroll
-    for (int e = 0; e < NH; ++e) load_k<KVT, D>(kr[e], tile(k_cache, bn, e), lane);
-    if constexpr (kInt4<KVT>) kr[0].sc = load_scales(scale_row(k_scales, bn), lane);
-    if constexpr (kNvfp4<KVT>) kr[0].sc[0] = load_bscales(bscale_tile(k_scales, bn), k_bscale_offset(lane));
+    const u32x4 ksc = kr[P][0].sc;    // int4: this block's K scales (before the reload)
+    load_block_k(kr[P], bn);
     // online softmax over this lane's 4 keys of its head
     float sv[4];
     bool raise = false;
@@ -591,8 +628,9 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
         acc[e][mt] = mfma_k16(a, phi, acc[e][mt]);
         acc[e][mt] = mfma_k16(a, plo, acc[e][mt]);
       }
-    id_cur = id_next;
-    id_next = id_new;
+#pragma unroll
+    for (int k = 0; k < kDepth; ++k) ids[k] = ids[k + 1];
+    ids[kDepth] = id_new;
 
     // A segment ends with its sequence, at a chunk boundary, or at b1.
     const int seq_end = cc.before + cc.n;
@@ -652,6 +690,13 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
         for (int ks = 0; ks < M::kKSteps; ++ks) qb[ks] = qn[ks];
         if constexpr (kInt4<KVT>) kcorr = offset_share();
       }
+    }
+  };
+  for (int x = b0; x < b1; x += kDepth) {
+    step(std::integral_constant<int, 0>{}, x);
+    if constexpr (kDepth == 2) {
+      if (x + 1 >= b1) break;
+      step(std::integral_constant<int, kDepth - 1>{}, x + 1);
     }
   }
 }
