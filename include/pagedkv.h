@@ -80,7 +80,8 @@ const char* pkv_status_string(pkv_status status);
 /* Bytes of KV cache one token occupies over a whole model:
  * 2 (key and value) x bytes_per_elem x num_layers x num_kv_heads x head_dim
  * ("vLLM 引擎解剖", section "KV 缓存需要多少内存？", the formula of Table 1).
- * Returns -1 if any argument is negative. Host-only, no GPU work. */
+ * Returns -1 if any argument is negative or the product does not fit in
+ * int64. Host-only, no GPU work. */
 int64_t kv_bytes_per_token(int32_t num_layers, int32_t num_kv_heads,
                            int32_t head_dim, int32_t bytes_per_elem);
 

@@ -24,5 +24,8 @@ extern "C" int64_t kv_bytes_per_token(int32_t num_layers, int32_t num_kv_heads,
                                       int32_t head_dim, int32_t bytes_per_elem) {
   if (num_layers < 0 || num_kv_heads < 0 || head_dim < 0 || bytes_per_elem < 0)
     return -1;
-  return int64_t(2) * bytes_per_elem * num_layers * num_kv_heads * head_dim;
+  int64_t r = 2;
+  for (const int32_t f : {bytes_per_elem, num_layers, num_kv_heads, head_dim})
+    if (__builtin_mul_overflow(r, int64_t(f), &r)) return -1;
+  return r;
 }

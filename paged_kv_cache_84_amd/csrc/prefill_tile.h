@@ -282,12 +282,15 @@ PKV_DEVICE void prefill_tile_at(
       raise |= lmax[qb] > m[qb] + kRaise;
     }
     if (__builtin_expect(__ballot(raise) != 0, 0)) {
+      // only the rows that need it are raised: a row's arithmetic then never
+      // depends on the other rows of its wave, so the rows come out the same
+      // however the chunks of a prompt are cut
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         float mx = lmax[qb];
         mx = fmaxf(mx, shfl_xor(mx, 16));
         mx = fmaxf(mx, shfl_xor(mx, 32));
-        const float mn = fmaxf(m[qb], mx);
+        const float mn = mx > m[qb] + kRaise ? mx : m[qb];
         const float alpha = fast_exp2(m[qb] - mn);
         l[qb] *= alpha;
 #pragma unroll

@@ -157,3 +157,31 @@ def test_step_append_fullsize(name):
         assert torch.equal(ra[layer].view(torch.int16), rb[layer].view(torch.int16))
     del a, b, ra, rb, s
     torch.cuda.empty_cache()
+
+
+def test_append_fp8_special_rows():
+    """The fused call's own fp8 encoding of the new rows: NaN, +-inf, -0,
+    values that saturate at 448 (449, 464, 465, 1e6), values at and between
+    the smallest subnormals, and ties, give the same cache bytes as
+    reshape_and_cache (whose encoder the oracle pins bit for bit); outputs
+    of sequences whose new rows are finite match the write-then-decode path
+    bitwise."""
+    announce("decode append fp8 specials")
+    lengths = [17, 40, 5, 33, 64, 1]
+    hq, hkv, d = 16, 2, 128
+    q, nk, nv, kc, vc, ks, vs, tables, lens, slots = _batch(lengths, hq, hkv, F.FP8_E4M3,
+                                                            seed=77, d=d)
+    specials = torch.tensor([float("nan"), float("inf"), -float("inf"), -0.0, 0.0, 448.0,
+                             449.0, 464.0, 465.0, -1e6, 2.0 ** -9, 2.0 ** -10, 1.5 * 2.0 ** -9,
+                             0.5 * 2.0 ** -9 * 3, 2.0 ** -6, 1.0625, 1.1875, -240.0])
+    n = specials.numel()
+    # sequences 0 and 1 carry the specials (scaled back by the cache scales so
+    # that x / scale lands on them); the others stay finite
+    nk[0, 0, :n] = (specials * ks).to(torch.bfloat16)
+    nv[1, 1, :n] = (specials * vs).to(torch.bfloat16)
+    nk[1, 0, n:2 * n] = (specials * ks).to(torch.bfloat16)
+    ka, va, ref, kb, vb, got = _both(q, nk, nv, kc, vc, ks, vs, tables, lens, slots, 0)
+    assert torch.equal(kb.view(torch.uint8), ka.view(torch.uint8))
+    assert torch.equal(vb.view(torch.uint8), va.view(torch.uint8))
+    finite = [2, 3, 4, 5]
+    assert torch.equal(got[finite].view(torch.int16), ref[finite].view(torch.int16))
