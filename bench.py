@@ -1,8 +1,9 @@
 """Benchmark of the paged-attention hot path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
-                    [--no-mixed] [--no-longctx] [--no-mha] [--no-swap] [--no-window] [--no-int4] [--no-nvfp4]
-                    [--no-blocks] [--no-ceilings]
+    python bench.py [--steps K] [--warmup W] [--settle-ms MS] [--gpus 1]
+                    [--no-cpu-baseline] [--no-mixed] [--no-longctx] [--no-mha]
+                    [--no-swap] [--no-window] [--no-int4] [--no-nvfp4]
+                    [--no-blocks] [--no-ceilings] [--no-clock] [--plain-decode]
     python bench.py --copy-calibration     (a plain 1 GiB device copy, for
                                             the HBM byte counters' scale)
 
@@ -12,19 +13,23 @@ decode layer (64 sequences, context 512..4096, 32 q / 8 kv heads, head_dim
 writes and paged decode attention, all in the one decode launch
 (paged_attention_decode_append: balanced chunks + merge).  Inputs are resident
 in HBM before timing starts; two copies of the KV pool alternate between
-steps so that the 256 MB last-level cache cannot serve a re-read.
+steps so that the 256 MB last-level cache cannot serve a re-read.  Each leg
+first runs untimed for --settle-ms (the clock ramps up from idle), then its
+warm-up steps, then the timed ones.
 
 Prints one JSON line (rank 0): whole-step throughput in algorithmic KV GB/s,
 KV tokens/s, the decode call's roofline fraction, the oracle's CPU rate on a
 bounded sample, the mixed unified step with chunked prefill (MFMA
 utilisation of the prefill call), the fp8 long-context decode, the
 32-layer MHA decode step, the 8B batch with a sliding window and over an
-int4 per token-head cache and over an nvfp4-style cache,
-a device <-> host block swap of one long sequence, measured ceilings (a streaming HBM read
-with the decode's loads, a register-only bf16 MFMA loop) that the decode and prefill rates are
-also read against, and the host block manager's operations per second on a serving
-trace (with the oracle's rate on a bounded sample beside it).  The roofline's "traffic" is the HBM bytes per
-decode call that rocprofv3's FETCH_SIZE and WRITE_SIZE counters measured
+int4 per token-head cache and over an nvfp4-style cache, a device <-> host
+block swap of one long sequence, measured ceilings (a streaming HBM read
+with the decode's loads, a register-only bf16 MFMA loop, and that loop with
+softmax-like vector work from the same waves) that the decode and prefill
+rates are also read against, and the host block manager's operations per
+second on a serving trace (with the oracle's rate on a bounded sample
+beside it).  The roofline's "traffic" is the HBM bytes per step call that
+rocprofv3's FETCH_SIZE and WRITE_SIZE counters measured
 (profiles/decode_llama3_8b_64seq_traffic.md), used only while the decode
 sources are the ones those counters were taken on.
 """
@@ -114,6 +119,21 @@ def copy_calibration(nbytes=1 << 30, reps=5):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
+
+
+def settle(run, ms):
+    """Untimed calls of `run` for about `ms` of wall time (at least one), so
+    that every leg is timed at the clock the GPU holds under steady load
+    rather than while it ramps up from idle."""
+    t0 = time.perf_counter()
+    i = 0
+    while True:
+        run(i)
+        i += 1
+        if i % 4 == 0 or ms <= 0:
+            torch.cuda.synchronize()
+            if (time.perf_counter() - t0) * 1e3 >= ms:
+                return i
 
 
 def time_region(fn, iters, stream):
@@ -359,12 +379,17 @@ def bench_decode(args, pk, step):
 
     def one_step(i):
         # the 64 new tokens' slots and cache writes, then the decode: one launch
-        dss[i % 2].decode_append(0)
+        if args.plain_decode:
+            dss[i % 2].decode(0)
+        else:
+            dss[i % 2].decode_append(0)
 
+    settle(one_step, args.settle_ms)
     for i in range(args.warmup):
         one_step(i)
     ms_step = time_region(one_step, args.steps, stream)
     stats_step = time_each(one_step, args.steps, stream)
+    settle(lambda i: dss[i % 2].decode(0), args.settle_ms)
     ms_decode, stats_decode = timed(lambda i: dss[i % 2].decode(0), args.steps, stream)
     nbytes = decode_bytes(step)
     tokens = int(step.decode_context_lens.sum())
@@ -376,13 +401,17 @@ def bench_mixed(args, pk, C):
     s = C.config4(device="cuda")
     ds = pk.step.DeviceStep(s)
     stream = torch.cuda.current_stream()
+    settle(lambda i: ds.run(), args.settle_ms)
     for _ in range(max(2, args.warmup)):
         ds.run()
     iters = max(5, args.steps // 2)
     ms_step, st_step = timed(lambda i: ds.run(), iters, stream)
+    settle(lambda i: ds.prefill(0), args.settle_ms)
     ms_prefill, st_prefill = timed(lambda i: ds.prefill(0), iters, stream)
+    settle(lambda i: ds.decode(0), args.settle_ms)
     ms_decode, st_decode = timed(lambda i: ds.decode(0), iters, stream)
     # the same step with one unified attention launch for all requests
+    settle(lambda i: ds.run_varlen(), args.settle_ms)
     for _ in range(2):
         ds.run_varlen()
     ms_step_varlen = time_region(lambda i: ds.run_varlen(), iters, stream)
@@ -561,9 +590,10 @@ def bench_extra_decode(args, pk, C, which):
         for layer in layers:
             ds.decode_append(layer)
 
+    settle(run, args.settle_ms)
     for i in range(2):
         run(i)
-    iters = max(3, min(args.steps, 10))
+    iters = max(3, min(args.steps, 10 if which == "mha" else args.steps))
     ms, stats = timed(run, iters, stream)
     nbytes = decode_bytes(s) * len(layers)
     tokens = int(s.decode_context_lens.sum()) * len(layers)
@@ -591,6 +621,7 @@ def bench_window(args, pk, ds, step, window=1024):
                                           ds.dec_lens, int(lens.max()), step.softmax_scale,
                                           window, out=out, workspace=ws)
 
+    settle(run, args.settle_ms)
     for i in range(args.warmup):
         run(i)
     ms, stats = timed(run, args.steps, stream)
@@ -632,6 +663,7 @@ def bench_int4(args, pk, step, copies=3):
         pk.paged_attention_decode_int4(q, kc, vc, ks, vs, tables, lens_d, int(lens.max()),
                                        step.softmax_scale, out=out, workspace=ws)
 
+    settle(run, args.settle_ms)
     for i in range(args.warmup):
         run(i)
     ms, stats = timed(run, args.steps, stream)
@@ -674,6 +706,7 @@ def bench_nvfp4(args, pk, step, copies=3):
         pk.paged_attention_decode_nvfp4(q, kc, vc, ks, vs, tables, lens_d, int(lens.max()),
                                         step.softmax_scale, 1.0, 1.0, out=out, workspace=ws)
 
+    settle(run, args.settle_ms)
     for i in range(args.warmup):
         run(i)
     ms, stats = timed(run, args.steps, stream)
@@ -697,9 +730,11 @@ def xor_of_range(n):
 def bench_ceilings(args, pk, read_bytes=4 << 30, mfma_waves=4096, mfma_iters=4096):
     """Measured ceilings: a streaming read of 4 GiB with the decode's
     16-byte non-temporal loads (the buffer holds the word ramp 0, 1, 2, ...,
-    whose XOR checks that every word was read), and a register-only loop of
+    whose XOR checks that every word was read), a register-only loop of
     the prefill's bf16 MFMA on 4 waves per SIMD (each wave's result checks
-    that every product was issued)."""
+    that every product was issued), and that loop with the softmax's kind
+    of vector work from the same waves, alone and together: the share of
+    the vector time the matrix cores do not hide."""
     stream = torch.cuda.current_stream()
     words = torch.arange(read_bytes // 4, dtype=torch.int32, device="cuda")
     checksum = torch.zeros(1, dtype=torch.int32, device="cuda")
@@ -713,6 +748,17 @@ def bench_ceilings(args, pk, read_bytes=4 << 30, mfma_waves=4096, mfma_iters=409
     pk.measure_mfma_bf16(mfma_iters, result)
     ms_mfma = time_region(lambda i: pk.measure_mfma_bf16(mfma_iters, result), 3, stream)
     assert bool(torch.all(result == 32.0 * mfma_iters)), "MFMA loop result mismatch"
+    pair = torch.zeros(2 * mfma_waves, dtype=torch.float32, device="cuda")
+    ms_mode = []
+    for mode in range(3):
+        pk.measure_mfma_valu(mfma_iters, mode, pair)
+        ms_mode.append(time_region(lambda i: pk.measure_mfma_valu(mfma_iters, mode, pair),
+                                   3, stream))
+        r = pair.view(-1, 2).cpu()
+        assert bool(torch.all(r[:, 0] == (0.0 if mode == 1 else 32.0 * mfma_iters))) and \
+            bool(torch.all(r[:, 1] == r[0, 1])) and (float(r[0, 1]) > 0) == (mode > 0), \
+            "MFMA + vector loop result mismatch"
+    del pair
     read_gbs = read_bytes / (ms_read * 1e-3) / 1e9
     tflops = mfma_waves * mfma_iters * 8 * 16384 / (ms_mfma * 1e-3) / 1e12
     return {"hbm_read": {"bytes": read_bytes, "ms": round(ms_read, 4),
@@ -720,7 +766,12 @@ def bench_ceilings(args, pk, read_bytes=4 << 30, mfma_waves=4096, mfma_iters=409
                          "frac_of_peak": round(read_gbs / HBM_PEAK_GBS, 4)},
             "mfma_bf16": {"waves": mfma_waves, "mfma_per_wave": mfma_iters * 8,
                           "ms": round(ms_mfma, 4), "tflops": round(tflops, 1),
-                          "frac_of_peak": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4)}}
+                          "frac_of_peak": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4)},
+            "mfma_with_vector_work": {
+                "waves": mfma_waves, "iterations": mfma_iters,
+                "ms_mfma_only": round(ms_mode[0], 4), "ms_vector_only": round(ms_mode[1], 4),
+                "ms_both": round(ms_mode[2], 4),
+                "vector_share_not_hidden": round((ms_mode[2] - ms_mode[0]) / ms_mode[1], 4)}}
 
 
 def main():
@@ -728,6 +779,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="untimed calls of each leg for this many ms before its warm-up "
+                         "steps (the GPU clock ramps up from idle)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mixed", action="store_true")
     ap.add_argument("--no-longctx", action="store_true",
@@ -742,6 +796,13 @@ def main():
                     help="skip the int4 per token-head decode of the 8B batch")
     ap.add_argument("--no-nvfp4", action="store_true",
                     help="skip the nvfp4-style decode of the 8B batch")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip sampling the shader clock with rocm-smi (e.g. under a "
+                         "profiler, whose preloaded library the rocm-smi child inherits)")
+    ap.add_argument("--plain-decode", action="store_true",
+                    help="time the plain paged_attention_decode call as the step (for "
+                         "builds whose decode kernel has no fused cache write, e.g. one "
+                         "built with -DPKV_DECODE_USE_MFMA=0)")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the measured HBM-read and MFMA ceilings")
     ap.add_argument("--no-blocks", action="store_true",
@@ -781,6 +842,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": args.settle_ms,
         "ms_per_step": round(r["ms_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -811,12 +873,18 @@ def main():
                                            "frac": round(gbs_decode / HBM_PEAK_GBS, 4),
                                            "stats": r["stats_decode"]}},
     }
-    line["gpu_clock"] = gpu_clock_under_load(lambda: [dss[i % 2].decode_append(0)
-                                                      for i in range(20)])
+    if args.plain_decode:
+        line["config"]["workload"] += "; timed as the plain paged_attention_decode call"
+        line["roofline"]["kernel"] = "paged_attention_decode (chunk kernel + merge kernel)"
+    if not args.no_clock:
+        line["gpu_clock"] = gpu_clock_under_load(
+            lambda: [(dss[i % 2].decode(0) if args.plain_decode else dss[i % 2].decode_append(0))
+                     for i in range(20)])
     tr = measured_traffic()
     if tr is not None:
-        line["roofline"]["traffic"] = tr["bytes_per_call"]
-        line["roofline"]["traffic_over_algorithmic"] = round(tr["bytes_per_call"] / r["bytes"], 3)
+        key = "bytes_per_call" if args.plain_decode else "append_call_bytes"
+        line["roofline"]["traffic"] = tr[key]
+        line["roofline"]["traffic_over_algorithmic"] = round(tr[key] / r["bytes"], 3)
     if not args.no_mixed:
         line["mixed_step"] = bench_mixed(args, pk, C)
     if not args.no_longctx:

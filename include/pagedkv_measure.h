@@ -53,6 +53,23 @@ pkv_status pkv_measure_hbm_read(const void* buf, int64_t bytes, uint32_t* checks
 pkv_status pkv_measure_mfma_bf16(int32_t iterations, int32_t waves, float* result,
                                  void* stream);
 
+/*
+ * pkv_measure_mfma_valu -- how much of the softmax's vector work the matrix
+ * cores hide: the loop of pkv_measure_mfma_bf16 (8 independent MFMAs per
+ * iteration) and, from the same waves, 8 chains of fp32 vector work per
+ * iteration (fma, integer and, sub, add; a transcendental 2^x on 3 of the 8),
+ * about the prefill tile's mix of vector instructions per MFMA.
+ *   mode  0: the MFMAs only; 1: the vector work only; 2: both, interleaved
+ *   result device float[2 * waves]: wave w writes 32 * iterations to
+ *          result[2w] when it ran the MFMAs (else 0), and its vector sum to
+ *          result[2w + 1] (the same in every wave; 0 without vector work)
+ * Time the three modes with events: (t2 - t0) / t1 is the share of the
+ * vector work the MFMAs do not hide.
+ * Errors: PKV_ERR_NULL, PKV_ERR_ALIGN, PKV_ERR_SHAPE, PKV_ERR_LAUNCH.
+ */
+pkv_status pkv_measure_mfma_valu(int32_t iterations, int32_t waves, int32_t mode,
+                                 float* result, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

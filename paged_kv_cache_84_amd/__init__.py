@@ -24,6 +24,7 @@ from ._binding import (  # noqa: F401
     library_path,
     measure_hbm_read,
     measure_mfma_bf16,
+    measure_mfma_valu,
     varlen_workspace_size,
     paged_attention_decode,
     paged_attention_decode_append,

@@ -76,6 +76,7 @@ _SIGNATURES = {
     # hardware ceilings (include/pagedkv_measure.h)
     "pkv_measure_hbm_read": (_I32, [_P, _I64, _P, _P]),
     "pkv_measure_mfma_bf16": (_I32, [_I32, _I32, _P, _P]),
+    "pkv_measure_mfma_valu": (_I32, [_I32, _I32, _I32, _P, _P]),
     # host block manager (include/pagedkv_blocks.h)
     "pkv_bm_create": (_I32, [_I32, _P, _I32, _P]),
     "pkv_bm_destroy": (None, [_P]),
@@ -488,6 +489,14 @@ def measure_mfma_bf16(iterations, result):
     st = library().pkv_measure_mfma_bf16(int(iterations), result.numel(),
                                          _dev(result, "result", torch.float32), _stream(result))
     _check("pkv_measure_mfma_bf16", st)
+
+
+def measure_mfma_valu(iterations, mode, result):
+    """MFMA loop (mode 0), the softmax-like vector work (1) or both from the
+    same waves (2) on `result.numel() // 2` waves (see the header)."""
+    st = library().pkv_measure_mfma_valu(int(iterations), result.numel() // 2, int(mode),
+                                         _dev(result, "result", torch.float32), _stream(result))
+    _check("pkv_measure_mfma_valu", st)
 
 
 def reshape_and_cache_from_schedule(key, value, k_cache, v_cache, block_tables,

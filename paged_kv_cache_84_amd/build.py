@@ -1,6 +1,6 @@
 """Compile the HIP sources into ``libpagedkv.so`` (gfx950), in-tree.
 
-    python -m paged_kv_cache_84_amd.build
+    python -m paged_kv_cache_84_amd.build [-D NAME=VALUE ...] [--lib PATH]
 
 Each ``csrc/*.hip`` file is compiled to an object in ``_build/`` (in
 parallel), then linked into ``libpagedkv.so`` next to this file.  hipcc
@@ -90,5 +90,21 @@ def build(verbose=False, extra_flags=(), lib=LIB, build_dir=BUILD):
     return lib
 
 
+def main(argv=None):
+    import argparse
+    ap = argparse.ArgumentParser(description="build libpagedkv.so for gfx950")
+    ap.add_argument("-D", "--define", action="append", default=[], metavar="NAME=VALUE",
+                    help="a preprocessor definition for every HIP source (tuning "
+                         "macros, e.g. PKV_DECODE_USE_MFMA=0)")
+    ap.add_argument("--lib", default=LIB, help="output library path")
+    ap.add_argument("--build-dir", default=None, help="object directory (default: "
+                    "_build/ for the default library, else beside --lib)")
+    a = ap.parse_args(argv)
+    lib = os.path.abspath(a.lib)
+    build_dir = a.build_dir or (BUILD if lib == LIB else os.path.join(os.path.dirname(lib),
+                                                                        "_build"))
+    build(verbose=True, extra_flags=[f"-D{d}" for d in a.define], lib=lib, build_dir=build_dir)
+
+
 if __name__ == "__main__":
-    build(verbose=True)
+    main()

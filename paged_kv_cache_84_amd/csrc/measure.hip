@@ -1,6 +1,7 @@
 // Hardware ceilings for reading the hot path's rates: a streaming HBM read
-// with the decode's 16-byte non-temporal loads, and a register-only loop of
-// the prefill's bf16 MFMA.  Each leaves a result the caller can check, so
+// with the decode's 16-byte non-temporal loads, a register-only loop of the
+// prefill's bf16 MFMA, and the same loop with the softmax's vector work
+// issued by the same waves.  Each leaves a result the caller can check, so
 // that the compiler cannot have dropped the work being timed.
 
 #include "abi_util.h"
@@ -85,6 +86,61 @@ __global__ __launch_bounds__(kMfmaWavesPerWg * kWave) void mfma_bf16_kernel(
   if (lane == 0) result[wave] = others >= 0.f ? c[0][0] : -1.f;
 }
 
+// The prefill's mix of work: bf16 MFMAs and the softmax's vector
+// instructions (fp32 fma and add, a transcendental 2^x every third step,
+// integer ops of the bf16 split), both from the same waves.  Mode 0 issues
+// only the MFMAs, 1 only the vector work, 2 both, interleaved in one loop
+// (8 MFMAs and 8 chains x (fma, and, sub, add) plus 3 exp2 per iteration:
+// 4 vector instructions per MFMA, 0.375 exp2 per MFMA, the prefill tile's
+// ratio within a factor of 1.5).  Lane 0 of each wave stores
+// result[2w] = element (0, 0) of its first accumulator (32 * iterations when
+// the MFMAs ran, else 0) and result[2w + 1] = its vector chains' sum (equal
+// in every wave, 0 when the vector work did not run).
+template <int MODE>
+__global__ __launch_bounds__(kMfmaWavesPerWg * kWave) void mfma_valu_kernel(
+    int32_t iterations, float* __restrict__ result) {
+  const int lane = lane_id();
+  constexpr bool do_m = MODE != 1, do_v = MODE != 0;
+  bf16x8_t a, b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] = (__bf16)float(lane % 16 + 1);
+    b[e] = (__bf16)1.0f;
+  }
+  f32x4_t c[kMfmaChains];
+  float x[kMfmaChains], y[kMfmaChains];
+#pragma unroll
+  for (int j = 0; j < kMfmaChains; ++j) {
+    c[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    x[j] = 0.125f * float(j);
+    y[j] = 0.f;
+  }
+  for (int r = 0; r < iterations; ++r) {
+#pragma unroll
+    for (int j = 0; j < kMfmaChains; ++j) {
+      if constexpr (do_m) c[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c[j], 0, 0, 0);
+      if constexpr (do_v) {
+        // x contracts toward 0.5 and stays in [0, 1); p = 2^(x - 1) on some
+        x[j] = __builtin_fmaf(x[j], 0.5f, 0.25f);
+        float p = x[j];
+        if (j % 3 == 0) p = __builtin_amdgcn_exp2f(x[j] - 1.0f);
+        const float hi = __uint_as_float(__float_as_uint(p) & 0xffff0000u);
+        y[j] += p - hi;
+      }
+    }
+  }
+  float others = 0.f, v = 0.f;
+#pragma unroll
+  for (int j = 1; j < kMfmaChains; ++j) others += c[j][0] + c[j][3];
+#pragma unroll
+  for (int j = 0; j < kMfmaChains; ++j) v += y[j];
+  const int wave = int(blockIdx.x) * kMfmaWavesPerWg + int(threadIdx.x) / kWave;
+  if (lane == 0) {
+    result[2 * wave] = others >= 0.f ? c[0][0] : -1.f;
+    result[2 * wave + 1] = v;
+  }
+}
+
 }  // namespace
 }  // namespace pkv
 
@@ -115,5 +171,19 @@ extern "C" pkv_status pkv_measure_mfma_bf16(int32_t iterations, int32_t waves, f
   if (!aligned(result, 4)) return PKV_ERR_ALIGN;
   hipLaunchKernelGGL(mfma_bf16_kernel, dim3(waves / kMfmaWavesPerWg),
                      dim3(kMfmaWavesPerWg * kWave), 0, as_stream(stream), iterations, result);
+  return launch_status();
+}
+
+extern "C" pkv_status pkv_measure_mfma_valu(int32_t iterations, int32_t waves, int32_t mode,
+                                            float* result, void* stream) {
+  if (iterations < 1 || iterations > 524288 || waves < kMfmaWavesPerWg ||
+      waves % kMfmaWavesPerWg != 0 || mode < 0 || mode > 2)
+    return PKV_ERR_SHAPE;
+  if (!result) return PKV_ERR_NULL;
+  if (!aligned(result, 4)) return PKV_ERR_ALIGN;
+  auto kernel = mode == 0 ? mfma_valu_kernel<0> : mode == 1 ? mfma_valu_kernel<1>
+                                                            : mfma_valu_kernel<2>;
+  hipLaunchKernelGGL(kernel, dim3(waves / kMfmaWavesPerWg), dim3(kMfmaWavesPerWg * kWave), 0,
+                     as_stream(stream), iterations, result);
   return launch_status();
 }

@@ -393,3 +393,11 @@ def test_measure_errors(lib):
     assert g(10, 0, p, None) == SHAPE
     assert g(10, 8, None, None) == NULL
     assert g(10, 8, p + 2, None) == ALIGN
+    h = lib.pkv_measure_mfma_valu
+    assert h(0, 8, 0, p, None) == SHAPE
+    assert h(524289, 8, 2, p, None) == SHAPE
+    assert h(10, 12, 1, p, None) == SHAPE
+    assert h(10, 8, 3, p, None) == SHAPE
+    assert h(10, 8, -1, p, None) == SHAPE
+    assert h(10, 8, 2, None, None) == NULL
+    assert h(10, 8, 2, p + 2, None) == ALIGN
