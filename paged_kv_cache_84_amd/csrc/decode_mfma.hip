@@ -508,12 +508,12 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // O^T per head of the wave (a column keeps the one of its own head)
-  f32x4_t acc[NH][M::kMTiles];
+  // O^T: column n of the accumulators is the output of column n's own head
+  // (with two heads per wave, each head's products see P^T with the other
+  // head's columns zeroed, so both accumulate into one set)
+  f32x4_t acc[M::kMTiles];
 #pragma unroll
-  for (int e = 0; e < NH; ++e)
-#pragma unroll
-    for (int mt = 0; mt < M::kMTiles; ++mt) acc[e][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int mt = 0; mt < M::kMTiles; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   // running max starts finite: a fully masked block then gives weights
   // 2^-inf = 0 instead of 2^(-inf + inf)
   float m = kNoMax, l = 0.f;
@@ -590,9 +590,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
       l *= alpha;
       if constexpr (kInt4<KVT>) lp *= alpha;
 #pragma unroll
-      for (int e = 0; e < NH; ++e)
-#pragma unroll
-        for (int mt = 0; mt < M::kMTiles; ++mt) acc[e][mt] *= alpha;
+      for (int mt = 0; mt < M::kMTiles; ++mt) acc[mt] *= alpha;
     }
     float p[4];
 #pragma unroll
@@ -619,15 +617,19 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
     }
     const i16x4_t phi = __builtin_bit_cast(i16x4_t, uint2{hi[0], hi[1]});
     const i16x4_t plo = __builtin_bit_cast(i16x4_t, uint2{lo[0], lo[1]});
-    // O^T += V^T . P^T
+    // O^T += V^T . P^T (head e's V against the columns of head e only)
 #pragma unroll
-    for (int e = 0; e < NH; ++e)
+    for (int e = 0; e < NH; ++e) {
+      const i16x4_t zero = {0, 0, 0, 0};
+      const i16x4_t ph = NH == 1 || half == e ? phi : zero;
+      const i16x4_t pl = NH == 1 || half == e ? plo : zero;
 #pragma unroll
       for (int mt = 0; mt < M::kMTiles; ++mt) {
         const i16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(vt_base(e) + mt * 4);
-        acc[e][mt] = mfma_k16(a, phi, acc[e][mt]);
-        acc[e][mt] = mfma_k16(a, plo, acc[e][mt]);
+        acc[mt] = mfma_k16(a, ph, acc[mt]);
+        acc[mt] = mfma_k16(a, pl, acc[mt]);
       }
+    }
 #pragma unroll
     for (int k = 0; k < kDepth; ++k) ids[k] = ids[k + 1];
     ids[kDepth] = id_new;
@@ -643,14 +645,9 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
         float lpt = lp + shfl_xor(lp, 16);
         lpt += shfl_xor(lpt, 32);
 #pragma unroll
-        for (int mt = 0; mt < M::kMTiles; ++mt) acc[0][mt] -= kInt4Offset * lpt;
+        for (int mt = 0; mt < M::kMTiles; ++mt) acc[mt] -= kInt4Offset * lpt;
       }
-      // this lane's column: its own head's products
-      f32x4_t o[M::kMTiles];
-#pragma unroll
-      for (int mt = 0; mt < M::kMTiles; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) o[mt][r] = (NH == 2 && half) ? acc[NH - 1][mt][r] : acc[0][mt][r];
+      const f32x4_t (&o)[M::kMTiles] = acc;
       if (head_ok) {
         if (seg_start == cc.before && x + 1 == seq_end) {
           const float f = v_scale / lt;
@@ -673,9 +670,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
         }
       }
 #pragma unroll
-      for (int e = 0; e < NH; ++e)
-#pragma unroll
-        for (int mt = 0; mt < M::kMTiles; ++mt) acc[e][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int mt = 0; mt < M::kMTiles; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       m = kNoMax;
       l = 0.f;
       lp = 0.f;
