@@ -56,9 +56,9 @@ pkv_status pkv_measure_mfma_bf16(int32_t iterations, int32_t waves, float* resul
 /*
  * pkv_measure_mfma_valu -- how much of the softmax's vector work the matrix
  * cores hide: the loop of pkv_measure_mfma_bf16 (8 independent MFMAs per
- * iteration) and, from the same waves, 8 chains of fp32 vector work per
- * iteration (fma, integer and, sub, add; a transcendental 2^x on 3 of the 8),
- * about the prefill tile's mix of vector instructions per MFMA.
+ * iteration) and, from the same waves, 5 chains of fp32 vector work per
+ * iteration (fma, integer and, sub, add; a transcendental 2^x on 2 of the 5):
+ * 3 vector instructions and 0.25 exp2 per MFMA, near the prefill tile's mix.
  *   mode  0: the MFMAs only; 1: the vector work only; 2: both, interleaved
  *   result device float[2 * waves]: wave w writes 32 * iterations to
  *          result[2w] when it ran the MFMAs (else 0), and its vector sum to

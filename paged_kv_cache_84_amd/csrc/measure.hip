@@ -60,6 +60,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kMfmaWavesPerWg = 8;
 constexpr int kMfmaChains = 8;          // independent accumulators per wave
+constexpr int kVecChains = 5;           // vector chains beside them
 
 __global__ __launch_bounds__(kMfmaWavesPerWg * kWave) void mfma_bf16_kernel(
     int32_t iterations, float* __restrict__ result) {
@@ -87,12 +88,12 @@ __global__ __launch_bounds__(kMfmaWavesPerWg * kWave) void mfma_bf16_kernel(
 }
 
 // The prefill's mix of work: bf16 MFMAs and the softmax's vector
-// instructions (fp32 fma and add, a transcendental 2^x every third step,
-// integer ops of the bf16 split), both from the same waves.  Mode 0 issues
-// only the MFMAs, 1 only the vector work, 2 both, interleaved in one loop
-// (8 MFMAs and 8 chains x (fma, and, sub, add) plus 3 exp2 per iteration:
-// 4 vector instructions per MFMA, 0.375 exp2 per MFMA, the prefill tile's
-// ratio within a factor of 1.5).  Lane 0 of each wave stores
+// instructions (fp32 fma and add, a transcendental 2^x, integer ops of the
+// bf16 split), both from the same waves.  Mode 0 issues only the MFMAs, 1
+// only the vector work, 2 both, interleaved in one loop: per iteration 8
+// MFMAs and 5 chains x (fma, and, sub, add) plus 2 x (sub, exp2), i.e. 3
+// vector instructions and 0.25 exp2 per MFMA (the prefill tile issues 2.8
+// and 0.33).  Lane 0 of each wave stores
 // result[2w] = element (0, 0) of its first accumulator (32 * iterations when
 // the MFMAs ran, else 0) and result[2w + 1] = its vector chains' sum (equal
 // in every wave, 0 when the vector work did not run).
@@ -108,10 +109,11 @@ __global__ __launch_bounds__(kMfmaWavesPerWg * kWave) void mfma_valu_kernel(
     b[e] = (__bf16)1.0f;
   }
   f32x4_t c[kMfmaChains];
-  float x[kMfmaChains], y[kMfmaChains];
+  float x[kVecChains], y[kVecChains];
 #pragma unroll
-  for (int j = 0; j < kMfmaChains; ++j) {
-    c[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < kMfmaChains; ++j) c[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < kVecChains; ++j) {
     x[j] = 0.125f * float(j);
     y[j] = 0.f;
   }
@@ -119,7 +121,7 @@ __global__ __launch_bounds__(kMfmaWavesPerWg * kWave) void mfma_valu_kernel(
 #pragma unroll
     for (int j = 0; j < kMfmaChains; ++j) {
       if constexpr (do_m) c[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c[j], 0, 0, 0);
-      if constexpr (do_v) {
+      if constexpr (do_v) if (j < kVecChains) {
         // x contracts toward 0.5 and stays in [0, 1); p = 2^(x - 1) on some
         x[j] = __builtin_fmaf(x[j], 0.5f, 0.25f);
         float p = x[j];
@@ -133,7 +135,7 @@ __global__ __launch_bounds__(kMfmaWavesPerWg * kWave) void mfma_valu_kernel(
 #pragma unroll
   for (int j = 1; j < kMfmaChains; ++j) others += c[j][0] + c[j][3];
 #pragma unroll
-  for (int j = 0; j < kMfmaChains; ++j) v += y[j];
+  for (int j = 0; j < kVecChains; ++j) v += y[j];
   const int wave = int(blockIdx.x) * kMfmaWavesPerWg + int(threadIdx.x) / kWave;
   if (lane == 0) {
     result[2 * wave] = others >= 0.f ? c[0][0] : -1.f;
