@@ -572,14 +572,20 @@ def bench_extra_decode(args, pk, C, which):
     writes inside the decode launch)."""
     if which == "longctx":
         s = C.config5(device="cuda")
-        ds = pk.step.DeviceStep(s, partition_tokens=512)
+        # two device copies of the 1.6 GB cache, used in turn (the inputs
+        # were made on the GPU, so the second step gets cloned caches)
+        dss = [pk.step.DeviceStep(s, partition_tokens=512) for _ in range(2)]
+        dss[1].k_caches = [t.clone() for t in dss[1].k_caches]
+        dss[1].v_caches = [t.clone() for t in dss[1].v_caches]
         layers = [0]
         name = ("Llama-3.1-70B-shaped long-context decode, one layer: 6 x 131072 "
                 "tokens, 64 q / 8 kv heads, d128, bf16 q, fp8 e4m3 K/V, 512-token "
-                "partitions; new tokens' fp8 write + decode in one call")
+                "partitions; new tokens' fp8 write + decode in one call; two copies "
+                "of the cache used in turn")
     else:
         s = C.config3(device="cuda")
-        ds = pk.step.DeviceStep(s)
+        # one copy: each step reads 128 GiB, far past the last-level cache
+        dss = [pk.step.DeviceStep(s)]
         layers = list(range(s.num_layers))
         name = ("Llama-2-7B-shaped MHA decode, 32 layers back to back: 32 x 8192 "
                 "tokens, 32/32 heads, d128, bf16; per layer, new tokens' write + "
@@ -587,6 +593,7 @@ def bench_extra_decode(args, pk, C, which):
     stream = torch.cuda.current_stream()
 
     def run(i):
+        ds = dss[i % len(dss)]
         for layer in layers:
             ds.decode_append(layer)
 
