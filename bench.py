@@ -86,11 +86,38 @@ DECODE_SOURCES = ("paged_kv_cache_84_amd/csrc/decode.hip",
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_llama3_8b_64seq_traffic.md")
 
 
+def strip_comments(text):
+    """C++ source without its comments and blank lines, each line's trailing
+    spaces dropped (string and character literals kept whole): what the
+    compiler sees, so that editing a comment keeps the hash."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            while i < n and text[i] != "\n":
+                i += 1
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    lines = (line.rstrip() for line in "".join(out).split("\n"))
+    return "\n".join(line for line in lines if line)
+
+
 def decode_source_hash():
+    """Hash of the decode kernels' sources, comments aside."""
     h = hashlib.sha256()
     for rel in DECODE_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(strip_comments(f.read()).encode("utf-8"))
     return h.hexdigest()[:16]
 
 

@@ -10,6 +10,11 @@
 //
 // One wave per (work chunk, kv head) holds all query heads of the kv head's
 // group as the 16 columns of MFMA tiles (unused columns carry zero queries).
+// With an fp8 cache and a group of at most 8, one wave serves two adjacent
+// kv heads (NH = 2): their groups take columns 0-7 and 8-15, S^T is one
+// product chain per head with each column keeping its own head's, the
+// softmax and the table walk serve both, and each head's PV products see
+// P^T with the other head's columns zeroed, so both accumulate into one set.
 // Per 16-token block:
 //   S^T (16 keys x 16 heads) = K (16 x D) . Q^T      D/32 v_mfma_f32_16x16x32_bf16
 //     K is loaded straight into A-operand registers: lane l holds 16 bytes of
