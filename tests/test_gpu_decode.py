@@ -72,6 +72,11 @@ CASES = [
     (16, 2, 128, F.F32, F.F32, "f32"),
     (64, 8, 128, F.BF16, F.FP8_E4M3, "fp8_e4m3"),
     (12, 2, 64, F.BF16, F.FP8_E4M3, "fp8_e4m3"),
+    # fp8 with two kv heads per wave at group 1, and with one per wave where
+    # the kv head count is odd
+    (4, 4, 128, F.BF16, F.FP8_E4M3, "fp8_e4m3"),
+    (9, 3, 128, F.BF16, F.FP8_E4M3, "fp8_e4m3"),
+    (8, 1, 128, F.BF16, F.FP8_E4M3, "fp8_e4m3"),
 ]
 
 

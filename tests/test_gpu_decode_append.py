@@ -69,7 +69,7 @@ def _both(q, nk, nv, kc, vc, ks, vs, tables, lens, slots, partition):
 
 @pytest.mark.parametrize("kv", [F.BF16, F.FP8_E4M3])
 @pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (64, 8, 128), (16, 16, 128), (12, 4, 64),
-                                      (8, 1, 64)])
+                                      (8, 1, 64), (9, 3, 128)])
 @pytest.mark.parametrize("partition", [0, 64])
 def test_append_equals_write_then_decode(kv, hq, hkv, d, partition):
     announce("decode append", kv, hq, hkv, d, partition)
