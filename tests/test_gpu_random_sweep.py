@@ -1,0 +1,213 @@
+"""Seeded random configurations against the fp64 oracle: each case draws its
+own head counts, head size, cache dtype, lengths (including 0, 1 and block
+edges), partition size, value scale and block placement, so that the
+combinations the hand-picked cases do not name are covered too.
+
+Decode (plain, with the new token's write inside the launch, and with a
+sliding window), the chunked prefill (matrix-core tile and vector rows) and
+the unified launch; every output compared, cache bytes compared bitwise
+where a call writes them.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_84_amd as pk
+from gpu_util import announce, as_f64, host
+from oracle import formats as F
+from oracle import paged as P
+from synth import rng as R
+from synth.allocator import BlockPool, Sequence, tables_array
+from tolerance import assert_attention_close
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+EDGES = [0, 1, 15, 16, 17, 31, 32, 33]
+
+
+def _lengths(rng, n, hi):
+    """n lengths: block edges mixed with uniform draws up to hi."""
+    out = []
+    for _ in range(n):
+        if rng.random() < 0.4:
+            out.append(int(rng.choice(EDGES)))
+        else:
+            out.append(int(rng.integers(1, hi + 1)))
+    return out
+
+
+def _pool(rng, lengths, spare=3):
+    nb = sum(P.blocks_needed(max(L, 1)) for L in lengths) + spare
+    pool = BlockPool(nb, rng.permutation(nb))
+    seqs = [Sequence.fresh(pool, max(L, 1)) for L in lengths]
+    return nb, tables_array(seqs)
+
+
+def _caches(shape, kvd, seed, std):
+    if kvd == F.FP8_E4M3:
+        kc, ks = R.fp8_normal(shape, seed, 1, DEV)
+        vc, vs = R.fp8_normal(shape, seed, 2, DEV)
+        return kc.view(torch.uint8), vc.view(torch.uint8), ks, vs
+    return (R.normal(shape, kvd, seed, 1, DEV, std), R.normal(shape, kvd, seed, 2, DEV, std),
+            1.0, 1.0)
+
+
+def _decode_case(i):
+    rng = np.random.default_rng([84, 1, i])
+    hkv = int(rng.choice([1, 2, 3, 4, 8]))
+    group = int(rng.choice([1, 2, 3, 4, 6, 8]))
+    d = int(rng.choice([64, 128]))
+    kvd = F.FP8_E4M3 if rng.random() < 0.4 else F.BF16
+    n = int(rng.integers(1, 40))
+    lengths = _lengths(rng, n, int(rng.choice([300, 3000])))
+    partition = int(rng.choice([0, 0, 16, 48, 512]))
+    std = float(rng.choice([0.5, 1.0, 3.0]))
+    return rng, hkv, group, d, kvd, lengths, partition, std
+
+
+def _kind(kvd):
+    return "fp8_e4m3" if kvd == F.FP8_E4M3 else "bf16"
+
+
+def _cache_as_oracle(t, kvd):
+    """A device cache as the oracle's host array (fp8: the code bytes)."""
+    return host(t)
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_decode_random(i):
+    rng, hkv, group, d, kvd, lengths, partition, std = _decode_case(i)
+    hq = hkv * group
+    announce("random decode", i, hq, hkv, d, kvd, len(lengths), partition, std)
+    nb, tables = _pool(rng, lengths)
+    kc, vc, ks, vs = _caches((nb, hkv, 16, d), kvd, 7000 + i, std)
+    q = R.normal((len(lengths), hq, d), F.BF16, 7000 + i, 3, DEV, std)
+    lens = np.array(lengths, np.int32)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    bt, ln = torch.as_tensor(tables, device=DEV), torch.as_tensor(lens, device=DEV)
+    out = pk.paged_attention_decode(q, kc, vc, bt, ln, int(lens.max()), scale, ks, vs, partition)
+    torch.cuda.synchronize()
+    ref = P.decode_attention(host(q), F.BF16, _cache_as_oracle(kc, kvd),
+                             _cache_as_oracle(vc, kvd), kvd, tables, lens, scale, ks, vs)
+    assert_attention_close(as_f64(out), ref, _kind(kvd), f"random decode {i}")
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_decode_append_random(i):
+    """The new token's K/V written inside the decode launch: cache bytes as
+    the oracle's writer leaves them, outputs as the oracle's decode over
+    them."""
+    rng, hkv, group, d, kvd, lengths, partition, std = _decode_case(100 + i)
+    lengths = [max(L, 1) for L in lengths]          # every sequence brings a token
+    hq = hkv * group
+    announce("random decode append", i, hq, hkv, d, kvd, len(lengths), partition)
+    nb, tables = _pool(rng, lengths)
+    kc, vc, ks, vs = _caches((nb, hkv, 16, d), kvd, 7100 + i, std)
+    q = R.normal((len(lengths), hq, d), F.BF16, 7100 + i, 3, DEV, std)
+    nk = R.normal((len(lengths), hkv, d), F.BF16, 7100 + i, 4, DEV, std)
+    nv = R.normal((len(lengths), hkv, d), F.BF16, 7100 + i, 5, DEV, std)
+    lens = np.array(lengths, np.int32)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    rk, rv = _cache_as_oracle(kc, kvd), _cache_as_oracle(vc, kvd)
+    bt, ln = torch.as_tensor(tables, device=DEV), torch.as_tensor(lens, device=DEV)
+    out = pk.paged_attention_decode_append(q, nk, nv, kc, vc, bt, ln, int(lens.max()), scale,
+                                           ks, vs, partition)
+    torch.cuda.synchronize()
+    slots = np.array([P.slot_of(tables[s], int(lens[s]) - 1) for s in range(len(lens))],
+                     np.int64)
+    rk, rv = P.reshape_and_cache(host(nk), host(nv), rk, rv, slots, F.BF16, kvd, ks, vs)
+    assert np.array_equal(_cache_as_oracle(kc, kvd).view(np.uint8), rk.view(np.uint8))
+    assert np.array_equal(_cache_as_oracle(vc, kvd).view(np.uint8), rv.view(np.uint8))
+    ref = P.decode_attention(host(q), F.BF16, rk, rv, kvd, tables, lens, scale, ks, vs)
+    assert_attention_close(as_f64(out), ref, _kind(kvd), f"random decode append {i}")
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_sliding_window_random(i):
+    rng, hkv, group, d, kvd, lengths, partition, std = _decode_case(200 + i)
+    hq = hkv * group
+    window = int(rng.choice([1, 16, 17, 100, 1000]))
+    announce("random sliding window", i, hq, hkv, d, kvd, window, partition)
+    nb, tables = _pool(rng, lengths)
+    kc, vc, ks, vs = _caches((nb, hkv, 16, d), kvd, 7200 + i, std)
+    q = R.normal((len(lengths), hq, d), F.BF16, 7200 + i, 3, DEV, std)
+    lens = np.array(lengths, np.int32)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    bt, ln = torch.as_tensor(tables, device=DEV), torch.as_tensor(lens, device=DEV)
+    out = pk.paged_attention_decode_sliding(q, kc, vc, bt, ln, int(lens.max()), scale, window,
+                                            ks, vs, partition)
+    torch.cuda.synchronize()
+    ref = P.decode_attention_window(host(q), F.BF16, _cache_as_oracle(kc, kvd),
+                                    _cache_as_oracle(vc, kvd), kvd, tables, lens, scale, window,
+                                    ks, vs)
+    assert_attention_close(as_f64(out), ref, _kind(kvd), f"random window {i}")
+
+
+def _prefill_case(i, d_choices=(64, 128)):
+    rng = np.random.default_rng([84, 2, i])
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    group = int(rng.choice([1, 2, 4, 8]))
+    d = int(rng.choice(d_choices))
+    n = int(rng.integers(1, 12))
+    new, computed = [], []
+    for _ in range(n):
+        new.append(int(rng.choice([0, 1, 5, 16, 17, 100, 300])) if rng.random() < 0.5
+                   else int(rng.integers(1, 200)))
+        computed.append(int(rng.choice([0, 1, 15, 16, 17])) if rng.random() < 0.4
+                        else int(rng.integers(0, 1500)))
+    std = float(rng.choice([0.5, 1.0, 3.0]))
+    return rng, hkv, group, d, new, computed, std
+
+
+def _prefill_inputs(i, rng, hkv, group, d, new, computed, std, qd=F.BF16):
+    lens_total = [c + n for c, n in zip(computed, new)]
+    nb, tables = _pool(rng, lens_total)
+    shape = (nb, hkv, 16, d)
+    kc, vc = R.normal(shape, qd, 7300 + i, 1, DEV, std), R.normal(shape, qd, 7300 + i, 2, DEV, std)
+    qsl = np.concatenate([[0], np.cumsum(new)]).astype(np.int32)
+    comp = np.array(computed, np.int32)
+    q = R.normal((max(int(qsl[-1]), 1), hkv * group, d), qd, 7300 + i, 3, DEV, std)
+    return lens_total, tables, kc, vc, qsl, comp, q
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_prefill_random(i):
+    rng, hkv, group, d, new, computed, std = _prefill_case(i)
+    if sum(new) == 0:
+        new[0] = 3
+    announce("random prefill", i, hkv * group, hkv, d, new, computed)
+    lens_total, tables, kc, vc, qsl, comp, q = _prefill_inputs(i, rng, hkv, group, d, new,
+                                                               computed, std)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    bt, qs, cp = (torch.as_tensor(a, device=DEV) for a in (tables, qsl, comp))
+    out = pk.paged_attention_prefill_chunk(q, kc, vc, bt, qs, cp, int(max(new)), scale)
+    torch.cuda.synchronize()
+    ref = P.prefill_attention(host(q), F.BF16, host(kc), host(vc), F.BF16, tables, qsl, comp,
+                              scale)
+    assert_attention_close(as_f64(out)[:int(qsl[-1])], ref, "bf16", f"random prefill {i}")
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_varlen_random(i):
+    """The unified launch (bf16, head_dim 128) on a random mix of decodes,
+    short verifications and chunks."""
+    rng, hkv, group, d, new, computed, std = _prefill_case(100 + i, d_choices=(128,))
+    for r in range(len(new)):              # make some requests decodes or verifications
+        if rng.random() < 0.4:
+            new[r] = int(rng.choice([1, 1, 2, 4]))
+            computed[r] = int(rng.integers(0, 3000))
+    if sum(new) == 0:
+        new[0] = 1
+    announce("random varlen", i, hkv * group, hkv, new, computed)
+    lens_total, tables, kc, vc, qsl, comp, q = _prefill_inputs(100 + i, rng, hkv, group, d,
+                                                               new, computed, std)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    bt, qs, cp = (torch.as_tensor(a, device=DEV) for a in (tables, qsl, comp))
+    out = pk.paged_attention_varlen(q, kc, vc, bt, qs, cp, int(max(lens_total)), scale)
+    torch.cuda.synchronize()
+    ref = P.prefill_attention(host(q), F.BF16, host(kc), host(vc), F.BF16, tables, qsl, comp,
+                              scale)
+    assert_attention_close(as_f64(out)[:int(qsl[-1])], ref, "bf16", f"random varlen {i}")
