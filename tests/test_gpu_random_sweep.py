@@ -21,7 +21,7 @@ from oracle import formats as F
 from oracle import paged as P
 from synth import rng as R
 from synth.allocator import BlockPool, Sequence, tables_array
-from tolerance import assert_attention_close
+from tolerance import assert_attention_close, assert_fp32_accumulation_close
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -211,3 +211,83 @@ def test_varlen_random(i):
     ref = P.prefill_attention(host(q), F.BF16, host(kc), host(vc), F.BF16, tables, qsl, comp,
                               scale)
     assert_attention_close(as_f64(out)[:int(qsl[-1])], ref, "bf16", f"random varlen {i}")
+
+
+def _four_bit_case(i):
+    rng = np.random.default_rng([84, 3, i])
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    group = int(rng.choice([1, 2, 3, 4, 8]))
+    n = int(rng.integers(1, 40))
+    lengths = _lengths(rng, n, int(rng.choice([300, 3000])))
+    partition = int(rng.choice([0, 0, 16, 48, 512]))
+    return rng, hkv, group, lengths, partition
+
+
+@pytest.mark.parametrize("fmt", ["int4", "nvfp4"])
+@pytest.mark.parametrize("i", range(8))
+def test_four_bit_decode_random(fmt, i):
+    """int4 per token-head and nvfp4-style caches with random codes and
+    scales (head_dim 128, bf16 queries)."""
+    rng, hkv, group, lengths, partition = _four_bit_case(i if fmt == "int4" else 50 + i)
+    hq = hkv * group
+    announce("random", fmt, i, hq, hkv, len(lengths), partition)
+    nb, tables = _pool(rng, lengths)
+    seed = 7400 + i + (50 if fmt == "nvfp4" else 0)
+    kc = R.int4_codes((nb, hkv, 16, 64), seed, 1, DEV)
+    vc = R.int4_codes((nb, hkv, 16, 64), seed, 2, DEV)
+    q = R.normal((len(lengths), hq, 128), F.BF16, seed, 5, DEV)
+    lens = np.array(lengths, np.int32)
+    scale = float(np.float32(1 / math.sqrt(128)))
+    bt, ln = torch.as_tensor(tables, device=DEV), torch.as_tensor(lens, device=DEV)
+    if fmt == "int4":
+        ks = R.int4_scales((nb, hkv, 16), seed, 3, DEV)
+        vs = R.int4_scales((nb, hkv, 16), seed, 4, DEV)
+        out = pk.paged_attention_decode_int4(q, kc, vc, ks, vs, bt, ln, int(lens.max()), scale,
+                                             partition_tokens=partition)
+        torch.cuda.synchronize()
+        ref = P.decode_attention_int4(host(q), F.BF16, host(kc), host(vc), host(ks), host(vs),
+                                      tables, lens, scale)
+    else:
+        ks = R.nvfp4_bscales((nb, hkv, 16, 8), seed, 3, DEV)
+        vs = R.nvfp4_bscales((nb, hkv, 16, 8), seed, 4, DEV)
+        g_k, g_v = float(rng.choice([0.25, 1.0, 3.0])), float(rng.choice([0.5, 1.0, 2.0]))
+        out = pk.paged_attention_decode_nvfp4(q, kc, vc, ks, vs, bt, ln, int(lens.max()), scale,
+                                              g_k, g_v, partition_tokens=partition)
+        torch.cuda.synchronize()
+        ref = P.decode_attention_nvfp4(host(q), F.BF16, host(kc), host(vc), host(ks), host(vs),
+                                       tables, lens, scale, g_k, g_v)
+    assert_attention_close(as_f64(out), ref, "bf16", f"random {fmt} {i}")
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_prefill_other_dtypes_random(i):
+    """The chunked prefill's vector rows: fp32 caches, fp8 caches with bf16
+    queries, and head_dim 64."""
+    rng, hkv, group, d, new, computed, std = _prefill_case(300 + i)
+    if sum(new) == 0:
+        new[0] = 3
+    kind = ["f32", "fp8", "d64"][i % 3]
+    qd, kvd = (F.F32, F.F32) if kind == "f32" else (F.BF16, F.FP8_E4M3 if kind == "fp8" else F.BF16)
+    d = 64 if kind == "d64" else d
+    announce("random prefill", kind, i, hkv * group, hkv, d, new, computed)
+    lens_total = [c + n for c, n in zip(computed, new)]
+    nb, tables = _pool(rng, lens_total)
+    kc, vc, ks, vs = _caches((nb, hkv, 16, d), kvd, 7500 + i, std)
+    qsl = np.concatenate([[0], np.cumsum(new)]).astype(np.int32)
+    comp = np.array(computed, np.int32)
+    q = R.normal((int(qsl[-1]), hkv * group, d), qd, 7500 + i, 3, DEV, std)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    bt, qs, cp = (torch.as_tensor(a, device=DEV) for a in (tables, qsl, comp))
+    out = pk.paged_attention_prefill_chunk(q, kc, vc, bt, qs, cp, int(max(new)), scale, ks, vs)
+    torch.cuda.synchronize()
+    ref = P.prefill_attention(host(q), qd, host(kc), host(vc), kvd, tables, qsl, comp, scale,
+                              ks, vs)
+    if qd == F.F32:
+        # contexts of up to ~1,700 keys: the gate follows the fp32 rounding
+        mag = P.prefill_attention(host(q), qd, host(kc), np.abs(host(vc)), kvd, tables, qsl,
+                                  comp, scale, ks, vs)
+        assert_fp32_accumulation_close(as_f64(out), ref, mag, max(lens_total),
+                                       f"random prefill {kind} {i}")
+        return
+    tol = "fp8_e4m3" if kvd == F.FP8_E4M3 else "bf16"
+    assert_attention_close(as_f64(out), ref, tol, f"random prefill {kind} {i}")

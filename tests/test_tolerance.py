@@ -1,6 +1,7 @@
 """The attention accuracy gate itself (CPU only)."""
 
 import numpy as np
+import pytest
 import torch
 
 from tolerance import attention_errors, half_ulp
@@ -36,3 +37,24 @@ def test_floored_relative_bound_rejects_zero_output():
     r = np.full(64, 2e-3) * np.where(np.arange(64) % 2, 1, -1)
     ratio_a, ratio_b, _, _ = attention_errors(np.zeros_like(r), r, "bf16")
     assert ratio_a <= 1.0 and ratio_b > 1.0
+
+
+def test_fp32_accumulation_gate():
+    """The fp32 long-context gate: passes the rounding of a binary32 sum of n
+    terms, fails a result that lost one of n comparable terms."""
+    import numpy as np
+    from tolerance import assert_fp32_accumulation_close
+    rng = np.random.default_rng(5)
+    n = 1500
+    w = rng.random(n)
+    v = rng.normal(size=(n, 64)) * 3.0
+    exact = (w[:, None] * v).sum(0) / w.sum()
+    mag = (w[:, None] * np.abs(v)).sum(0) / w.sum()
+    acc = np.zeros(64, np.float32)
+    for i in range(n):                       # plain binary32 recursive summation
+        acc += np.float32(w[i]) * v[i].astype(np.float32)
+    got = acc / np.float32(w.astype(np.float32).sum())
+    assert_fp32_accumulation_close(got, exact, mag, n)
+    dropped = ((w[1:, None] * v[1:]).sum(0)) / w.sum()
+    with pytest.raises(AssertionError):
+        assert_fp32_accumulation_close(dropped, exact, mag, n)

@@ -70,3 +70,33 @@ def assert_attention_close(got, ref, kind, what=""):
         f"{what}: max abs err {max_abs:.3e} (worst |err|/(eps_abs + ulp/2) {ratio_a:.3f}); "
         f"max floored rel err {max_rel:.3e} (limit {eps_rel:.0e}, worst ratio {ratio_b:.3f})")
     return max_abs, max_rel
+
+
+U32 = 2.0 ** -24     # unit roundoff of binary32
+
+
+def assert_fp32_accumulation_close(got, ref, mag, n_terms, what=""):
+    """fp32 paths over long contexts, where the output is a normalised sum
+    of n_terms products accumulated in binary32.  Recursive summation of n
+    terms in binary32 errs by at most (n - 1) u times the sum of the terms'
+    magnitudes (u = 2^-24); with the rounding of the weights, their sum
+    and the final division (a few u more) the element-wise bound is
+
+        |g_i - r_i| <= 1e-5 + (n_terms + 8) * u * mag_i,
+
+    where mag_i is attention with |V| in place of V (the normalised sum of
+    magnitudes the output is accumulated from), from the same oracle.  The
+    fixed 1e-5 / 1e-4 gate of the fp32 toy assumes short contexts; this one
+    grows with the number of terms, as the rounding does, and stays far
+    below the change one wrong or missing key makes (about mag_i / n_eff)."""
+    g = np.asarray(got, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    m = np.asarray(mag, dtype=np.float64)
+    assert g.shape == r.shape == m.shape, (g.shape, r.shape, m.shape)
+    if r.size == 0:
+        return 0.0
+    assert np.all(np.isfinite(g)), f"{what}: non-finite output"
+    bound = 1e-5 + (n_terms + 8) * U32 * m
+    ratio = float((np.abs(g - r) / bound).max())
+    assert ratio <= 1.0, f"{what}: worst |err| / bound {ratio:.3f} (n_terms {n_terms})"
+    return ratio
