@@ -291,3 +291,93 @@ def test_prefill_other_dtypes_random(i):
         return
     tol = "fp8_e4m3" if kvd == F.FP8_E4M3 else "bf16"
     assert_attention_close(as_f64(out), ref, tol, f"random prefill {kind} {i}")
+
+
+def _bits(a):
+    a = np.ascontiguousarray(a)
+    return a.view(np.uint8)
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_cache_write_random(i):
+    """reshape_and_cache (copy or fp8), and the int4 and nvfp4 writers, with
+    random shapes, value scales and distinct slots, some of them -1: cache
+    bytes equal the oracle's."""
+    rng = np.random.default_rng([84, 4, i])
+    fmt = ["copy", "fp8", "int4", "nvfp4"][i % 4]
+    src = F.BF16 if rng.random() < 0.6 else F.F32
+    hkv = int(rng.choice([1, 2, 3, 8]))
+    d = 128 if fmt in ("int4", "nvfp4") else int(rng.choice([64, 128]))
+    nb = int(rng.integers(2, 40))
+    t = int(rng.integers(1, nb * 16))
+    std = float(rng.choice([0.01, 1.0, 50.0]))
+    slots = rng.permutation(nb * 16)[:t].astype(np.int64)
+    slots[rng.random(t) < 0.1] = -1
+    announce("random cache write", i, fmt, src, hkv, d, nb, t, std)
+    key = R.normal((t, hkv, d), src, 7600 + i, 1, DEV, std)
+    val = R.normal((t, hkv, d), src, 7600 + i, 2, DEV, std)
+    sl = torch.as_tensor(slots, device=DEV)
+    if fmt in ("copy", "fp8"):
+        dst = src if fmt == "copy" else F.FP8_E4M3
+        if dst == F.FP8_E4M3:
+            kc = R.int4_codes((nb, hkv, 16, d), 7600 + i, 3, DEV)      # arbitrary bytes
+            vc = R.int4_codes((nb, hkv, 16, d), 7600 + i, 4, DEV)
+            ks, vs = float(rng.choice([0.05, 1.0, 3.0])), float(rng.choice([0.01, 0.5]))
+        else:
+            kc = R.normal((nb, hkv, 16, d), dst, 7600 + i, 3, DEV)
+            vc = R.normal((nb, hkv, 16, d), dst, 7600 + i, 4, DEV)
+            ks = vs = 1.0
+        rk, rv = host(kc), host(vc)
+        pk.reshape_and_cache(key, val, kc, vc, sl, ks, vs)
+        torch.cuda.synchronize()
+        rk, rv = P.reshape_and_cache(host(key), host(val), rk, rv, slots, src, dst, ks, vs)
+        got = (host(kc), host(vc))
+        want = (rk, rv)
+    elif fmt == "int4":
+        kc = R.int4_codes((nb, hkv, 16, d // 2), 7600 + i, 3, DEV)
+        vc = R.int4_codes((nb, hkv, 16, d // 2), 7600 + i, 4, DEV)
+        ksc = R.int4_scales((nb, hkv, 16), 7600 + i, 5, DEV)
+        vsc = R.int4_scales((nb, hkv, 16), 7600 + i, 6, DEV)
+        before = [host(a) for a in (kc, vc, ksc, vsc)]
+        pk.reshape_and_cache_int4(key, val, kc, vc, ksc, vsc, sl)
+        torch.cuda.synchronize()
+        want = P.reshape_and_cache_int4(host(key), host(val), *before, slots, src)
+        got = tuple(host(a) for a in (kc, vc, ksc, vsc))
+    else:
+        kc = R.int4_codes((nb, hkv, 16, d // 2), 7600 + i, 3, DEV)
+        vc = R.int4_codes((nb, hkv, 16, d // 2), 7600 + i, 4, DEV)
+        kbs = R.nvfp4_bscales((nb, hkv, 16, d // 16), 7600 + i, 5, DEV)
+        vbs = R.nvfp4_bscales((nb, hkv, 16, d // 16), 7600 + i, 6, DEV)
+        g_k, g_v = float(rng.choice([0.25, 1.0, 7.0])), float(rng.choice([0.5, 1.0, 2.0]))
+        before = [host(a) for a in (kc, vc, kbs, vbs)]
+        pk.reshape_and_cache_nvfp4(key, val, kc, vc, kbs, vbs, sl, g_k, g_v)
+        torch.cuda.synchronize()
+        want = P.reshape_and_cache_nvfp4(host(key), host(val), *before, slots, src, g_k, g_v)
+        got = tuple(host(a) for a in (kc, vc, kbs, vbs))
+    for g, w in zip(got, want):
+        assert np.array_equal(_bits(g), _bits(w))
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_copy_blocks_random(i):
+    """copy_blocks over several layers with random (src, dst) pairs (distinct
+    destinations, none of them a source): every block as the oracle's."""
+    rng = np.random.default_rng([84, 5, i])
+    layers = int(rng.integers(1, 5))
+    hkv = int(rng.choice([1, 2, 8]))
+    d = int(rng.choice([64, 128]))
+    dt = F.BF16 if rng.random() < 0.7 else F.F32
+    nb = int(rng.integers(4, 64))
+    n = int(rng.integers(1, nb // 2 + 1))
+    perm = rng.permutation(nb)
+    src, dst = perm[:n], perm[n:2 * n]
+    pairs = np.stack([rng.choice(src, n), dst], axis=1).astype(np.int64)
+    announce("random copy_blocks", i, layers, hkv, d, dt, nb, n)
+    kcs = [R.normal((nb, hkv, 16, d), dt, 7700 + i, 2 * l, DEV) for l in range(layers)]
+    vcs = [R.normal((nb, hkv, 16, d), dt, 7700 + i, 2 * l + 1, DEV) for l in range(layers)]
+    rk, rv = P.copy_blocks([host(a) for a in kcs], [host(a) for a in vcs], pairs)
+    pk.copy_blocks(kcs, vcs, torch.as_tensor(pairs, device=DEV))
+    torch.cuda.synchronize()
+    for l in range(layers):
+        assert np.array_equal(_bits(host(kcs[l])), _bits(rk[l]))
+        assert np.array_equal(_bits(host(vcs[l])), _bits(rv[l]))
