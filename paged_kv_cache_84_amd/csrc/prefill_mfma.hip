@@ -1,6 +1,6 @@
 // Chunked-prefill attention on the gfx950 matrix cores (bf16, head_dim 128):
-// the kernel around prefill_tile (prefill_tile.h), one workgroup per (token
-// tile, kv head).
+// the kernel around prefill_tile (prefill_tile.h), one workgroup per (eight
+// 16-row units of the requests' rows, kv head).
 
 #include "abi_util.h"
 #include "common.h"
@@ -17,20 +17,22 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(
     int32_t num_reqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t group,
     float scale_log2) {
   __shared__ pf::Stage stage0, stage1;
-  prefill_tile(stage0, stage1, blockIdx.x, 0, out, query, k_cache, v_cache, num_blocks,
+  prefill_tile(stage0, stage1, blockIdx.x, out, query, k_cache, v_cache, num_blocks,
                block_tables, max_blocks, query_start_loc, num_computed, num_reqs, num_q_heads,
                num_kv_heads, group, scale_log2);
 }
 
-// Host launch: grid = (token tiles upper bound) x kv heads, kv head fastest.
-// The softmax uses the raw maximum score to decide rescaling, which needs a
-// positive scale; the caller routes other scales to the vector kernel.
+// Host launch: grid = (workgroups of units, upper bound) x kv heads, kv head
+// fastest.  A request of n tokens has ceil(n group / 16) units, at most
+// n group / 16 + 1.  The softmax uses the raw maximum score to decide
+// rescaling, which needs a positive scale; the caller routes other scales to
+// the vector kernel.
 pkv_status launch_prefill_mfma(const PrefillArgs& a) {
   const int group = a.num_q_heads / a.num_kv_heads;
-  const int tokens_per_wg = pf::kRows / group;
-  const int64_t tiles = (int64_t(a.num_q_tokens) + tokens_per_wg - 1) / tokens_per_wg +
+  const int64_t units = (int64_t(a.num_q_tokens) * group + pf::kUnitRows - 1) / pf::kUnitRows +
                         a.num_reqs;
-  const int64_t grid = tiles * a.num_kv_heads;
+  const int64_t pieces = (units + pf::kUnits - 1) / pf::kUnits;
+  const int64_t grid = pieces * a.num_kv_heads;
   if (grid > 0x7fffffff) return PKV_ERR_SHAPE;
   hipLaunchKernelGGL(prefill_mfma_kernel, dim3(uint32_t(grid)), dim3(256), 0,
                      as_stream(a.stream), static_cast<uint16_t*>(a.out),

@@ -7,11 +7,13 @@
 // chunk, QK^T and PV are dense contractions, so both run on MFMA
 // (v_mfma_f32_16x16x32_bf16), with fp32 accumulation.
 //
-// Work decomposition.  A workgroup (4 waves) owns 128 query rows of one
-// request and one kv head; rows are (token, q head) pairs of the kv head's
-// group, so the group's heads share every K/V tile.  Workgroups are numbered
-// kv-head-fastest, which puts one kv head on each of the eight XCDs (their L2
-// caches then each hold one head's shared prefix).
+// Work decomposition.  A workgroup (4 waves) owns 128 query rows and one kv
+// head; rows are (token, q head) pairs of the kv head's group, so the
+// group's heads share every K/V tile.  The rows are eight 16-row units taken
+// in order from the requests' rows, so a workgroup may hold the end of one
+// request and the start of the next (details above prefill_units).
+// Workgroups are numbered kv-head-fastest, which puts one kv head on each of
+// the eight XCDs (their L2 caches then each hold one head's shared prefix).
 //
 // Staging.  Keys are walked in tiles of 64 (four 16-token blocks gathered
 // through the block table).  Each wave copies one block of K and of V
@@ -62,6 +64,8 @@ constexpr int kD = 128;
 constexpr int kWaves = 4;
 constexpr int kRowsPerWave = 32;
 constexpr int kRows = kWaves * kRowsPerWave;   // query rows per workgroup
+constexpr int kUnitRows = 16;                  // rows of a unit (one MFMA column block)
+constexpr int kUnits = kRows / kUnitRows;      // units per workgroup, two per wave
 constexpr int kKeys = 64;                      // keys per tile (four blocks)
 constexpr int kRowBytes = kD * 2;              // one K or V row
 constexpr int kTileBytes = kKeys * kRowBytes;  // 16 KiB
@@ -111,12 +115,35 @@ struct Stage {
 }  // namespace pf
 
 
-// One workgroup (4 waves) of the chunked prefill: token tile `tile_in_req` of
-// request `req`, kv head `kvh`.  stage0 and stage1 are the workgroup's two
-// LDS stages, passed as separate objects so the compiler can tell the stage
-// being read from the stage the copies are writing.
-PKV_DEVICE void prefill_tile_at(
-    pf::Stage& stage0, pf::Stage& stage1, int req, int tile_in_req, int kvh,
+// One workgroup (4 waves) of the chunked prefill over kv head `kvh`.
+//
+// Its query rows are eight 16-row units taken in order from the requests'
+// rows (a request's rows are its (token, q head) pairs of the kv head's
+// group, token-major, so a unit holds 16 / group whole tokens).  Lane i < 8
+// passes unit i as (request, index of the unit in that request's rows);
+// request < 0 marks a unit past the last one.  Wave w owns units 2w and
+// 2w + 1, one per 16-row block of its S^T columns.  So a request's rows are
+// cut into workgroups without a partly empty workgroup at each request's
+// end: a request of 100 tokens at group 4 is 25 units, not three full tiles
+// and a fourth of 16 rows.
+//
+// Keys are walked in 64-key tiles in order.  At tile kt, the requests of the
+// workgroup whose four block ids for the tile are the same (requests on a
+// shared prefix, "PagedAttention：为 KV 缓存分页", the sharing of physical
+// blocks) are served by one staged copy; a request whose ids differ gets a
+// copy of its own, one after the other.  A wave multiplies only the copies
+// of its units' requests.  Within such a copy, a row of another request has
+// every score masked: its weights are 0, its rescale factor exactly 1 and
+// its products add exact zeros, so its running max, sum and output are
+// untouched.  Every row therefore sees exactly the tiles of its own request,
+// in order, with the same arithmetic whatever else shares its workgroup, and
+// a prompt's rows come out the same however its chunks are cut.
+//
+// stage0 and stage1 are the workgroup's two LDS stages, passed as separate
+// objects so the compiler can tell the stage being read from the stage the
+// copies are writing.
+PKV_DEVICE void prefill_units(
+    pf::Stage& stage0, pf::Stage& stage1, int unit_req, int unit_idx, int kvh,
     uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
     const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
     int32_t num_blocks, const int32_t* __restrict__ block_tables, int32_t max_blocks,
@@ -126,37 +153,110 @@ PKV_DEVICE void prefill_tile_at(
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int tokens_per_wg = kRows / group;
-  const int q_begin = load_scalar(query_start_loc, req);
-  const int n_req = load_scalar(query_start_loc, req + 1) - q_begin;
-  const int computed = load_scalar(num_computed, req);
-  const int tok0 = tile_in_req * tokens_per_wg;
-  const int ntok = min(tokens_per_wg, n_req - tok0);
-  const int first_pos = computed + tok0;           // position of the tile's first query
-  const int kv_len = first_pos + ntok;             // keys 0 .. kv_len-1 are visible
-  const int ntiles = (kv_len + kKeys - 1) / kKeys;
-  const int32_t* trow = block_tables + int64_t(req) * max_blocks;
+  const int tpu = kUnitRows / group;     // tokens per unit
 
-  // ---- this lane's queries (one per 16-row block) and their Q fragments
+  // ---- the units, lane i < 8 holding unit i
+  const int ur = lane < kUnits ? unit_req : -1;
+  const int uu = lane < kUnits ? unit_idx : 0;
+  const bool uvalid = ur >= 0;
+  int ubeg = 0, un = 0, ucomp = 0;
+  if (uvalid) {
+    ubeg = query_start_loc[ur];
+    un = query_start_loc[ur + 1] - ubeg;
+    ucomp = num_computed[ur];
+  }
+  const uint64_t valids = __ballot(uvalid);
+  if (valids == 0) return;      // the same for every wave of the workgroup
+  // keys the unit's rows see (through its last token)
+  const int ukeys = uvalid ? ucomp + min(uu * tpu + tpu, un) : 0;
+  // a request's first unit in the workgroup is its slot
+  const int prev = __shfl_up(ur, 1, kWave);
+  const bool ufirst = uvalid && (lane == 0 || prev != ur);
+  const uint64_t firsts = __ballot(ufirst);
+  const int uslot = uvalid ? 63 - __builtin_clzll(firsts & ((2ull << lane) - 1)) : 0;
+  // keys a slot's request sees in this workgroup: those of its last unit
+  int skeys;
+  {
+    const uint64_t above = lane < kWave - 1 ? firsts >> (lane + 1) : 0;
+    const int last = above ? lane + __builtin_ctzll(above) : __popcll(valids) - 1;
+    const int k = __shfl(ukeys, last, kWave);
+    skeys = ufirst ? k : 0;
+  }
+  const int stiles = (skeys + kKeys - 1) / kKeys;
+
+  // ---- this wave's units (2 wave + qb), their rows and Q fragments
   const int g = lane >> 4;          // lane group: keys 4g..4g+3 of a 16-key block
   const int n16 = lane & 15;
-  const bool wave_active = wave * kRowsPerWave < ntok * group;
-  int qpos[2];
+  int qreq[2], qslot[2], fpos[2], qbeg[2], qpos[2];
   bool qvalid[2];
   u32x4 qf[2][4];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const int row = wave * kRowsPerWave + qb * 16 + n16;
+    const int s = 2 * wave + qb;
+    qreq[qb] = __builtin_amdgcn_readlane(ur, s);
+    qslot[qb] = __builtin_amdgcn_readlane(uslot, s);
+    qbeg[qb] = __builtin_amdgcn_readlane(ubeg, s);
+    const int u = __builtin_amdgcn_readlane(uu, s);
+    const int n = __builtin_amdgcn_readlane(un, s);
+    const int c = __builtin_amdgcn_readlane(ucomp, s);
+    fpos[qb] = c + u * tpu;         // position of the unit's first token
+    const int row = u * kUnitRows + n16;
     const int t = row / group;
     const int h = kvh * group + row % group;
-    qvalid[qb] = t < ntok;
-    qpos[qb] = qvalid[qb] ? first_pos + t : -1;
-    const int tc = qvalid[qb] ? t : 0;      // keep the address inside the chunk
-    const uint16_t* qp = query + (int64_t(q_begin + tok0 + tc) * num_q_heads + h) * kD + g * 8;
+    qvalid[qb] = qreq[qb] >= 0 && t < n;
+    qpos[qb] = qvalid[qb] ? c + t : -1;
+    const int tc = qvalid[qb] ? t : 0;      // keep the address inside the batch
+    const uint16_t* qp = query + (int64_t(qbeg[qb] + tc) * num_q_heads + h) * kD + g * 8;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
       qf[qb][ks] = qvalid[qb] ? load16(qp + ks * 32) : u32x4{0, 0, 0, 0};
   }
+
+  // ---- block ids of a tile: lane 4i + b < 32 holds block b of unit i's
+  // request.  The loads are unconditional buffer loads (a lane without a
+  // request reads past the range and gets 0), so a load in flight is never
+  // merged into a register before it is used; entries past a table row are
+  // replaced by -1 when the ids are used.
+  const int idreq = __shfl(ur, (lane >> 2) & (kUnits - 1), kWave);
+  const bool idlane = lane < 4 * kUnits && idreq >= 0;
+  const int last_req = __builtin_amdgcn_readlane(ur, __popcll(valids) - 1);
+  const auto id_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int32_t*>(block_tables), 0,
+      int32_t(min<int64_t>((int64_t(last_req) + 1) * max_blocks * 4, 0x7fffffff)),
+      kRawBufferFlags);
+  const uint32_t id_off =
+      idlane ? uint32_t((int64_t(idreq) * max_blocks + (lane & 3)) * 4) : 0x80000000u;
+  auto load_ids = [&](int kt) -> int32_t {
+    return __builtin_amdgcn_raw_buffer_load_b32(id_rsrc, id_off + uint32_t(kt) * 16, 0, 0);
+  };
+  auto ids_at = [&](int32_t raw, int kt) -> int32_t {
+    return idlane && kt * 4 + (lane & 3) < max_blocks ? raw : -1;
+  };
+  // slots whose request reaches tile kt
+  auto active = [&](int kt) -> uint32_t { return uint32_t(__ballot(ufirst && kt < stiles)); };
+  // the copy that serves `pend`'s first slot, and the pending slots it serves
+  auto pick = [&](uint32_t pend, int32_t ids, int& lead, uint32_t& members) {
+    lead = __builtin_ctz(pend);
+    members = 1u << lead;
+    if (pend != members) {
+      const int32_t lid = __shfl(ids, 4 * lead + (lane & 3), kWave);
+      const uint64_t eq = __ballot(lane < 4 * kUnits && ids == lid);
+      const uint32_t e = uint32_t(eq);
+      const uint32_t all4 = e & (e >> 1) & (e >> 2) & (e >> 3);
+#pragma unroll
+      for (int i = 1; i < kUnits; ++i) members |= ((all4 >> (4 * i)) & 1u) << i;
+      members &= pend;
+    }
+  };
+  // keys the members' requests see: the copy stages no row past them
+  auto member_keys = [&](int lead, uint32_t members) -> int {
+    if (members == (1u << lead)) return __builtin_amdgcn_readlane(skeys, lead);
+    int k = (lane < kUnits && ((members >> (lane & 7)) & 1u)) ? skeys : 0;
+    k = max(k, __shfl_xor(k, 1, kWave));
+    k = max(k, __shfl_xor(k, 2, kWave));
+    k = max(k, __shfl_xor(k, 4, kWave));
+    return __builtin_amdgcn_readfirstlane(k);
+  };
 
   // ---- staging: wave w copies block w of each tile (4 x 1 KiB per cache).
   // Copy i writes rows 4i..4i+3 of the block; lane L lands on row 4i + L/16,
@@ -173,17 +273,21 @@ PKV_DEVICE void prefill_tile_at(
   const int64_t block_bytes = int64_t(num_kv_heads) * head_bytes;
   const char* kbase = reinterpret_cast<const char*>(k_cache) + int64_t(kvh) * head_bytes;
   const char* vbase = reinterpret_cast<const char*>(v_cache) + int64_t(kvh) * head_bytes;
-  auto table_id = [&](int lb) -> int32_t {
-    return lb < max_blocks ? load_scalar(trow, lb) : -1;
+  // a copy to stage: tile kt, leading slot, member slots, and for this
+  // wave's block the id and the rows inside the members' contexts
+  struct Copy {
+    int kt, lead, rows;
+    uint32_t members;
+    int32_t id;
   };
-  // issue the copies of logical block lb (id already read) into a stage
-  auto copy_block = [&](pf::Stage& st, int lb, int32_t id) {
-    int rows = min(max(kv_len - lb * kBlock, 0), kBlock);
-    const bool usable = id >= 0 && id < num_blocks;
+  // issue the copies of this wave's block of a copy into a stage
+  auto copy_block = [&](pf::Stage& st, const Copy& c) {
+    int rows = c.rows;
+    const bool usable = c.id >= 0 && c.id < num_blocks;
     // flag for compute(): inside the context but unusable
     if (lane == 0) st.bad[wave] = (rows > 0 && !usable) ? 1u : 0u;
     if (!usable) rows = 0;
-    const int32_t b = rows > 0 ? id : 0;
+    const int32_t b = rows > 0 ? c.id : 0;
     const auto rk = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<char*>(kbase + int64_t(b) * block_bytes), 0, rows * kRowBytes, kRawBufferFlags);
     const auto rv = __builtin_amdgcn_make_buffer_rsrc(
@@ -221,7 +325,9 @@ PKV_DEVICE void prefill_tile_at(
   float m[2] = {kNoMax, kNoMax};
   float l[2] = {0.f, 0.f};
 
-  auto compute = [&](const pf::Stage& st, int kt) {
+  // qp[qb]: positions the causal mask compares with (-1: every key masked);
+  // first_pos: the smallest of them over the wave's rows that take part
+  auto compute = [&](const pf::Stage& st, int kt, const int (&qp)[2], int first_pos) {
     lds_char_t* kl = (lds_char_t*)(&st.k[0]);
     lds_char_t* vl = (lds_char_t*)(&st.v[0]);
     // S^T for the 64 keys x 32 queries of this wave
@@ -262,7 +368,7 @@ PKV_DEVICE void prefill_tile_at(
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            if (key0 + kb * 16 + r > qpos[qb]) s[kb][qb][r] = -INFINITY;
+            if (key0 + kb * 16 + r > qp[qb]) s[kb][qb][r] = -INFINITY;
     }
     // does any score exceed its query's running max by more than kRaise?
     // (the scale is positive, so the raw maximum decides)
@@ -337,44 +443,134 @@ PKV_DEVICE void prefill_tile_at(
       }
     }
   };
+  // multiply the staged copy if it serves one of this wave's units
+  auto take = [&](const pf::Stage& st, int kt, uint32_t members) {
+    bool in[2];
+    int qp[2], first_pos = 0x7fffffff;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      in[qb] = qreq[qb] >= 0 && ((members >> qslot[qb]) & 1u);
+      qp[qb] = in[qb] ? qpos[qb] : -1;
+      // a unit of another request: every key masked; a unit past the end:
+      // rows that are never written, no constraint
+      if (qreq[qb] >= 0) first_pos = min(first_pos, in[qb] ? fpos[qb] : -1);
+    }
+    if (in[0] || in[1]) compute(st, kt, qp, first_pos);
+  };
 
-  // ---- the key loop: tile kt is read from stage kt % 2 while tile kt + 1
-  // is copied into the other stage; block ids come one tile ahead of that.
-  int32_t id_next = table_id(wave);               // tile 0
-  int32_t id_after = table_id(kKeys / kBlock + wave);   // tile 1
-  copy_block(stage0, wave, id_next);
+  if (firsts == 1) {
+    // ---- one request: one copy per tile, its block ids by scalar loads two
+    // tiles ahead
+    const int kv = __builtin_amdgcn_readlane(skeys, 0);
+    const int ntiles = (kv + kKeys - 1) / kKeys;
+    const int32_t* trow = block_tables + int64_t(__builtin_amdgcn_readlane(ur, 0)) * max_blocks;
+    auto table_id = [&](int lb) -> int32_t {
+      return lb < max_blocks ? load_scalar(trow, lb) : -1;
+    };
+    auto single = [&](int kt, int32_t id) {
+      Copy c;
+      c.kt = kt;
+      c.lead = 0;
+      c.members = 1;
+      c.id = id;
+      c.rows = min(max(kv - (kt * (kKeys / kBlock) + wave) * kBlock, 0), kBlock);
+      return c;
+    };
+    int32_t id_next = table_id(wave);
+    int32_t id_after = table_id(kKeys / kBlock + wave);
+    copy_block(stage0, single(0, id_next));
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+    for (int kt = 0; kt < ntiles; kt += 2) {
+      {
+        const bool more = kt + 1 < ntiles;
+        if (more) {
+          id_next = id_after;
+          id_after = table_id((kt + 2) * (kKeys / kBlock) + wave);
+          copy_block(stage1, single(kt + 1, id_next));
+        }
+        take(stage0, kt, 1u);
+        if (!more) break;
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        __syncthreads();
+      }
+      {
+        const bool more = kt + 2 < ntiles;
+        if (more) {
+          id_next = id_after;
+          id_after = table_id((kt + 3) * (kKeys / kBlock) + wave);
+          copy_block(stage0, single(kt + 2, id_next));
+        }
+        take(stage1, kt + 1, 1u);
+        if (!more) break;
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        __syncthreads();
+      }
+    }
+  } else {
+  // ---- the walk over copies.  ids_c holds the ids of tile nkt (the tile of
+  // the last copy decided); raw_n those of tile nkt + 1, reloaded before
+  // each copy is issued.  A copy is decided one copy ahead, after the
+  // products of the copy before it are issued, so that the walk's scalar
+  // work overlaps the tail of those products and the barrier.
+  int nkt = 0;
+  uint32_t covered = 0;
+  int32_t ids_c = ids_at(load_ids(0), 0);
+  int32_t raw_n = load_ids(1);
+  auto advance = [&](Copy& c) -> bool {
+    uint32_t pend = active(nkt) & ~covered;
+    if (pend == 0) {
+      ++nkt;
+      covered = 0;
+      ids_c = ids_at(raw_n, nkt);
+      pend = active(nkt);
+      if (pend == 0) return false;
+    }
+    pick(pend, ids_c, c.lead, c.members);
+    covered |= c.members;
+    c.kt = nkt;
+    const int lb = nkt * (kKeys / kBlock) + wave;
+    c.id = __builtin_amdgcn_readlane(ids_c, 4 * c.lead + wave);
+    c.rows = min(max(member_keys(c.lead, c.members) - lb * kBlock, 0), kBlock);
+    return true;
+  };
+
+  // ---- the key loop: copy c is read from stage c % 2 while copy c + 1 is
+  // staged into the other stage
+  Copy cur, nxt, nn;
+  advance(cur);                   // a valid unit sees at least one key
+  copy_block(stage0, cur);
+  bool more = advance(nxt);
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __syncthreads();
-  for (int kt = 0; kt < ntiles; kt += 2) {
-    // even tile from stage 0, its successor copied into stage 1
+  for (;;) {
     {
-      const bool more = kt + 1 < ntiles;
-      if (more) {
-        id_next = id_after;
-        id_after = table_id((kt + 2) * (kKeys / kBlock) + wave);
-        copy_block(stage1, (kt + 1) * (kKeys / kBlock) + wave, id_next);
-      }
-      if (wave_active) compute(stage0, kt);
+      raw_n = load_ids(nkt + 1);
+      if (more) copy_block(stage1, nxt);
+      take(stage0, cur.kt, cur.members);
       if (!more) break;
+      const bool more2 = advance(nn);
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
       __syncthreads();
+      cur = nxt;
+      nxt = nn;
+      more = more2;
     }
-    // odd tile from stage 1
     {
-      const bool more = kt + 2 < ntiles;
-      if (more) {
-        id_next = id_after;
-        id_after = table_id((kt + 3) * (kKeys / kBlock) + wave);
-        copy_block(stage0, (kt + 2) * (kKeys / kBlock) + wave, id_next);
-      }
-      if (wave_active) compute(stage1, kt + 1);
+      raw_n = load_ids(nkt + 1);
+      if (more) copy_block(stage0, nxt);
+      take(stage1, cur.kt, cur.members);
       if (!more) break;
+      const bool more2 = advance(nn);
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
       __syncthreads();
+      cur = nxt;
+      nxt = nn;
+      more = more2;
     }
   }
+  }
 
-  if (!wave_active) return;
   // ---- normalise and write: lane holds d = db*16 + 4g + 0..3 of its query
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
@@ -383,10 +579,10 @@ PKV_DEVICE void prefill_tile_at(
     lt += shfl_xor(lt, 32);
     if (!qvalid[qb]) continue;
     const float inv = 1.0f / lt;
-    const int row = wave * kRowsPerWave + qb * 16 + n16;
+    const int row = __builtin_amdgcn_readlane(uu, 2 * wave + qb) * kUnitRows + n16;
     const int t = row / group;
     const int h = kvh * group + row % group;
-    uint16_t* op = out + (int64_t(q_begin + tok0 + t) * num_q_heads + h) * kD + 4 * g;
+    uint16_t* op = out + (int64_t(qbeg[qb] + t) * num_q_heads + h) * kD + 4 * g;
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
       const uint32_t w0 = uint32_t(f32_to_bf16(o[db][qb][0] * inv)) |
@@ -398,12 +594,11 @@ PKV_DEVICE void prefill_tile_at(
   }
 }
 
-// The same, with the piece found by a scan over the requests: token tile
-// `wg / num_kv_heads` of the requests' tiles, kv head `wg % num_kv_heads`.
-// Requests with at most `narrow_rows` query rows (tokens x group) get no
-// tiles (another path serves them; 0 = every request).
+// The same, with the units found by a scan over the requests: units
+// 8 * (wg / num_kv_heads) .. +7 of all requests' units in order, kv head
+// wg % num_kv_heads.
 PKV_DEVICE void prefill_tile(
-    pf::Stage& stage0, pf::Stage& stage1, int wg, int narrow_rows,
+    pf::Stage& stage0, pf::Stage& stage1, int wg,
     uint16_t* __restrict__ out, const uint16_t* __restrict__ query,
     const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
     int32_t num_blocks, const int32_t* __restrict__ block_tables, int32_t max_blocks,
@@ -412,37 +607,33 @@ PKV_DEVICE void prefill_tile(
     float scale_log2) {
   using namespace pf;
   const int lane = threadIdx.x & (kWave - 1);
-  const int tokens_per_wg = kRows / group;
-
-  // ---- which (request, token tile, kv head) this workgroup owns
   const int kvh = wg % num_kv_heads;
-  const int tile = wg / num_kv_heads;
-  int req = -1, tile_in_req = 0;
-  {
-    int before = 0;
-    for (int base = 0; base < num_reqs; base += kWave) {
-      const int r = base + lane;
-      const int n = r < num_reqs ? query_start_loc[r + 1] - query_start_loc[r] : 0;
-      const int tiles = (n > 0 && n * group > narrow_rows) ? (n + tokens_per_wg - 1) / tokens_per_wg : 0;
-      const int incl = wave_scan(tiles);
-      const uint64_t hit = __ballot(before + incl > tile);
-      if (hit) {
-        const int first = __builtin_ctzll(hit);
-        const int incl_first = __shfl(incl, first, kWave);
-        const int tiles_first = __shfl(tiles, first, kWave);
-        req = base + first;
-        tile_in_req = tile - (before + incl_first - tiles_first);
-        break;
+  const int first = (wg / num_kv_heads) * kUnits;    // the workgroup's first unit
+  int ureq = -1, uidx = 0;
+  int before = 0;
+  for (int base = 0; base < num_reqs && before < first + kUnits; base += kWave) {
+    const int r = base + lane;
+    const int n = r < num_reqs ? query_start_loc[r + 1] - query_start_loc[r] : 0;
+    const int units = n > 0 ? int((int64_t(n) * group + kUnitRows - 1) / kUnitRows) : 0;
+    const int incl = wave_scan(units);
+    // unit t lies in the first request whose inclusive count passes it
+#pragma unroll
+    for (int i = 0; i < kUnits; ++i) {
+      const uint64_t hit = __ballot(before + incl > first + i);
+      if (hit != 0) {
+        const int j = __builtin_ctzll(hit);
+        const int start = before + __shfl(incl - units, j, kWave);
+        if (lane == i && ureq < 0) {
+          ureq = base + j;
+          uidx = first + i - start;
+        }
       }
-      before += __shfl(incl, kWave - 1, kWave);
     }
+    before += __shfl(incl, kWave - 1, kWave);
   }
-  req = __builtin_amdgcn_readfirstlane(req);
-  tile_in_req = __builtin_amdgcn_readfirstlane(tile_in_req);
-  if (req < 0) return;
-  prefill_tile_at(stage0, stage1, req, tile_in_req, kvh, out, query, k_cache, v_cache,
-                  num_blocks, block_tables, max_blocks, query_start_loc, num_computed,
-                  num_q_heads, num_kv_heads, group, scale_log2);
+  prefill_units(stage0, stage1, ureq, uidx, kvh, out, query, k_cache, v_cache, num_blocks,
+                block_tables, max_blocks, query_start_loc, num_computed, num_q_heads,
+                num_kv_heads, group, scale_log2);
 }
 
 }  // namespace pkv

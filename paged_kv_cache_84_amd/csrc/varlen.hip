@@ -16,8 +16,8 @@
 // cores on the chunks while the memory system streams the short requests'
 // histories:
 //   wide   requests with more than 16 query rows (tokens x group): the
-//          chunked-prefill tile of prefill_tile.h, one workgroup per (tile,
-//          kv head);
+//          chunked-prefill tile of prefill_tile.h, one workgroup per (eight
+//          16-row units of the wide requests' rows, kv head);
 //   narrow requests with at most 16 rows: one wave per (request, kv head,
 //          run of kNarrowChunk blocks) holds the request's rows as the 16
 //          columns of MFMA tiles and streams the run's blocks (as the decode
@@ -284,7 +284,7 @@ struct Plan {
   int32_t* tickets;        // counters: wide queue x at x * kTicketStride, narrow queue x
                            // at (8 + x) * kTicketStride; then the totals
   int32_t* cu_slots;       // workgroups arrived per compute unit
-  int2* wide_map;          // tile -> (request, tile of the request)
+  int2* wide_map;          // unit -> (request, 16-row unit of the request)
   int2* narrow_map;        // item -> (request, run)
   int32_t wide_cap, narrow_cap;
 };
@@ -295,7 +295,6 @@ __global__ __launch_bounds__(kPlanThreads) void varlen_plan_kernel(
   __shared__ int sw[kPlanThreads], sn[kPlanThreads];
   __shared__ int carry[2];
   const int tid = threadIdx.x;
-  const int tokens_per_wg = pf::kRows / group;
   if (tid < 2 * kQueues) plan.tickets[tid * kTicketStride] = 0;
   for (int i = tid; i < kCuSlots; i += kPlanThreads) plan.cu_slots[i] = 0;
   if (tid < 2) carry[tid] = 0;
@@ -307,7 +306,7 @@ __global__ __launch_bounds__(kPlanThreads) void varlen_plan_kernel(
       const int n = query_start_loc[r + 1] - query_start_loc[r];
       const int c = num_computed[r];
       if (n > 0 && n * group > vl::kNarrowRows)
-        wt = (n + tokens_per_wg - 1) / tokens_per_wg;
+        wt = (n * group + pf::kUnitRows - 1) / pf::kUnitRows;
       else if (n > 0 && c >= 0)
         ni = min(vl::runs_of(min((c + n + kBlock - 1) / kBlock, max_blocks)), runs_per_req);
     }
@@ -353,7 +352,8 @@ __global__ __launch_bounds__(256, 2) void varlen_kernel(
   const int x = blockIdx.x % kQueues;
   const int wide_x = (wide_wgs + kQueues - 1 - x) / kQueues;     // queue x's share of each kind
   const int narrow_x = (narrow_wgs + kQueues - 1 - x) / kQueues;
-  const int wide_tiles = load_scalar(plan.tickets, kWideCount);
+  const int wide_units = load_scalar(plan.tickets, kWideCount);
+  const int wide_pieces = (wide_units + pf::kUnits - 1) / pf::kUnits;
   const int narrow_items = load_scalar(plan.tickets, kNarrowCount);
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);
   // The first workgroup to arrive on a compute unit prefers wide work, the
@@ -385,7 +385,7 @@ __global__ __launch_bounds__(256, 2) void varlen_kernel(
     __syncthreads();     // every thread holds the ticket before the stages fill
     const int idx = k * kQueues + x;
     // indices only grow along a queue: the first one past the work closes it
-    if (wide && (k >= wide_x || idx / num_kv_heads >= wide_tiles)) {
+    if (wide && (k >= wide_x || idx / num_kv_heads >= wide_pieces)) {
       wide_open = false;
       continue;
     }
@@ -394,15 +394,14 @@ __global__ __launch_bounds__(256, 2) void varlen_kernel(
       continue;
     }
     if (wide) {
-      const int tile = idx / num_kv_heads;
-      {
-        const int2 piece = reinterpret_cast<const int2*>(plan.wide_map)[tile];
-        prefill_tile_at(stage0, stage1, __builtin_amdgcn_readfirstlane(piece.x),
-                        __builtin_amdgcn_readfirstlane(piece.y), idx % num_kv_heads, out,
-                        query, k_cache, v_cache, num_blocks, block_tables, max_blocks,
-                        query_start_loc, num_computed, num_q_heads, num_kv_heads, group,
-                        scale_log2);
-      }
+      // units 8 piece .. +7, lane i < 8 reading unit i's entry
+      const int lane = int(threadIdx.x) & (kWave - 1);
+      const int u = (idx / num_kv_heads) * pf::kUnits + (lane & (pf::kUnits - 1));
+      int2 unit = make_int2(-1, 0);
+      if (lane < pf::kUnits && u < wide_units) unit = plan.wide_map[u];
+      prefill_units(stage0, stage1, unit.x, unit.y, idx % num_kv_heads, out, query, k_cache,
+                    v_cache, num_blocks, block_tables, max_blocks, query_start_loc,
+                    num_computed, num_q_heads, num_kv_heads, group, scale_log2);
     } else {
       // narrow: wave w of workgroup idx takes unit idx * 4 + w; a unit is
       // (item, kv head) with the kv head fastest, so the waves of a workgroup
@@ -485,9 +484,9 @@ static bool varlen_plan(int32_t num_reqs, int32_t num_q_tokens, int32_t num_kv_h
     return false;
   const int nblk = (max_seq_len + kBlock - 1) / kBlock;
   p.runs_per_req = std::max(1, vl::runs_of(nblk));
-  // a tile holds at least 16 tokens (128 rows, group at most 8); each
-  // request's last tile may be partial
-  p.wide_cap = (int64_t(num_q_tokens) + 15) / 16 + num_reqs;
+  // 16-row units: at most n group / 16 + 1 for a request of n tokens, and
+  // the group is at most 8
+  p.wide_cap = (int64_t(num_q_tokens) + 1) / 2 + num_reqs;
   p.narrow_cap = int64_t(num_reqs) * p.runs_per_req;
   const size_t recs = size_t(p.narrow_cap) * num_kv_heads;
   p.ticket_bytes = align256((kNarrowCount + 1) * sizeof(int32_t)) + kCuSlots * sizeof(int32_t);
@@ -541,9 +540,10 @@ extern "C" pkv_status paged_attention_varlen(
     return PKV_ERR_SHAPE;
   if (!workspace || workspace_bytes < p.total()) return PKV_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return PKV_ERR_ALIGN;
-  const int tokens_per_wg = pf::kRows / group;
-  const int64_t wide = ((int64_t(num_q_tokens) + tokens_per_wg - 1) / tokens_per_wg + num_reqs) *
-                       num_kv_heads;
+  // workgroups of eight 16-row units (a request of n tokens: ceil(n group / 16))
+  const int64_t units = (int64_t(num_q_tokens) * group + pf::kUnitRows - 1) / pf::kUnitRows +
+                        num_reqs;
+  const int64_t wide = (units + pf::kUnits - 1) / pf::kUnits * num_kv_heads;
   const int64_t narrow = (int64_t(num_reqs) * p.runs_per_req * num_kv_heads + 3) / 4;
   // persistent: two workgroups per compute unit (the occupancy the LDS and
   // registers allow), never more than the longest queue needs
