@@ -320,8 +320,19 @@ __global__ __launch_bounds__(kPlanThreads) void varlen_plan_kernel(
       sn[tid] += an;
       __syncthreads();
     }
-    const int w0 = carry[0] + sw[tid] - wt, n0 = carry[1] + sn[tid] - ni;
-    for (int k = 0; k < wt && w0 + k < plan.wide_cap; ++k) plan.wide_map[w0 + k] = make_int2(r, k);
+    const int n0 = carry[1] + sn[tid] - ni;
+    // wide units: the threads share the entries (a long chunk has hundreds),
+    // each finding the request of its entry by a binary search of the scan
+    for (int g = tid; g < sw[kPlanThreads - 1]; g += kPlanThreads) {
+      int lo = 0, hi = kPlanThreads - 1;       // first i with sw[i] > g
+      while (lo < hi) {
+        const int mid = (lo + hi) / 2;
+        if (sw[mid] > g) hi = mid;
+        else lo = mid + 1;
+      }
+      const int u = carry[0] + g;
+      if (u < plan.wide_cap) plan.wide_map[u] = make_int2(base + lo, g - (lo > 0 ? sw[lo - 1] : 0));
+    }
     for (int k = 0; k < ni && n0 + k < plan.narrow_cap; ++k)
       plan.narrow_map[n0 + k] = make_int2(r, k);
     __syncthreads();
