@@ -130,15 +130,19 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
 }
 
 // ---------------------------------------- slot mapping + cache write in one
-// One workgroup per token t.  Its K/V loads go out first; meanwhile every
-// wave finds t's request: lanes load query_start_loc and num_computed_tokens
-// of kSearchBatch x 64 requests at once and the lane whose request holds t
-// wins a ballot.  Then one load of the block-table entry gives the slot
-// (the same formula and the same -1 cases as slot_mapping_kernel); thread 0
-// stores it, and the rows go to the cache.  Two dependent trips to memory
-// instead of the four of the two separate kernels.
+// One wave per token t, four tokens per workgroup.  The token's K/V loads go
+// out first; meanwhile the wave finds t's request: lanes load
+// query_start_loc and num_computed_tokens of kSearchBatch x 64 requests at
+// once and the lane whose request holds t wins a ballot.  Then one load of
+// the block-table entry gives the slot (the same formula and the same -1
+// cases as slot_mapping_kernel); lane 0 stores it, and the rows go to the
+// cache.  Two dependent trips to memory instead of the four of the two
+// separate kernels.  The work per token is small and latency-bound, so a
+// wave per token (not a workgroup) lets the whole step's tokens be in flight
+// at once.
 constexpr int kSearchBatch = 4;
-constexpr int kHeldVecs = 4;      // 16-byte source pieces a thread holds while searching
+constexpr int kHeldVecs = 4;      // 16-byte source pieces a lane holds while searching
+constexpr int kSchedTokensPerWg = 4;
 
 template <typename Src, typename Dst>
 __global__ __launch_bounds__(256) void reshape_and_cache_sched_kernel(
@@ -147,10 +151,11 @@ __global__ __launch_bounds__(256) void reshape_and_cache_sched_kernel(
     typename Dst::storage* __restrict__ k_cache, typename Dst::storage* __restrict__ v_cache,
     const int32_t* __restrict__ block_tables, int32_t max_blocks,
     const int32_t* __restrict__ query_start_loc, const int32_t* __restrict__ num_computed,
-    int32_t num_reqs, int64_t* __restrict__ slots_out, int32_t num_kv_heads,
+    int32_t num_reqs, int64_t* __restrict__ slots_out, int32_t num_tokens, int32_t num_kv_heads,
     int32_t head_dim, int32_t num_blocks, float k_scale, float v_scale) {
   using W = Writer<Src, Dst>;
-  const int t = blockIdx.x;
+  const int t = int(blockIdx.x) * kSchedTokensPerWg + int(threadIdx.x) / kWave;
+  if (t >= num_tokens) return;      // the wave's token is past the last
   const int lane = lane_id();
   const int vecs_per_head = head_dim / W::kElems;
   const int vecs = num_kv_heads * vecs_per_head;
@@ -163,7 +168,7 @@ __global__ __launch_bounds__(256) void reshape_and_cache_sched_kernel(
   u32x4 held[kHeldVecs];
 #pragma unroll
   for (int n = 0; n < kHeldVecs; ++n) {
-    const int i = int(threadIdx.x) + n * int(blockDim.x);
+    const int i = lane + n * kWave;
     if (i < 2 * vecs) held[n] = load16(src_of(i));
   }
 
@@ -205,7 +210,7 @@ __global__ __launch_bounds__(256) void reshape_and_cache_sched_kernel(
       if (b >= 0 && b < num_blocks) slot = int64_t(b) * kBlock + p % kBlock;
     }
   }
-  if (slots_out != nullptr && threadIdx.x == 0) slots_out[t] = slot;
+  if (slots_out != nullptr && lane == 0) slots_out[t] = slot;
   if (slot < 0) return;
   const int64_t block = slot / kBlock;
   const int offset = int(slot % kBlock);
@@ -217,10 +222,10 @@ __global__ __launch_bounds__(256) void reshape_and_cache_sched_kernel(
   };
 #pragma unroll
   for (int n = 0; n < kHeldVecs; ++n) {
-    const int i = int(threadIdx.x) + n * int(blockDim.x);
+    const int i = lane + n * kWave;
     if (i < 2 * vecs) W::store(held[n], dst_of(i, k_cache, v_cache), i >= vecs ? v_scale : k_scale);
   }
-  for (int i = int(threadIdx.x) + kHeldVecs * int(blockDim.x); i < 2 * vecs; i += blockDim.x)
+  for (int i = lane + kHeldVecs * kWave; i < 2 * vecs; i += kWave)
     W::run(src_of(i), dst_of(i, k_cache, v_cache), i >= vecs ? v_scale : k_scale);
 }
 
@@ -471,12 +476,14 @@ static pkv_status launch_write_sched(const void* key, const void* value, void* k
                                      const int32_t* computed, int32_t reqs, int64_t* slots,
                                      int32_t t, int32_t hkv, int32_t d, int32_t nb, float ks,
                                      float vs, void* stream) {
-  hipLaunchKernelGGL((reshape_and_cache_sched_kernel<Src, Dst>), dim3(t), dim3(256), 0,
+  hipLaunchKernelGGL((reshape_and_cache_sched_kernel<Src, Dst>),
+                     dim3((t + kSchedTokensPerWg - 1) / kSchedTokensPerWg),
+                     dim3(kWave * kSchedTokensPerWg), 0,
                      as_stream(stream), static_cast<const typename Src::storage*>(key),
                      static_cast<const typename Src::storage*>(value),
                      static_cast<typename Dst::storage*>(kc),
                      static_cast<typename Dst::storage*>(vc), bt, maxb, qsl, computed, reqs,
-                     slots, hkv, d, nb, ks, vs);
+                     slots, t, hkv, d, nb, ks, vs);
   return launch_status();
 }
 
