@@ -33,7 +33,7 @@ pkv_status launch_prefill_mfma(const PrefillArgs& a) {
                         a.num_reqs;
   const int64_t pieces = (units + pf::kUnits - 1) / pf::kUnits;
   const int64_t grid = pieces * a.num_kv_heads;
-  if (grid > 0x7fffffff) return PKV_ERR_SHAPE;
+  if (grid > 0x7fffffff || pieces * pf::kUnits > 0x7fffffff) return PKV_ERR_SHAPE;
   hipLaunchKernelGGL(prefill_mfma_kernel, dim3(uint32_t(grid)), dim3(256), 0,
                      as_stream(a.stream), static_cast<uint16_t*>(a.out),
                      static_cast<const uint16_t*>(a.query),

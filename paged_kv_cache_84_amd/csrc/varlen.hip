@@ -568,7 +568,9 @@ extern "C" pkv_status paged_attention_varlen(
       (2 * int64_t(cus) + kQueues - 1) / kQueues);
   const int64_t grid = per_queue * kQueues;
   if (grid > 0x7fffffff || int64_t(num_reqs) * num_kv_heads > 0x7fffffff) return PKV_ERR_SHAPE;
-  if (p.wide_cap > 0x7fffffff || p.narrow_cap > 0x7fffffff) return PKV_ERR_SHAPE;
+  if (p.wide_cap > 0x7fffffff || p.narrow_cap > 0x7fffffff ||
+      (units + pf::kUnits - 1) / pf::kUnits * pf::kUnits > 0x7fffffff)
+    return PKV_ERR_SHAPE;
   char* ws = static_cast<char*>(workspace);
   Plan plan;
   plan.tickets = reinterpret_cast<int32_t*>(ws);
