@@ -131,15 +131,19 @@ PKV_DEVICE int32_t load_scalar(const int32_t* p, int64_t i) {
   return ((const_i32_t*)p)[i];
 }
 
-// Sum of v over the lanes below this one.
+// Sum of v over the lanes below this one.  An inclusive scan by DPP moves
+// (no LDS round trips): within each row of 16 lanes, shifts by 1, 2, 4 and 8
+// (lanes shifted in from outside the row add 0); then the last lane of row 0
+// is added to row 1 and that of row 2 to row 3 (row_bcast:15), and lane 31
+// to rows 2 and 3 (row_bcast:31).
 PKV_DEVICE int wave_exclusive_sum(int v) {
-  const int lane = lane_id();
   int x = v;
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int t = __shfl_up(x, d, kWave);
-    if (lane >= d) x += t;
-  }
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
   return x - v;
 }
 

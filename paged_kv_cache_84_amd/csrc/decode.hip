@@ -637,13 +637,26 @@ __global__ __launch_bounds__(kWave * merge_waves<W>()) void decode_merge_kernel(
       for (int i = 0; i < kPer; ++i)
         x[j][i] = j < nparts ? po[j * stride * D + i * kWave] : 0.f;
     const float2 mine = lane < nparts ? ml[lane * stride] : make_float2(-INFINITY, 0.f);
-    const float big = wave_max(mine.x);
+    // the pairs sit in lanes 0..kFewParts-1 (the rest hold -inf, 0): read
+    // lane by lane; the weighted sum in the tree a butterfly over the wave
+    // would take, ((d0 + d1) + (d2 + d3)) + ((d4 + d5) + (d6 + d7))
+    static_assert(kFewParts == 8, "the sum tree below is written for eight partials");
+    auto lane_f = [](float v, int k) {
+      return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), k));
+    };
+    float big = lane_f(mine.x, 0);
+#pragma unroll
+    for (int k = 1; k < kFewParts; ++k) big = fmaxf(big, lane_f(mine.x, k));
     const float wk = lane < nparts ? fast_exp2(mine.x - big) : 0.f;
-    const float den = wave_sum(wk * mine.y);
+    const float dk = wk * mine.y;
+    float d[kFewParts];
+#pragma unroll
+    for (int k = 0; k < kFewParts; ++k) d[k] = lane_f(dk, k);
+    const float den = ((d[0] + d[1]) + (d[2] + d[3])) + ((d[4] + d[5]) + (d[6] + d[7]));
     float acc[kPer] = {};
 #pragma unroll
     for (int j = 0; j < kFewParts; ++j) {
-      const float wj = __shfl(wk, j, kWave);
+      const float wj = lane_f(wk, j);
 #pragma unroll
       for (int i = 0; i < kPer; ++i) acc[i] = fmaf(wj, x[j][i], acc[i]);
     }
