@@ -5,8 +5,8 @@ combinations the hand-picked cases do not name are covered too.
 
 Decode (plain, with the new token's write inside the launch, and with a
 sliding window), the chunked prefill (matrix-core tile and vector rows) and
-the unified launch; every output compared, cache bytes compared bitwise
-where a call writes them.
+the unified launch, also with requests that share leading blocks; every
+output compared, cache bytes compared bitwise where a call writes them.
 """
 
 import math
@@ -211,6 +211,76 @@ def test_varlen_random(i):
     ref = P.prefill_attention(host(q), F.BF16, host(kc), host(vc), F.BF16, tables, qsl, comp,
                               scale)
     assert_attention_close(as_f64(out)[:int(qsl[-1])], ref, "bf16", f"random varlen {i}")
+
+
+def _shared_tables(rng, lens_total):
+    """Block tables where a request may name the same physical blocks as an
+    earlier request for a random number of its leading blocks (a shared
+    prefix), the rest of its blocks its own."""
+    need = [P.blocks_needed(max(L, 1)) for L in lens_total]
+    nb = sum(need) + 3
+    free = [int(b) for b in rng.permutation(nb)]
+    rows = []
+    for r in range(len(lens_total)):
+        row = []
+        if r > 0 and rng.random() < 0.6:
+            src = int(rng.integers(max(0, r - 3), r))
+            row = list(rows[src][:int(rng.integers(1, min(need[r], need[src]) + 1))])
+        while len(row) < need[r]:
+            row.append(free.pop())
+        rows.append(row)
+    tables = np.full((len(rows), max(need)), -1, np.int32)
+    for r, row in enumerate(rows):
+        tables[r, :len(row)] = row
+    return nb, tables
+
+
+@pytest.mark.parametrize("path", ["chunk", "varlen"])
+@pytest.mark.parametrize("i", range(8))
+def test_shared_prefix_random(path, i):
+    """Requests whose tables share leading blocks, so that the matrix-core
+    tile stages a key tile once for several requests of a workgroup: every
+    row against the oracle, and bitwise against its request computed
+    alone."""
+    rng = np.random.default_rng([84, 6, i])
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    group = int(rng.choice([1, 2, 4, 8]))
+    n = int(rng.integers(2, 14))
+    new = [int(rng.choice([1, 2, 3, 4, 5, 8, 13, 16, 17, 33, 64, 100])) for _ in range(n)]
+    computed = [int(rng.choice([0, 16, 64, 100, 700])) if rng.random() < 0.5
+                else int(rng.integers(0, 800)) for _ in range(n)]
+    std = float(rng.choice([0.5, 1.0, 3.0]))
+    announce("random shared prefix", path, i, hkv * group, hkv, new, computed)
+    lens_total = [c + m for c, m in zip(computed, new)]
+    nb, tables = _shared_tables(rng, lens_total)
+    shape = (nb, hkv, 16, 128)
+    kc = R.normal(shape, F.BF16, 7600 + i, 1, DEV, std)
+    vc = R.normal(shape, F.BF16, 7600 + i, 2, DEV, std)
+    qsl = np.concatenate([[0], np.cumsum(new)]).astype(np.int32)
+    comp = np.array(computed, np.int32)
+    q = R.normal((int(qsl[-1]), hkv * group, 128), F.BF16, 7600 + i, 3, DEV, std)
+    scale = float(np.float32(1 / math.sqrt(128)))
+    max_len = int(max(lens_total))
+
+    def call(q_, tables_, qsl_, comp_):
+        bt, qs, cp = (torch.as_tensor(np.ascontiguousarray(a), device=DEV)
+                      for a in (tables_, qsl_, comp_))
+        if path == "chunk":
+            return pk.paged_attention_prefill_chunk(q_, kc, vc, bt, qs, cp,
+                                                    int(np.diff(qsl_).max()), scale)
+        return pk.paged_attention_varlen(q_, kc, vc, bt, qs, cp, max_len, scale)
+
+    whole = call(q, tables, qsl, comp)
+    alone = [call(q[int(qsl[r]):int(qsl[r + 1])].contiguous(), tables[r:r + 1],
+                  np.array([0, new[r]], np.int32), comp[r:r + 1]) for r in range(n)]
+    torch.cuda.synchronize()
+    for r in range(n):
+        a, b = int(qsl[r]), int(qsl[r + 1])
+        assert torch.equal(whole[a:b].view(torch.int16), alone[r].view(torch.int16)), (
+            f"request {r}: computed {computed[r]}, {new[r]} tokens")
+    ref = P.prefill_attention(host(q), F.BF16, host(kc), host(vc), F.BF16, tables, qsl, comp,
+                              scale)
+    assert_attention_close(as_f64(whole), ref, "bf16", f"random shared prefix {path} {i}")
 
 
 def _four_bit_case(i):
