@@ -95,11 +95,18 @@ constexpr bool kPacked4 = kInt4<KVT> || kNvfp4<KVT>;   // 4-bit codes, two per b
 template <typename KVT>
 constexpr int kElemBits = kPacked4<KVT> ? 4 : 8 * KVT::bytes;
 
-// 136 in bf16: an int4 element enters the products as 128 + u = 136 + q (a
-// bf16 with the nibble in its low mantissa bits), and 136 * (sum of the
+// 136 in bf16: an int4 K element enters the products as 128 + u = 136 + q
+// (a bf16 with the nibble in its low mantissa bits), and 136 * (sum of the
 // other operand) is subtracted afterwards.
 constexpr uint32_t kBf16x2_136 = 0x43084308u;
-constexpr float kInt4Offset = 136.0f;
+// An int4 V element enters the PV products as 1 + u/16 = 1.5 + q/16 (the
+// nibble in the top four mantissa bits of 1.0): the sum over the keys then
+// carries 1.5 sum p beside the wanted sum p q / 16, three times the wanted
+// part at most instead of seventeen with 136 + q, so removing the offset
+// after a long context cancels far fewer bits of the fp32 sum.  The factor
+// 16 is applied with the offset's removal (exact).
+constexpr float kInt4VOffset = 1.5f;
+constexpr float kInt4VFactor = 16.0f;
 
 // Eight nibbles (elements 0..7 of a little-endian dword) -> four dwords of
 // bf16 pairs 128 + u: dword e holds elements 2e (low half) and 2e + 1.
@@ -113,6 +120,19 @@ PKV_DEVICE u32x4 int4x8_to_bf16_offset(uint32_t w) {
     // 0x0C gives a zero byte
     const uint32_t sel = 0x0C000C00u | (uint32_t(4 + e) << 16) | uint32_t(e);
     o[e] = __builtin_amdgcn_perm(hi, lo, sel) | 0x43004300u;
+  }
+  return o;
+}
+// Eight nibbles -> four dwords of bf16 pairs 1 + u/16: the nibbles moved to
+// bits 3..6 of their bytes, and the exponent of 1.0 (0x3F80) or'ed in.
+PKV_DEVICE u32x4 int4x8_to_bf16_v(uint32_t w) {
+  const uint32_t lo = (w << 3) & 0x78787878u;    // elements 0, 2, 4, 6
+  const uint32_t hi = (w >> 1) & 0x78787878u;    // elements 1, 3, 5, 7
+  u32x4 o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t sel = 0x0C000C00u | (uint32_t(4 + e) << 16) | uint32_t(e);
+    o[e] = __builtin_amdgcn_perm(hi, lo, sel) | 0x3F803F80u;
   }
   return o;
 }
@@ -248,12 +268,12 @@ PKV_DEVICE void stage_v(VRegs<KVT, D>& r, char* vl, int lane, int rows) {
   }
   if constexpr (kInt4<KVT>) {
     // lane L holds dims 32 (L%4) .. + 31 of key L/4; every code is a finite
-    // bf16 (128 + u), and rows past `rows` get zero weight, so nothing is
+    // bf16 (1 + u/16), and rows past `rows` get zero weight, so nothing is
     // cleared here
     char* dst = vl + (lane / 4) * M::kVStride + (lane % 4) * 64;
 #pragma unroll
     for (int w = 0; w < 4; ++w)
-      *reinterpret_cast<u32x4*>(dst + 16 * w) = int4x8_to_bf16_offset(r.v[0][w]);
+      *reinterpret_cast<u32x4*>(dst + 16 * w) = int4x8_to_bf16_v(r.v[0][w]);
     return;
   }
   if (rows < kBlock) {
@@ -646,11 +666,12 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
       float lt = l + shfl_xor(l, 16);
       lt += shfl_xor(lt, 32);
       if constexpr (kInt4<KVT>) {
-        // remove the offset: O = sum p (136 + q) - 136 sum p
+        // remove the offset: O = 16 (sum p (1.5 + q/16) - 1.5 sum p)
         float lpt = lp + shfl_xor(lp, 16);
         lpt += shfl_xor(lpt, 32);
 #pragma unroll
-        for (int mt = 0; mt < M::kMTiles; ++mt) acc[mt] -= kInt4Offset * lpt;
+        for (int mt = 0; mt < M::kMTiles; ++mt)
+          acc[mt] = (acc[mt] - kInt4VOffset * lpt) * kInt4VFactor;
       }
       const f32x4_t (&o)[M::kMTiles] = acc;
       if (head_ok) {

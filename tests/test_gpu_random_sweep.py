@@ -293,8 +293,10 @@ def _four_bit_case(i):
     return rng, hkv, group, lengths, partition
 
 
+# 1003: a long-context int4 case on which the V products once lost too many
+# bits to the removal of the code offset (V entered them as 136 + q)
 @pytest.mark.parametrize("fmt", ["int4", "nvfp4"])
-@pytest.mark.parametrize("i", range(8))
+@pytest.mark.parametrize("i", list(range(8)) + [1003])
 def test_four_bit_decode_random(fmt, i):
     """int4 per token-head and nvfp4-style caches with random codes and
     scales (head_dim 128, bf16 queries)."""
