@@ -225,16 +225,17 @@ pkv_status swap_blocks(void* const* src_k_caches, void* const* src_v_caches,
  * c stands for value(c) * k_scale (v_scale for V).  L == 0 gives zeros.
  *
  * Work split: the blocks of all sequences are laid end to end and cut into
- * equal chunks; per kv head, a wave walks a run of consecutive chunks.  A
- * sequence that lies inside one chunk is written to `out` directly; one
- * that spans chunks leaves a (max, sum, weighted-value) partial per chunk in
- * `workspace`, and a second kernel merges them with a log-sum-exp rescale.
+ * equal chunks; per kv head, a wave walks a run of consecutive chunks.
+ * Each chunk of a sequence gives a (max, sum, weighted-value) partial; the
+ * partials of one sequence are combined with a log-sum-exp rescale, first
+ * by the wave that computed them (the chunks it walks), then by a second
+ * kernel across waves, which reads them from `workspace`.  A sequence
+ * walked whole by one wave is written to `out` directly.
  * partition_tokens = 0 lets the library size the chunks from the actual
  * lengths (all chunks equal, one per wave, enough waves to fill the GPU);
  * otherwise each chunk is exactly partition_tokens tokens (a positive
  * multiple of 16) of the laid-out blocks and a wave may walk several.
- * Results do not depend on the number of chunks a wave walks; they are
- * bitwise reproducible for the same arguments.  The workspace is
+ * Results are bitwise reproducible for the same arguments.  The workspace is
  * caller-owned device memory of at least
  * paged_attention_decode_workspace_size(...) bytes for the same arguments;
  * its contents need no initialisation and are scratch after the call.

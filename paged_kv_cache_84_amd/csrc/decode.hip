@@ -12,7 +12,11 @@
 // chunk block by block, crossing sequence boundaries (a wave that finishes a
 // sequence inside its chunk writes that sequence's output).  A sequence that
 // spans several chunks leaves one partial per chunk, in record (chunk +
-// sequence) of the workspace; decode_merge_kernel combines them.
+// sequence) of the workspace; decode_merge_kernel combines them.  (The
+// matrix-core kernel, decode_mfma.hip, whose waves may walk several chunks,
+// folds a wave's chunks of one sequence into one record, at the chunk where
+// that wave's part of the sequence starts; the merge is told how many chunks
+// a wave walks.)
 //
 // Per block, one (block, kv head) tile of K and of V (16 rows x head_dim) is
 // fetched with 16-byte loads:
@@ -594,7 +598,7 @@ __global__ __launch_bounds__(kWave * merge_waves<W>()) void decode_merge_kernel(
     typename QT::storage* __restrict__ out, const float* __restrict__ rec_out,
     const float* __restrict__ rec_ml, const int32_t* __restrict__ context_lens,
     int32_t num_seqs, int32_t max_len, int32_t num_q_heads, int32_t num_chunks,
-    int32_t fixed_chunk, float v_scale, int32_t window) {
+    int32_t fixed_chunk, int32_t chunks_per_wave, float v_scale, int32_t window) {
   constexpr int kPer = D / kWave;
   __shared__ float wts[merge_waves<W>()][kWave];
   __shared__ float part[W][D + 1];
@@ -619,11 +623,18 @@ __global__ __launch_bounds__(kWave * merge_waves<W>()) void decode_merge_kernel(
   }
   const int c = chunk_blocks(sc.total, num_chunks, fixed_chunk);
   const int g0 = before / c, g1 = (before + n - 1) / c;
-  if (g0 == g1) return;
-  const int nparts = g1 - g0 + 1;
-  // the partial of chunk g sits in record g + seq
+  // one record per wave that walked part of the sequence (a wave walks
+  // chunks_per_wave consecutive chunks): wave w0 + k's record sits at chunk
+  // g0 (k = 0) or (w0 + k) * chunks_per_wave, in record chunk + seq
+  const int w0 = g0 / chunks_per_wave, w1 = g1 / chunks_per_wave;
+  if (w0 == w1) return;              // one wave walked it all and wrote it
+  const int nparts = w1 - w0 + 1;
   const int64_t base = int64_t(g0 + seq) * num_q_heads + h;
   const int64_t stride = num_q_heads;
+  // record offset of part k from `base`, in records of one head
+  auto at = [&](int k) -> int64_t {
+    return (k == 0 ? 0 : int64_t(w0 + k) * chunks_per_wave - g0) * stride;
+  };
   const float2* ml = reinterpret_cast<const float2*>(rec_ml) + base;
   if (W == 1 && nparts <= kFewParts) {
     // A few partials (the library's own split): their (max, sum) pairs and
@@ -635,8 +646,8 @@ __global__ __launch_bounds__(kWave * merge_waves<W>()) void decode_merge_kernel(
     for (int j = 0; j < kFewParts; ++j)
 #pragma unroll
       for (int i = 0; i < kPer; ++i)
-        x[j][i] = j < nparts ? po[j * stride * D + i * kWave] : 0.f;
-    const float2 mine = lane < nparts ? ml[lane * stride] : make_float2(-INFINITY, 0.f);
+        x[j][i] = j < nparts ? po[at(j) * D + i * kWave] : 0.f;
+    const float2 mine = lane < nparts ? ml[at(lane)] : make_float2(-INFINITY, 0.f);
     // the pairs sit in lanes 0..kFewParts-1 (the rest hold -inf, 0): read
     // lane by lane; the weighted sum in the tree a butterfly over the wave
     // would take, ((d0 + d1) + (d2 + d3)) + ((d4 + d5) + (d6 + d7))
@@ -666,7 +677,7 @@ __global__ __launch_bounds__(kWave * merge_waves<W>()) void decode_merge_kernel(
     return;
   }
   float big = -INFINITY;
-  for (int k = lane; k < nparts; k += kWave) big = fmaxf(big, ml[k * stride].x);
+  for (int k = lane; k < nparts; k += kWave) big = fmaxf(big, ml[at(k)].x);
   big = wave_max(big);
   float acc[kPer] = {};
   float den = 0.f;
@@ -676,22 +687,21 @@ __global__ __launch_bounds__(kWave * merge_waves<W>()) void decode_merge_kernel(
     const int k = k0 + lane;
     float wk = 0.f;
     if (k < nparts) {
-      const float2 x = ml[k * stride];
+      const float2 x = ml[at(k)];
       wk = fast_exp2(x.x - big);
       den = fmaf(wk, x.y, den);
     }
     wts[wave][lane] = wk;
     __builtin_amdgcn_wave_barrier();
     const int cnt = min(kWave, nparts - k0);
-    const float* po = rec_out + (base + k0 * stride) * D + lane;
-    const int64_t step = stride * D;
+    const float* po = rec_out + base * D + lane;
     int j = 0;
     for (; j + 4 <= cnt; j += 4) {
       float x[4][kPer];
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int i = 0; i < kPer; ++i) x[u][i] = po[(j + u) * step + i * kWave];
+        for (int i = 0; i < kPer; ++i) x[u][i] = po[at(k0 + j + u) * D + i * kWave];
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
@@ -699,7 +709,7 @@ __global__ __launch_bounds__(kWave * merge_waves<W>()) void decode_merge_kernel(
     }
     for (; j < cnt; ++j)
 #pragma unroll
-      for (int i = 0; i < kPer; ++i) acc[i] = fmaf(wts[wave][j], po[j * step + i * kWave], acc[i]);
+      for (int i = 0; i < kPer; ++i) acc[i] = fmaf(wts[wave][j], po[at(k0 + j) * D + i * kWave], acc[i]);
     __builtin_amdgcn_wave_barrier();
   }
   den = wave_sum(den);
@@ -814,19 +824,22 @@ static_assert(2 * PKV_FP8_PAIR_WAVES_PER_SIMD <= kSplitWavesMax,
 template <typename QT, int D>
 static pkv_status launch_merge(void* out, const int32_t* lens, int32_t s, int32_t max_len,
                                int32_t hq, float v_scale, const DecodePlan& plan, void* ws,
-                               hipStream_t st, int32_t window = 0) {
+                               hipStream_t st, int32_t window = 0,
+                               int32_t chunks_per_wave = 1) {
   const float* rec_out = static_cast<const float*>(ws);
   const float* rec_ml =
       reinterpret_cast<const float*>(static_cast<const char*>(ws) + plan.out_bytes);
   if (plan.fixed_chunk > 0)
     hipLaunchKernelGGL((decode_merge_kernel<QT, D, 4>), dim3(hq, s), dim3(kWave * 4), 0, st,
                        static_cast<typename QT::storage*>(out), rec_out, rec_ml, lens, s,
-                       max_len, hq, plan.num_chunks, plan.fixed_chunk, v_scale, window);
+                       max_len, hq, plan.num_chunks, plan.fixed_chunk, chunks_per_wave,
+                       v_scale, window);
   else
     hipLaunchKernelGGL((decode_merge_kernel<QT, D, 1>),
                        dim3((hq + kMergeUnits - 1) / kMergeUnits, s), dim3(kWave * kMergeUnits), 0, st,
                        static_cast<typename QT::storage*>(out), rec_out, rec_ml, lens, s,
-                       max_len, hq, plan.num_chunks, plan.fixed_chunk, v_scale, window);
+                       max_len, hq, plan.num_chunks, plan.fixed_chunk, chunks_per_wave,
+                       v_scale, window);
   return launch_status();
 }
 
@@ -958,11 +971,14 @@ static pkv_status mfma_decode(void* out, const void* query, const void* k_cache,
   a.heads_per_wave = nh;
   if (launch_decode_mfma(a) != PKV_OK) return PKV_ERR_LAUNCH;
   hipStream_t st = as_stream(stream);
+  const int32_t stride = decode_mfma_record_stride(kv_dtype, int32_t(per_wave));
   return head_dim == 64
              ? launch_merge<BF16, 64>(out, context_lens, num_seqs, max_context_len,
-                                      num_q_heads, v_scale, lay, workspace, st, window)
+                                      num_q_heads, v_scale, lay, workspace, st, window,
+                                      stride)
              : launch_merge<BF16, 128>(out, context_lens, num_seqs, max_context_len,
-                                       num_q_heads, v_scale, lay, workspace, st, window);
+                                       num_q_heads, v_scale, lay, workspace, st, window,
+                                       stride);
 }
 
 }  // namespace pkv

@@ -47,6 +47,10 @@ bool decode_mfma_supported(pkv_dtype q_dtype, pkv_dtype kv_dtype, int head_dim, 
 // groups fit two to a wave's 16 columns (group <= 8, an even number of kv
 // heads), else 1.
 int decode_mfma_heads_per_wave(pkv_dtype kv_dtype, int group, int num_kv_heads);
+// Chunks between the records a sequence's partials leave for the merge:
+// chunks_per_wave for the caches whose kernel folds a wave's chunks of one
+// sequence into one record (bf16, fp8), 1 for the others.
+int decode_mfma_record_stride(pkv_dtype kv_dtype, int chunks_per_wave);
 // Launches the chunk kernel only; the caller launches the merge.
 pkv_status launch_decode_mfma(const DecodeMfmaArgs& a);
 

@@ -322,6 +322,23 @@ constexpr int prefetch_depth() {
   return kPacked4<KVT> ? PKV_DEPTH_4BIT : KVT::bytes == 2 ? PKV_DEPTH_BF16 : PKV_DEPTH_FP8;
 }
 
+// Whether the kernel holds a finished segment's result in registers and
+// folds a wave's chunks of one sequence into one record (section on the
+// result below), per cache type.  The 4-bit kernels store each result at
+// once: the held result's 34 registers would cost them one of the four
+// waves per SIMD their split asks for, which measured slower than the
+// stores.
+#ifndef PKV_DEFER_BF16
+#define PKV_DEFER_BF16 1
+#endif
+#ifndef PKV_DEFER_FP8
+#define PKV_DEFER_FP8 1
+#endif
+template <typename KVT>
+constexpr bool defers_results() {
+  return kPacked4<KVT> ? false : KVT::bytes == 2 ? PKV_DEFER_BF16 : PKV_DEFER_FP8;
+}
+
 // Where a block-range cursor stands: sequence s holds the n blocks
 // [before, before + n) of the flattened batch.
 struct SeqCursor {
@@ -547,6 +564,49 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
   int chunk = b0 / c;                 // chunk of the current segment
   int chunk_end = b0 + c;             // its end
 
+  // The result of the segments walked so far of one sequence.  With
+  // kDefer it is held in registers and stored only when the wave moves on
+  // to a second sequence or ends: a store inside the loop enters the same
+  // in-order memory counter as the block loads, so every later wait for a
+  // block would also wait for the store's completion.  Consecutive chunks of
+  // one sequence then fold into it with the merge's log-sum-exp rescale, and
+  // a wave leaves one record per sequence it walks part of, at the chunk
+  // where that part starts.  Without kDefer every segment's result is stored
+  // at its end, one record per chunk.
+  constexpr bool kDefer = defers_results<KVT>();
+  f32x4_t pend[M::kMTiles];
+  float pend_m = kNoMax, pend_l = 0.f;
+  int pend_s = -1;                    // its sequence, -1: nothing held
+  int pend_chunk = 0;
+  bool pend_first = false;            // it starts at the sequence's first block
+  bool pend_last = false;             // it ends at the sequence's last block
+  auto flush = [&]() {
+    if (pend_s < 0) return;
+    if (head_ok) {
+      if (pend_first && pend_last) {
+        // the whole sequence: the output itself
+        const float f = v_scale / pend_l;
+        uint16_t* op = out + (int64_t(pend_s) * num_q_heads + head) * D + 4 * j;
+#pragma unroll
+        for (int mt = 0; mt < M::kMTiles; ++mt) {
+          const uint2 w = {pack_bf16_rne(pend[mt][0] * f, pend[mt][1] * f),
+                           pack_bf16_rne(pend[mt][2] * f, pend[mt][3] * f)};
+          *reinterpret_cast<uint2*>(op + mt * 16) = w;
+        }
+      } else {
+        // the record of (pend_chunk, sequence) -> record pend_chunk + sequence
+        const int64_t idx = int64_t(pend_chunk + pend_s) * num_q_heads + head;
+        float* po = rec_out + idx * D + 4 * j;
+#pragma unroll
+        for (int mt = 0; mt < M::kMTiles; ++mt)
+          *reinterpret_cast<float4*>(po + mt * 16) =
+              make_float4(pend[mt][0], pend[mt][1], pend[mt][2], pend[mt][3]);
+        if (j == 0) reinterpret_cast<float2*>(rec_ml)[idx] = make_float2(pend_m, pend_l);
+      }
+    }
+    pend_s = -1;
+  };
+
   // One block: x, whose K/V sit in register set P (x - b0 = P mod kDepth).
   auto step = [&](auto set, int x) {
     constexpr int P = decltype(set)::value;
@@ -673,27 +733,35 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
         for (int mt = 0; mt < M::kMTiles; ++mt)
           acc[mt] = (acc[mt] - kInt4VOffset * lpt) * kInt4VFactor;
       }
-      const f32x4_t (&o)[M::kMTiles] = acc;
-      if (head_ok) {
-        if (seg_start == cc.before && x + 1 == seq_end) {
-          const float f = v_scale / lt;
-          uint16_t* op = out + (int64_t(cc.s) * num_q_heads + head) * D + 4 * j;
+      auto hold = [&]() {
 #pragma unroll
-          for (int mt = 0; mt < M::kMTiles; ++mt) {
-            const uint2 w = {pack_bf16_rne(o[mt][0] * f, o[mt][1] * f),
-                             pack_bf16_rne(o[mt][2] * f, o[mt][3] * f)};
-            *reinterpret_cast<uint2*>(op + mt * 16) = w;
-          }
+        for (int mt = 0; mt < M::kMTiles; ++mt) pend[mt] = acc[mt];
+        pend_m = m;
+        pend_l = lt;
+        pend_s = cc.s;
+        pend_chunk = chunk;
+        pend_first = seg_start == cc.before;
+        pend_last = x + 1 == seq_end;
+      };
+      if constexpr (kDefer) {
+        if (pend_s == cc.s) {
+          // an earlier chunk of this sequence, walked by this wave: fold
+          // (max a, sum A, O_a) and (b, B, O_b) into (c, A 2^(a-c) + B 2^(b-c),
+          // O_a 2^(a-c) + O_b 2^(b-c)), c = max(a, b)
+          const float mn = fmaxf(pend_m, m);
+          const float wa = fast_exp2(pend_m - mn), wb = fast_exp2(m - mn);
+#pragma unroll
+          for (int mt = 0; mt < M::kMTiles; ++mt) pend[mt] = pend[mt] * wa + acc[mt] * wb;
+          pend_l = pend_l * wa + lt * wb;
+          pend_m = mn;
+          pend_last = x + 1 == seq_end;
         } else {
-          // the partial of (chunk seg_start / c, sequence) -> record chunk + sequence
-          const int64_t idx = int64_t(chunk + cc.s) * num_q_heads + head;
-          float* po = rec_out + idx * D + 4 * j;
-#pragma unroll
-          for (int mt = 0; mt < M::kMTiles; ++mt)
-            *reinterpret_cast<float4*>(po + mt * 16) =
-                make_float4(o[mt][0], o[mt][1], o[mt][2], o[mt][3]);
-          if (j == 0) reinterpret_cast<float2*>(rec_ml)[idx] = make_float2(m, lt);
+          flush();
+          hold();
         }
+      } else {
+        hold();
+        flush();
       }
 #pragma unroll
       for (int mt = 0; mt < M::kMTiles; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -720,6 +788,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
       step(std::integral_constant<int, kDepth - 1>{}, x + 1);
     }
   }
+  if constexpr (kDefer) flush();
 }
 
 template <typename KVT, int D, int NH = 1>
@@ -745,6 +814,14 @@ static pkv_status launch_one(const DecodeMfmaArgs& a) {
 #ifndef PKV_DECODE_PAIR_BF16
 #define PKV_DECODE_PAIR_BF16 0
 #endif
+int decode_mfma_record_stride(pkv_dtype kv_dtype, int chunks_per_wave) {
+  switch (kv_dtype) {
+    case PKV_BF16: return defers_results<BF16>() ? chunks_per_wave : 1;
+    case PKV_FP8_E4M3: return defers_results<FP8>() ? chunks_per_wave : 1;
+    default: return 1;
+  }
+}
+
 int decode_mfma_heads_per_wave(pkv_dtype kv_dtype, int group, int num_kv_heads) {
   const bool pair = kv_dtype == PKV_FP8_E4M3 ? PKV_DECODE_PAIR_FP8
                                              : kv_dtype == PKV_BF16 && PKV_DECODE_PAIR_BF16;
