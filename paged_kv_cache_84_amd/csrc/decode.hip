@@ -577,13 +577,15 @@ __global__ __launch_bounds__(256) void prefill_rows_kernel(
 // sequence that spans several chunks,
 //   out = sum_k e^{m_k - M} o_k / sum_k e^{m_k - M} l_k,   M = max_k m_k
 // (m in log2 units).  Sequences inside one chunk were written by the chunk
-// kernel; empty ones get zeros here.  Each wave takes every W-th group of
-// 64 partials; within a group the weights are computed one per lane and
-// passed through LDS, so the partials' loads do not wait on each other.  The
-// waves' sums meet in LDS at the end.  (W = 4 for fixed partitions, which
-// leave hundreds of partials per sequence; 1 for the library's own split,
-// which leaves a few: up to kFewParts of them are merged from one round of
-// loads, pairs and vectors together.)
+// kernel; empty ones get zeros here.  The weights are computed one partial
+// per lane, so the partials' vector loads do not wait on each other.
+// W = 4 for fixed partitions, which leave tens to hundreds of partials per
+// sequence: wave w of the unit takes partials w, w + 4, w + 8, ..., reads
+// each weight back from its lane, loads eight partials' vectors before using
+// any, and the waves' sums meet in LDS at the end.  W = 1 for the library's
+// own split, which leaves a few: up to kFewParts of them are merged from one
+// round of loads, pairs and vectors together; more go in groups of 64 whose
+// weights pass through LDS.
 constexpr int kFewParts = 8;   // partials merged by the single-load path
 // With W = 1 a workgroup carries this many (head, sequence) units, one per
 // wave, each on its own (no workgroup barrier): a quarter of the workgroups
@@ -601,7 +603,7 @@ __global__ __launch_bounds__(kWave * merge_waves<W>()) void decode_merge_kernel(
     int32_t fixed_chunk, int32_t chunks_per_wave, float v_scale, int32_t window) {
   constexpr int kPer = D / kWave;
   __shared__ float wts[merge_waves<W>()][kWave];
-  __shared__ float part[W][D + 1];
+  __shared__ float part[W][D + 2];
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
   const int h = W == 1 ? int(blockIdx.x) * kMergeUnits + wave : int(blockIdx.x);
@@ -676,64 +678,108 @@ __global__ __launch_bounds__(kWave * merge_waves<W>()) void decode_merge_kernel(
     for (int i = 0; i < kPer; ++i) store_out<QT>(o + lane + i * kWave, acc[i] * f);
     return;
   }
-  float big = -INFINITY;
-  for (int k = lane; k < nparts; k += kWave) big = fmaxf(big, ml[at(k)].x);
-  big = wave_max(big);
-  float acc[kPer] = {};
-  float den = 0.f;
-  // W > 1: the waves take every W-th group of 64 partials of one unit;
-  // W = 1: each wave is a unit of its own and takes them all
-  for (int k0 = W == 1 ? 0 : wave * kWave; k0 < nparts; k0 += kWave * W) {
-    const int k = k0 + lane;
-    float wk = 0.f;
-    if (k < nparts) {
-      const float2 x = ml[at(k)];
-      wk = fast_exp2(x.x - big);
-      den = fmaf(wk, x.y, den);
+  const float* po = rec_out + base * D + lane;
+  if constexpr (W == 1) {
+    // each wave is a unit of its own and takes its partials in groups of 64
+    float big = -INFINITY;
+    for (int k = lane; k < nparts; k += kWave) big = fmaxf(big, ml[at(k)].x);
+    big = wave_max(big);
+    float acc[kPer] = {};
+    float den = 0.f;
+    for (int k0 = 0; k0 < nparts; k0 += kWave) {
+      const int k = k0 + lane;
+      float wk = 0.f;
+      if (k < nparts) {
+        const float2 x = ml[at(k)];
+        wk = fast_exp2(x.x - big);
+        den = fmaf(wk, x.y, den);
+      }
+      wts[wave][lane] = wk;
+      __builtin_amdgcn_wave_barrier();
+      const int cnt = min(kWave, nparts - k0);
+      int j = 0;
+      for (; j + 4 <= cnt; j += 4) {
+        float x[4][kPer];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int i = 0; i < kPer; ++i) x[u][i] = po[at(k0 + j + u) * D + i * kWave];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int i = 0; i < kPer; ++i) acc[i] = fmaf(wts[wave][j + u], x[u][i], acc[i]);
+      }
+      for (; j < cnt; ++j)
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) acc[i] = fmaf(wts[wave][j], po[at(k0 + j) * D + i * kWave], acc[i]);
+      __builtin_amdgcn_wave_barrier();
     }
-    wts[wave][lane] = wk;
-    __builtin_amdgcn_wave_barrier();
-    const int cnt = min(kWave, nparts - k0);
-    const float* po = rec_out + base * D + lane;
-    int j = 0;
-    for (; j + 4 <= cnt; j += 4) {
-      float x[4][kPer];
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) x[u][i] = po[at(k0 + j + u) * D + i * kWave];
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) acc[i] = fmaf(wts[wave][j + u], x[u][i], acc[i]);
-    }
-    for (; j < cnt; ++j)
-#pragma unroll
-      for (int i = 0; i < kPer; ++i) acc[i] = fmaf(wts[wave][j], po[at(k0 + j) * D + i * kWave], acc[i]);
-    __builtin_amdgcn_wave_barrier();
-  }
-  den = wave_sum(den);
-  if constexpr (W == 1) {     // the wave holds the whole unit
+    den = wave_sum(den);
     const float f = v_scale / den;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) store_out<QT>(o + lane + i * kWave, acc[i] * f);
-    return;
-  }
+  } else {
+    // W waves share the unit: wave w takes partials w, w + W, w + 2W, ...,
+    // kGroup at a time, loading a group's (max, sum) pairs (lane u holds the
+    // group's u-th) and vectors in one round; the wave keeps its own running
+    // max, and the waves' results meet in LDS with the same rescale.
+    constexpr int kGroup = 32;
+    const int mine = (nparts - wave + W - 1) / W;    // partials of this wave
+    float mw = -INFINITY, den = 0.f;
+    float acc[kPer] = {};
+    for (int i0 = 0; i0 < mine; i0 += kGroup) {
+      const int cnt = min(kGroup, mine - i0);
+      // past cnt, lanes and vector slots re-read the group's last partial
+      // with weight 0
+      const int ku = wave + W * (i0 + min(lane, cnt - 1));
+      const float2 x = ml[at(ku)];
+      float v[kGroup][kPer];
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) part[wave][lane + i * kWave] = acc[i];
-  if (lane == 0) part[wave][D] = den;
-  __syncthreads();
-  if (wave != 0) return;
-  float dsum = 0.f;
+      for (int u = 0; u < kGroup; ++u)
 #pragma unroll
-  for (int w = 0; w < W; ++w) dsum += part[w][D];
-  const float f = v_scale / dsum;
+        for (int i = 0; i < kPer; ++i)
+          v[u][i] = po[at(wave + W * (i0 + min(u, cnt - 1))) * D + i * kWave];
+      const float gm = wave_max(lane < cnt ? x.x : -INFINITY);
+      const float mn = fmaxf(mw, gm);
+      const float r = fast_exp2(mw - mn);        // 0 while mw is -inf
+      const float wk = lane < cnt ? fast_exp2(x.x - mn) : 0.f;
+      den = den * r + wave_sum(wk * x.y);
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    float a = 0.f;
+      for (int i = 0; i < kPer; ++i) acc[i] *= r;
 #pragma unroll
-    for (int w = 0; w < W; ++w) a += part[w][lane + i * kWave];
-    store_out<QT>(o + lane + i * kWave, a * f);
+      for (int u = 0; u < kGroup; ++u) {
+        const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk), u));
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) acc[i] = fmaf(wu, v[u][i], acc[i]);
+      }
+      mw = mn;
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) part[wave][lane + i * kWave] = acc[i];
+    if (lane == 0) {
+      part[wave][D] = den;
+      part[wave][D + 1] = mw;
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    float big = part[0][D + 1];
+#pragma unroll
+    for (int w = 1; w < W; ++w) big = fmaxf(big, part[w][D + 1]);
+    float fw[W];
+    float dsum = 0.f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      fw[w] = fast_exp2(part[w][D + 1] - big);   // 0 for a wave with no partials
+      dsum = fmaf(fw[w], part[w][D], dsum);
+    }
+    const float f = v_scale / dsum;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      float a = 0.f;
+#pragma unroll
+      for (int w = 0; w < W; ++w) a = fmaf(fw[w], part[w][lane + i * kWave], a);
+      store_out<QT>(o + lane + i * kWave, a * f);
+    }
   }
 }
 
