@@ -278,3 +278,31 @@ def test_decode_library_split_many_partials(long_len):
     ref_long = np.stack([P.decode_attention_one(hq_, F.BF16, kc_, vc_, F.BF16, tables, lens,
                                                 0.088, 0, h) for h in heads])
     assert_attention_close(got[0, heads], ref_long, "bf16", "long sequence")
+
+
+@pytest.mark.parametrize("hq,hkv,kvd,kind", [(8, 1, F.BF16, "bf16"),
+                                             (16, 2, F.FP8_E4M3, "fp8_e4m3")])
+def test_fixed_partitions_merge_many_records_per_wave(hq, hkv, kvd, kind):
+    """16-token partitions with one kv head (one two-head wave for fp8): the
+    split plans for the batch's widest shape (5 x 1,250 partitions), so a
+    wave walks seven partitions and folds them into one record per sequence;
+    the 20,000-token sequence leaves 179 records and each of the merge's
+    four waves combines about 45 of them in two groups (32 + 13), rescaling
+    its running maximum between groups.  Every output against the oracle."""
+    announce("decode fixed partitions, many records per merge wave", hq, hkv, kvd)
+    lengths = [20000, 3000, 17, 0, 777]
+    q, kc, vc, tables, lens, ks, vs = _random_decode(hq, hkv, 128, F.BF16, kvd, lengths,
+                                                     seed=31 + hq)
+    chunks = pk.decode_num_chunks(len(lengths), hq, hkv, int(lens.max()), 16)
+    assert chunks >= 5 * P.blocks_needed(20000)       # 16-token chunks over the laid-out batch
+    out = pk.paged_attention_decode(q, kc.view(torch.uint8) if kvd == F.FP8_E4M3 else kc,
+                                    vc.view(torch.uint8) if kvd == F.FP8_E4M3 else vc,
+                                    torch.as_tensor(tables, device=DEV),
+                                    torch.as_tensor(lens, device=DEV), int(lens.max()),
+                                    0.088, ks, vs, 16)
+    torch.cuda.synchronize()
+    ref = P.decode_attention(host(q), F.BF16, host(kc), host(vc), kvd, tables, lens, 0.088,
+                             ks, vs)
+    got = as_f64(out)
+    assert np.all(got[3] == 0.0)
+    assert_attention_close(got, ref, kind, f"fixed partitions {hq}/{hkv} {kvd}")
