@@ -44,8 +44,8 @@ struct DecodeMfmaArgs {
 // per token-head or nvfp4-style cache (head_dim 128); group <= 16.
 bool decode_mfma_supported(pkv_dtype q_dtype, pkv_dtype kv_dtype, int head_dim, int group);
 // kv heads one wave of the chunk kernel serves: 2 for fp8 caches whose query
-// groups fit two to a wave's 16 columns (group <= 8, an even number of kv
-// heads), else 1.
+// groups fit two to a wave's 16 columns (group <= 8) and for bf16 caches with
+// one query head per kv head, given an even number of kv heads; else 1.
 int decode_mfma_heads_per_wave(pkv_dtype kv_dtype, int group, int num_kv_heads);
 // Chunks between the records a sequence's partials leave for the merge:
 // chunks_per_wave for the caches whose kernel folds a wave's chunks of one
